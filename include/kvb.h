@@ -1,0 +1,255 @@
+/*
+ * kvb.h - C ABI of the link-step library for selective KV recompute over a
+ * spliced, position-shifted reused KV cache, built for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The method: the KV caches of several chunks, each compiled alone from
+ * position 0 (EPIC page, section 3.1, compile step), are spliced into one
+ * request and a subset of tokens is recomputed (link step).  Two ways of
+ * choosing the subset are served by the same calls:
+ *   - CacheSlide Weighted Correction Attention (CacheSlide page, "Method
+ *     details", weighted-correction paragraphs and Algorithm 2): layer 1
+ *     recomputes every token and ranks them by d_i = ||K_i^rec - K_i^reuse||^2;
+ *     layers 2..L recompute the top-k and fuse
+ *     K_i <- alpha_i K_i^rec + (1 - alpha_i) K_i^reuse (same for V) with
+ *     alpha_i = d_i / ||K_i^reuse||^2; every four layers a cosine check
+ *     retires tokens and refills from the ranking;
+ *   - EPIC LegoLink (EPIC page, section 4): the first k tokens of every chunk
+ *     but the first, recomputed in every layer, replacing the cached K/V.
+ * Recomputed K/V go to freshly allocated pages (CacheSlide page, SLIDE
+ * implementation paragraph) of a paged cache with 16-token pages.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - All calls are enqueue-only on the given HIP stream (a hipStream_t passed
+ *    as void*; NULL = the default stream) and never synchronise the device.
+ *  - Arguments are validated on the host before anything is enqueued; on error
+ *    nothing is enqueued, a status < 0 is returned and kvb_last_error() gives a
+ *    thread-local message.  A failed kernel launch returns KVB_ERR_HIP.
+ *  - Every device buffer is allocated and owned by the caller; the library
+ *    allocates no device memory in these calls and keeps no pointer after a
+ *    call returns.  Buffers are row-major, contiguous and 16-byte aligned.
+ *  - Storage type (desc->dtype): KVB_F32 (float) or KVB_BF16 (bfloat16 bits
+ *    in uint16).  Weights, embeddings, hidden state, Q/K/V, attention output
+ *    and the KV pool all use it; reductions and softmax run in float32.
+ *  - Token space: the requests of a batch are concatenated; token g of the
+ *    batch is "global token g", 0 <= g < n_tok.  Per-token int32 arrays
+ *    indexed by g: tok_pos[g] = RoPE position, tok_lo[g] = first key index
+ *    visible to g (the start of its request, or of its chunk at compile time).
+ *  - Row batches: a call works on T rows; row r is global token row_tok[r]
+ *    (row_tok == NULL means row r is token r).  T_max is a host bound used
+ *    for launch sizes; n_rows (device int32, may be NULL = T_max) holds the
+ *    actual count, so counts produced on the device need no host round trip.
+ *    Rows >= *n_rows are neither read nor written.
+ *  - KV pool: K and V are separate arrays of n_pages pages, each
+ *    [n_kv_heads][page_size][head_dim]; slot s lives in page s / page_size at
+ *    position s % page_size.  Slots outside [0, n_pages*page_size) are skipped
+ *    by the kernels (never dereferenced).
+ */
+#ifndef KVB_H
+#define KVB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t kvb_status;
+#define KVB_OK 0
+#define KVB_ERR_INVALID_ARG (-1)  /* null pointer, negative size, inconsistent shape */
+#define KVB_ERR_UNSUPPORTED (-2)  /* dtype, head_dim not in {64,128}, page_size != 16, bf16 dims not multiples of 64 */
+#define KVB_ERR_HIP (-3)          /* HIP runtime / launch error */
+#define KVB_ERR_CAPACITY (-4)     /* page pool exhausted */
+#define KVB_ERR_WORKSPACE (-5)    /* workspace missing or too small */
+
+#define KVB_F32 0
+#define KVB_BF16 1
+
+/* alpha handling of kvb_blend_scatter */
+#define KVB_ALPHA_LAG 0      /* blend with the stored alpha, then store this layer's alpha (Algorithm 2 order) */
+#define KVB_ALPHA_CURRENT 1  /* blend with this layer's alpha and store it */
+#define KVB_ALPHA_ONE 2      /* alpha = 1: the recomputed rows replace the cached ones; nothing stored */
+
+/* retire rule of kvb_cosine_refresh */
+#define KVB_REFRESH_LITERAL 0  /* retire when CKSim < tau (the pages' stated test) */
+#define KVB_REFRESH_DISSIM 1   /* retire when CKSim > 1 - tau (alternative reading) */
+
+typedef struct kvb_model_desc {
+  int32_t d_model;     /* hidden size d */
+  int32_t n_q_heads;   /* Hq */
+  int32_t n_kv_heads;  /* Hkv, divides Hq */
+  int32_t head_dim;    /* 64 or 128 */
+  int32_t ffn;         /* SwiGLU inner size F */
+  int32_t page_size;   /* must be 16 */
+  float rope_base;     /* RoPE base, e.g. 10000 */
+  float rms_eps;       /* RMSNorm epsilon */
+  int32_t dtype;       /* KVB_F32 or KVB_BF16 */
+} kvb_model_desc;
+
+typedef struct kvb_ctx kvb_ctx;
+typedef struct kvb_pool kvb_pool;
+
+/* ----------------------------------------------------------------- basics */
+
+const char* kvb_status_string(kvb_status s);
+/* Message of the last failing call on this thread ("" if none). */
+const char* kvb_last_error(void);
+
+/* Context bound to HIP device `device` (queried once for its CU count).
+ * A context is used by one host thread at a time. */
+kvb_status kvb_create(int32_t device, kvb_ctx** out);
+kvb_status kvb_destroy(kvb_ctx* ctx);
+
+/* Bytes of workspace the calls below need for batches of at most max_rows
+ * rows, max_tokens tokens and max_requests requests. */
+kvb_status kvb_workspace_size(kvb_ctx* ctx, const kvb_model_desc* desc, int32_t max_rows,
+                              int32_t max_tokens, int32_t max_requests, size_t* bytes);
+
+/* --------------------------------------------------- host page allocator
+ * Deterministic allocator over page ids 0..n_pages-1: kvb_pool_alloc hands out
+ * the n lowest free ids in ascending order, or fails with KVB_ERR_CAPACITY
+ * and allocates nothing (SLIDE preallocation of new pages, CacheSlide page,
+ * SLIDE implementation paragraph).  Host memory only. */
+kvb_status kvb_pool_create(int32_t n_pages, kvb_pool** out);
+kvb_status kvb_pool_destroy(kvb_pool* pool);
+kvb_status kvb_pool_alloc(kvb_pool* pool, int32_t n, int32_t* out_ids /* host [n] */);
+kvb_status kvb_pool_release(kvb_pool* pool, int32_t n, const int32_t* ids /* host [n] */);
+kvb_status kvb_pool_free_count(const kvb_pool* pool, int32_t* out);
+
+/* ------------------------------------------------------------ the path */
+
+/* hidden[row_tok[r]] = table[tokens[row_tok[r]]] for r < *n_rows.
+ * First step of every recomputed token at layer 1 (EPIC page, section 4,
+ * LegoLink step 1: embeddings E of the selected tokens).  tokens: device int32
+ * [n_tok] vocabulary ids in [0, vocab) (rows with other ids are skipped);
+ * table: [vocab, d]; hidden: [n_tok, d]. */
+kvb_status kvb_embed(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t T_max,
+                     const int32_t* n_rows, const int32_t* row_tok, const int32_t* tokens,
+                     int32_t vocab, const void* table, void* hidden);
+
+/* Gathered-row RMSNorm + Q/K/V projection (EPIC page, section 4, LegoLink
+ * step 2: Q, K, V = E W for the recomputed rows only).
+ *   a_r = RMSNorm(hidden[row_tok[r]]) * norm_w;  [q|k|v]_r = a_r W_qkv^T
+ * hidden [n_tok, d]; norm_w [d]; w_qkv [(Hq + 2 Hkv) * hd, d] (Q rows, then K,
+ * then V); outputs q [T, Hq, hd], k [T, Hkv, hd], v [T, Hkv, hd].
+ * If tok_pos != NULL, rotate-half RoPE at position tok_pos[row_tok[r]] is
+ * applied to q and k (as kvb_rope).  The per-row result does not depend on
+ * T, on the row's place in the batch or on the other rows (a chunk seen at
+ * the same positions in compile and link gets bitwise-equal keys). */
+kvb_status kvb_qkv_proj(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t T_max,
+                        const int32_t* n_rows, const int32_t* row_tok, const void* hidden,
+                        const void* norm_w, const void* w_qkv, const int32_t* tok_pos, void* q,
+                        void* k, void* v);
+
+/* In-place rotate-half RoPE of q [T, Hq, hd] and k [T, Hkv, hd] at positions
+ * tok_pos[row_tok[r]]: pair (j, j + hd/2) rotated by pos * base^(-2j/hd).
+ * Angles are formed in double precision. */
+kvb_status kvb_rope(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t T_max,
+                    const int32_t* n_rows, const int32_t* row_tok, const int32_t* tok_pos, void* q,
+                    void* k);
+
+/* Fusion and scatter of the recomputed rows into the page pool (CacheSlide
+ * page, Algorithm 2 fusion line and alpha definition; SLIDE writes the
+ * selected tokens' K/V into newly allocated pages).  For each row r < *n_rows
+ * with token g = row_tok[r]:
+ *   reuse = pool rows at src_slot[g] (the token's cached K/V of this layer)
+ *   d_r   = ||k_rec_r - k_reuse||^2 (whole row, all KV heads), float32
+ *   a_new = d_r / ||k_reuse||^2   (0 if both are 0, 1 if only the norm is 0)
+ *   a_use = alpha[g] (KVB_ALPHA_LAG), a_new (KVB_ALPHA_CURRENT) or 1 (KVB_ALPHA_ONE)
+ *   K, V at dst_slot[r] <- a_use * rec + (1 - a_use) * reuse  (float32, one rounding)
+ *   alpha[g] <- a_new unless KVB_ALPHA_ONE;  d_out[r] <- d_r;
+ *   cksim_out[r] <- mean over KV heads of cos(k_rec_r,h, k_reuse_h)
+ *                   (1 if both vectors are 0, 0 if exactly one is).
+ * src_slot == NULL means "no cached row": only KVB_ALPHA_ONE is allowed and
+ * d_out / cksim_out must be NULL (compile step, layer 1, LegoLink).
+ * k_rec, v_rec [T, Hkv, hd]; alpha [n_tok] float; d_out, cksim_out [T] float
+ * or NULL; dst_slot [T]; src_slot [n_tok]. */
+kvb_status kvb_blend_scatter(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t T_max,
+                             const int32_t* n_rows, const int32_t* row_tok, const void* k_rec,
+                             const void* v_rec, void* k_pool, void* v_pool, int32_t n_pages,
+                             const int32_t* src_slot, const int32_t* dst_slot, int32_t alpha_mode,
+                             float* alpha, float* d_out, float* cksim_out);
+
+/* Causal grouped-query attention of gathered query rows over the full spliced
+ * KV of the layer (EPIC page, section 4, LegoLink steps 3-5:
+ * A = softmax(Q K_exp^T, causal) over all N tokens, O = A V_exp).  Row r
+ * (token g = row_tok[r]) attends the keys j with tok_lo[g] <= j <= g, read
+ * from slot slot_map[j] of the pools; query head h reads KV head
+ * h / (Hq / Hkv); scores are scaled by `scale`.
+ * q [T, Hq, hd]; slot_map [n_tok]; o [T, Hq * hd]. */
+kvb_status kvb_sparse_query_attn(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc,
+                                 int32_t T_max, const int32_t* n_rows, const int32_t* row_tok,
+                                 const int32_t* tok_lo, const void* q, const void* k_pool,
+                                 const void* v_pool, int32_t n_pages, const int32_t* slot_map,
+                                 float scale, void* o, void* ws, size_t ws_bytes);
+
+/* Output projection and SwiGLU MLP of the recomputed rows (EPIC page,
+ * section 4, LegoLink step 5: O = A V_exp W_O, the layer output):
+ *   h1 = hidden[g] + o_r W_o^T ;  b = RMSNorm(h1) * norm2_w ;
+ *   hidden[g] <- h1 + (silu(b W_gate^T) * (b W_up^T)) W_down^T
+ * o [T, Hq*hd]; w_o [d, Hq*hd]; w_gate_up [2F, d] (gate rows then up rows);
+ * w_down [d, F]; hidden [n_tok, d] updated in place at rows row_tok[r].
+ * Needs workspace (kvb_workspace_size). */
+kvb_status kvb_mlp(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t T_max,
+                   const int32_t* n_rows, const int32_t* row_tok, const void* attn_o,
+                   const void* w_o, void* hidden, const void* norm2_w, const void* w_gate_up,
+                   const void* w_down, void* ws, size_t ws_bytes);
+
+/* Layer-1 deviation and top-k selection of CacheSlide (CacheSlide page,
+ * Algorithm 2 initialisation: d_i, alpha_i for every token, S = {d_i > 0},
+ * S_k = top-k of S by d).  For request b (tokens cu_tok[b] .. cu_tok[b+1]-1):
+ *   d[g]     = ||k_rec[g] - k_reuse(g)||^2, reuse read at slot reuse_slot[g]
+ *   alpha[g] = d[g] / ||k_reuse(g)||^2   (zero-norm rule as kvb_blend_scatter)
+ *   ranking[cu_tok[b] + i] = the i-th token of S by d descending, ties by
+ *     lower index; entries from s_count[b] on list the d == 0 tokens ascending
+ *   s_count[b] = |S|;  k_b = min(k_cap[b], |S|);  cursor[b] = k_b
+ *   sel[cu_rows[b] .. cu_rows[b+1]-1] = the k_b top tokens in ascending order
+ *   cu_rows[0] = 0, cu_rows[b+1] = cu_rows[b] + k_b
+ * k_rec is token-indexed [n_tok, Hkv, hd] (layer 1 recomputes every token);
+ * cu_tok, k_cap device int32; d, alpha float [n_tok]; ranking, sel int32
+ * [n_tok]; s_count, cursor int32 [B]; cu_rows int32 [B+1].  Needs workspace.
+ * Results are bitwise deterministic. */
+kvb_status kvb_deviation_topk(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t B,
+                              int32_t n_tok, const int32_t* cu_tok, const void* k_rec,
+                              const void* k_pool, int32_t n_pages, const int32_t* reuse_slot,
+                              const int32_t* k_cap, float* d, float* alpha, int32_t* ranking,
+                              int32_t* s_count, int32_t* sel, int32_t* cu_rows, int32_t* cursor,
+                              void* ws, size_t ws_bytes);
+
+/* Similarity-gated refresh (CacheSlide page, Algorithm 2, every four layers:
+ * a token of S_k whose CKSim is below tau leaves S_k and S, and the token of
+ * S \ S_k with the largest deviation joins).  Works on a snapshot: for
+ * request b with rows cu_rows_in[b] .. cu_rows_in[b+1]-1 of sel_in and their
+ * cksim values, R_b = rows to retire under `rule`; the next
+ * m_b = min(|R_b|, s_count[b] - cursor[b]) tokens of the ranking (from
+ * ranking[cu_tok[b] + cursor[b]]) join; cursor[b] += m_b.  The new set, in
+ * ascending order, goes to sel_out at cu_rows_out[b] (cu_rows_out[0] = 0).
+ * sel_in and sel_out must not overlap.  Needs workspace. */
+kvb_status kvb_cosine_refresh(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t B,
+                              int32_t n_tok, const int32_t* cu_tok, int32_t T_max,
+                              const int32_t* cu_rows_in, const int32_t* sel_in,
+                              const float* cksim, float tau, int32_t rule,
+                              const int32_t* ranking, const int32_t* s_count, int32_t* cursor,
+                              int32_t* sel_out, int32_t* cu_rows_out, void* ws, size_t ws_bytes);
+
+/* Slot map of one layer (SLIDE: selected tokens are routed to the layer's new
+ * pages through the request's slot mapping).  slot_map[g] = reuse_slot[g] for
+ * every token, then for each row r of request b (rank j = r - cu_rows[b]):
+ *   dst_slot[r] = new_pages[cu_pages[b] + j / page_size] * page_size + j % page_size
+ *   slot_map[row_tok[r]] = dst_slot[r]
+ * Rows whose rank exceeds the request's page list get dst_slot = -1 and keep
+ * their reuse slot.  reuse_slot may be NULL (slot_map starts at -1).
+ * row_tok NULL = identity (then cu_rows doubles as cu_tok). */
+kvb_status kvb_slot_map(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t B,
+                        int32_t n_tok, int32_t T_max, const int32_t* cu_rows,
+                        const int32_t* row_tok, const int32_t* reuse_slot,
+                        const int32_t* new_pages, const int32_t* cu_pages, int32_t* slot_map,
+                        int32_t* dst_slot);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVB_H */

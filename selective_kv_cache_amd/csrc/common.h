@@ -1,0 +1,95 @@
+// Internal helpers shared by the kvb HIP sources (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/kvb.h"
+
+// ------------------------------------------------------------------ errors
+
+namespace kvb {
+
+void set_error(const std::string& msg);
+kvb_status fail(kvb_status s, const std::string& msg);
+kvb_status check_launch(const char* what);
+
+struct Ctx {
+  int device = 0;
+  int n_cu = 256;
+};
+
+// Validates the model description; returns KVB_OK or an error with message.
+kvb_status check_desc(const kvb_model_desc* d);
+kvb_status check_ctx(const kvb_ctx* c);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
+
+// workspace layouts (bytes), shared by kvb_workspace_size and the entry points
+size_t ws_mlp_bytes(const kvb_model_desc* d, int32_t max_rows);
+size_t ws_topk_bytes(int32_t max_tokens, int32_t max_requests);
+size_t ws_refresh_bytes(int32_t max_tokens, int32_t max_requests);
+size_t ws_attn_bytes(const kvb_model_desc* d, int32_t max_rows, int32_t max_tokens);
+
+}  // namespace kvb
+
+#define KVB_CHECK_PTR(p, name) \
+  do { if (!(p)) return kvb::fail(KVB_ERR_INVALID_ARG, std::string(name) + " is NULL"); } while (0)
+#define KVB_TRY(expr) \
+  do { kvb_status _s = (expr); if (_s != KVB_OK) return _s; } while (0)
+
+// ------------------------------------------------------------------ bf16
+
+typedef uint16_t bf16_t;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// float -> bfloat16, round to nearest even (NaN kept quiet)
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+// storage-type traits: T is float (KVB_F32) or bf16_t (KVB_BF16)
+template <class T> struct Store;
+template <> struct Store<float> {
+  __device__ __forceinline__ static float ld(const float* p) { return *p; }
+  __device__ __forceinline__ static void st(float* p, float v) { *p = v; }
+  __device__ __forceinline__ static float cvt(float v) { return v; }
+};
+template <> struct Store<bf16_t> {
+  __device__ __forceinline__ static float ld(const bf16_t* p) { return bf2f(*p); }
+  __device__ __forceinline__ static void st(bf16_t* p, float v) { *p = f2bf(v); }
+  __device__ __forceinline__ static bf16_t cvt(float v) { return f2bf(v); }
+};
+
+template <class T> __device__ __forceinline__ float to_f(T v);
+template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f<bf16_t>(bf16_t v) { return bf2f(v); }
+
+__device__ __forceinline__ int row_count(const int32_t* n_rows, int T_max) {
+  if (!n_rows) return T_max;
+  int n = *n_rows;
+  return n < T_max ? n : T_max;
+}
+
+// wave64 reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}

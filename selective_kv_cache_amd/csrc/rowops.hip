@@ -1,0 +1,421 @@
+// Bandwidth-bound row kernels of the link step: embedding gather, RoPE,
+// CacheSlide's fusion + scatter into new pages, and the per-layer slot map.
+//
+// Every reduction here runs in a fixed order that depends only on the element
+// index inside a row, never on the row's place in a batch, so results are
+// bitwise reproducible from run to run and from batch to batch.
+#include "common.h"
+
+namespace kvb {
+
+// ------------------------------------------------------------------ embedding
+// hidden[g] = table[tokens[g]], g = row_tok[r]
+
+template <class T>
+__global__ void embed_kernel(int T_max, const int32_t* __restrict__ n_rows, const int32_t* __restrict__ row_tok,
+                             const int32_t* __restrict__ tokens, int vocab, const T* __restrict__ table,
+                             T* __restrict__ hidden, int d) {
+  const int r = blockIdx.x;
+  if (r >= row_count(n_rows, T_max)) return;
+  const int g = row_tok ? row_tok[r] : r;
+  const int id = tokens[g];
+  if (id < 0 || id >= vocab) return;
+  const uint4* src = reinterpret_cast<const uint4*>(table + (size_t)id * d);
+  uint4* dst = reinterpret_cast<uint4*>(hidden + (size_t)g * d);
+  const int nvec = d * (int)sizeof(T) / 16;
+  for (int i = threadIdx.x; i < nvec; i += blockDim.x) dst[i] = src[i];
+}
+
+// ------------------------------------------------------------------ RoPE
+// rotate-half: (x_j, x_{j+hd/2}) -> (x_j c - x_{j+hd/2} s, x_{j+hd/2} c + x_j s),
+// angle = pos * base^(-2j/hd) formed in double precision.
+
+template <class T>
+__global__ void rope_kernel(int T_max, const int32_t* __restrict__ n_rows, const int32_t* __restrict__ row_tok,
+                            const int32_t* __restrict__ tok_pos, T* __restrict__ q, T* __restrict__ k, int Hq,
+                            int Hkv, int hd, float base) {
+  const int r = blockIdx.x;
+  if (r >= row_count(n_rows, T_max)) return;
+  const int g = row_tok ? row_tok[r] : r;
+  const double pos = (double)tok_pos[g];
+  const int half = hd / 2;
+  __shared__ float cs[64], sn[64];
+  for (int j = threadIdx.x; j < half; j += blockDim.x) {
+    double inv = pow((double)base, -2.0 * (double)j / (double)hd);
+    double s, c;
+    sincos(pos * inv, &s, &c);
+    cs[j] = (float)c;
+    sn[j] = (float)s;
+  }
+  __syncthreads();
+  const int npairs = (Hq + Hkv) * half;
+  for (int p = threadIdx.x; p < npairs; p += blockDim.x) {
+    const int h = p / half, j = p % half;
+    T* x = (h < Hq) ? (q + ((size_t)r * Hq + h) * hd) : (k + ((size_t)r * Hkv + (h - Hq)) * hd);
+    const float x1 = to_f<T>(x[j]), x2 = to_f<T>(x[j + half]);
+    const float c = cs[j], s = sn[j];
+    Store<T>::st(x + j, x1 * c - x2 * s);
+    Store<T>::st(x + j + half, x2 * c + x1 * s);
+  }
+}
+
+// ------------------------------------------------------------------ pool addressing
+
+__device__ __forceinline__ size_t pool_off(int slot, int h, int Hkv, int hd) {
+  // page-major: [page][head][16][hd]
+  return (((size_t)(slot >> 4) * Hkv + h) * 16 + (slot & 15)) * hd;
+}
+
+// 8 consecutive elements of a row as float
+template <class T> __device__ __forceinline__ void load8(const T* p, float* o);
+template <> __device__ __forceinline__ void load8<float>(const float* p, float* o) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+  o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+}
+template <> __device__ __forceinline__ void load8<bf16_t>(const bf16_t* p, float* o) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    o[2 * i] = __uint_as_float(w[i] << 16);
+    o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+template <class T> __device__ __forceinline__ void store8(T* p, const float* v);
+template <> __device__ __forceinline__ void store8<float>(float* p, const float* v) {
+  reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+  reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+template <> __device__ __forceinline__ void store8<bf16_t>(bf16_t* p, const float* v) {
+  uint4 o;
+  o.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+  o.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+  o.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
+  o.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+  *reinterpret_cast<uint4*>(p) = o;
+}
+
+// Per-row sums in a fixed order.  Thread t owns the 8-element vector t of the
+// row (head t / (hd/8)); per-head partials are reduced over the hd/8 threads of
+// the head with xor shuffles, then across heads in head order by one thread.
+struct RowSums {
+  float d, nrm, cks;
+};
+
+template <int VPH>  // vectors per head = hd / 8 (8 or 16)
+__device__ __forceinline__ float head_reduce(float v) {
+#pragma unroll
+  for (int o = VPH / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// shared scratch: [Hkv][4] partials (diff^2, reuse^2, rec.reuse, rec^2)
+template <int VPH>
+__device__ RowSums row_sums(const float* a, const float* b, bool active, int Hkv, float* sh) {
+  float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+  if (active) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const float df = a[i] - b[i];
+      p0 += df * df;
+      p1 += b[i] * b[i];
+      p2 += a[i] * b[i];
+      p3 += a[i] * a[i];
+    }
+  }
+  p0 = head_reduce<VPH>(p0);
+  p1 = head_reduce<VPH>(p1);
+  p2 = head_reduce<VPH>(p2);
+  p3 = head_reduce<VPH>(p3);
+  const int t = threadIdx.x;
+  if (active && (t % VPH) == 0) {
+    const int h = t / VPH;
+    sh[h * 4 + 0] = p0;
+    sh[h * 4 + 1] = p1;
+    sh[h * 4 + 2] = p2;
+    sh[h * 4 + 3] = p3;
+  }
+  __syncthreads();
+  RowSums s{0.f, 0.f, 0.f};
+  for (int h = 0; h < Hkv; h++) {
+    s.d += sh[h * 4 + 0];
+    s.nrm += sh[h * 4 + 1];
+    const float na = sh[h * 4 + 3], nb = sh[h * 4 + 1];
+    float c;
+    if (na == 0.f && nb == 0.f) c = 1.f;
+    else if (na == 0.f || nb == 0.f) c = 0.f;
+    else c = sh[h * 4 + 2] / (sqrtf(na) * sqrtf(nb));
+    s.cks += c;
+  }
+  s.cks /= (float)Hkv;
+  return s;
+}
+
+__device__ __forceinline__ float alpha_rule(float d, float nrm) {
+  if (nrm > 0.f) return d / nrm;
+  return d == 0.f ? 0.f : 1.f;
+}
+
+// ------------------------------------------------------------------ fusion + scatter
+// One block per row; thread t owns elements 8t..8t+7 of the [Hkv*hd] row.
+
+template <class T, int VPH>
+__global__ void blend_scatter_kernel(int T_max, const int32_t* __restrict__ n_rows,
+                                     const int32_t* __restrict__ row_tok, const T* __restrict__ k_rec,
+                                     const T* __restrict__ v_rec, T* __restrict__ k_pool, T* __restrict__ v_pool,
+                                     int n_slots, const int32_t* __restrict__ src_slot,
+                                     const int32_t* __restrict__ dst_slot, int alpha_mode, float* __restrict__ alpha,
+                                     float* __restrict__ d_out, float* __restrict__ cksim_out, int Hkv, int hd) {
+  __shared__ float sh[4 * 64];
+  const int r = blockIdx.x;
+  if (r >= row_count(n_rows, T_max)) return;
+  const int g = row_tok ? row_tok[r] : r;
+  const int dst = dst_slot[r];
+  const int t = threadIdx.x;
+  const int nvec = Hkv * hd / 8;
+  const bool active = t < nvec;
+  const int h = t / VPH, e0 = (t % VPH) * 8;
+  float kr[8], vr[8], ku[8], vu[8];
+  if (active) {
+    load8<T>(k_rec + (size_t)r * Hkv * hd + t * 8, kr);
+    load8<T>(v_rec + (size_t)r * Hkv * hd + t * 8, vr);
+  }
+  const int src = src_slot ? src_slot[g] : -1;
+  const bool have_src = src_slot && src >= 0 && src < n_slots;
+  float a_use = 1.f;
+  if (src_slot) {
+    if (active) {
+      if (have_src) {
+        load8<T>(k_pool + pool_off(src, h, Hkv, hd) + e0, ku);
+        load8<T>(v_pool + pool_off(src, h, Hkv, hd) + e0, vu);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; i++) ku[i] = vu[i] = 0.f;
+      }
+    }
+    const RowSums s = row_sums<VPH>(kr, ku, active, Hkv, sh);
+    const float a_new = alpha_rule(s.d, s.nrm);
+    if (alpha_mode == KVB_ALPHA_LAG) a_use = alpha ? alpha[g] : 1.f;
+    else if (alpha_mode == KVB_ALPHA_CURRENT) a_use = a_new;
+    __syncthreads();  // every thread has read alpha[g] before it is overwritten
+    if (t == 0) {
+      if (alpha && alpha_mode != KVB_ALPHA_ONE) alpha[g] = a_new;
+      if (d_out) d_out[r] = s.d;
+      if (cksim_out) cksim_out[r] = s.cks;
+    }
+  }
+  if (!active || dst < 0 || dst >= n_slots) return;
+  float ko[8], vo[8];
+  if (src_slot && a_use != 1.f) {
+    const float b = 1.f - a_use;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      ko[i] = a_use * kr[i] + b * ku[i];
+      vo[i] = a_use * vr[i] + b * vu[i];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      ko[i] = kr[i];
+      vo[i] = vr[i];
+    }
+  }
+  store8<T>(k_pool + pool_off(dst, h, Hkv, hd) + e0, ko);
+  store8<T>(v_pool + pool_off(dst, h, Hkv, hd) + e0, vo);
+}
+
+// ------------------------------------------------------------------ deviation (layer 1)
+// d[g], alpha[g] and the 64-bit sort key (~bits(d) << 32 | g) for every token.
+
+template <class T, int VPH>
+__global__ void deviation_kernel(int n_tok, const T* __restrict__ k_rec, const T* __restrict__ k_pool, int n_slots,
+                                 const int32_t* __restrict__ reuse_slot, float* __restrict__ d,
+                                 float* __restrict__ alpha, int Hkv, int hd) {
+  __shared__ float sh[4 * 64];
+  const int g = blockIdx.x;
+  if (g >= n_tok) return;
+  const int t = threadIdx.x;
+  const int nvec = Hkv * hd / 8;
+  const bool active = t < nvec;
+  const int h = t / VPH, e0 = (t % VPH) * 8;
+  float kr[8], ku[8];
+  const int src = reuse_slot[g];
+  const bool have = src >= 0 && src < n_slots;
+  if (active) {
+    load8<T>(k_rec + (size_t)g * Hkv * hd + t * 8, kr);
+    if (have) load8<T>(k_pool + pool_off(src, h, Hkv, hd) + e0, ku);
+    else {
+#pragma unroll
+      for (int i = 0; i < 8; i++) ku[i] = 0.f;
+    }
+  }
+  const RowSums s = row_sums<VPH>(kr, ku, active, Hkv, sh);
+  if (t == 0) {
+    d[g] = s.d;
+    alpha[g] = alpha_rule(s.d, s.nrm);
+  }
+}
+
+template <class T>
+kvb_status launch_deviation(hipStream_t st, int n_tok, const void* k_rec, const void* k_pool, int n_pages,
+                            const int32_t* reuse_slot, float* d, float* alpha, int Hkv, int hd) {
+  const int nvec = Hkv * hd / 8;
+  const int threads = ((nvec + 63) / 64) * 64;
+  if (n_tok == 0) return KVB_OK;
+  if (hd == 128)
+    deviation_kernel<T, 16><<<n_tok, threads, 0, st>>>(n_tok, (const T*)k_rec, (const T*)k_pool, n_pages * 16,
+                                                        reuse_slot, d, alpha, Hkv, hd);
+  else
+    deviation_kernel<T, 8><<<n_tok, threads, 0, st>>>(n_tok, (const T*)k_rec, (const T*)k_pool, n_pages * 16,
+                                                       reuse_slot, d, alpha, Hkv, hd);
+  return check_launch("deviation_kernel");
+}
+template kvb_status launch_deviation<float>(hipStream_t, int, const void*, const void*, int, const int32_t*, float*,
+                                            float*, int, int);
+template kvb_status launch_deviation<bf16_t>(hipStream_t, int, const void*, const void*, int, const int32_t*, float*,
+                                             float*, int, int);
+
+template <class T>
+kvb_status launch_rope(hipStream_t st, int T_max, const int32_t* n_rows, const int32_t* row_tok,
+                       const int32_t* tok_pos, void* q, void* k, const kvb_model_desc* d) {
+  if (T_max == 0) return KVB_OK;
+  rope_kernel<T><<<T_max, 256, 0, st>>>(T_max, n_rows, row_tok, tok_pos, (T*)q, (T*)k, d->n_q_heads, d->n_kv_heads,
+                                        d->head_dim, d->rope_base);
+  return check_launch("rope_kernel");
+}
+template kvb_status launch_rope<float>(hipStream_t, int, const int32_t*, const int32_t*, const int32_t*, void*, void*,
+                                       const kvb_model_desc*);
+template kvb_status launch_rope<bf16_t>(hipStream_t, int, const int32_t*, const int32_t*, const int32_t*, void*, void*,
+                                        const kvb_model_desc*);
+
+// ------------------------------------------------------------------ slot maps
+
+__global__ void copy_slots_kernel(int n_tok, const int32_t* __restrict__ reuse_slot, int32_t* __restrict__ slot_map) {
+  const int g = blockIdx.x * blockDim.x + threadIdx.x;
+  if (g < n_tok) slot_map[g] = reuse_slot ? reuse_slot[g] : -1;
+}
+
+__global__ void scatter_slots_kernel(int B, int T_max, const int32_t* __restrict__ cu_rows,
+                                     const int32_t* __restrict__ row_tok, const int32_t* __restrict__ new_pages,
+                                     const int32_t* __restrict__ cu_pages, int32_t* __restrict__ slot_map,
+                                     int32_t* __restrict__ dst_slot, int n_tok) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= T_max || r >= cu_rows[B]) return;
+  int lo = 0, hi = B;  // find b with cu_rows[b] <= r < cu_rows[b+1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu_rows[mid] <= r) lo = mid;
+    else hi = mid;
+  }
+  const int b = lo;
+  const int j = r - cu_rows[b];
+  const int np = cu_pages[b + 1] - cu_pages[b];
+  int slot = -1;
+  if ((j >> 4) < np) slot = new_pages[cu_pages[b] + (j >> 4)] * 16 + (j & 15);
+  if (dst_slot) dst_slot[r] = slot;
+  const int g = row_tok ? row_tok[r] : r;
+  if (slot >= 0 && g >= 0 && g < n_tok) slot_map[g] = slot;
+}
+
+}  // namespace kvb
+
+using namespace kvb;
+
+// ------------------------------------------------------------------ entry points
+
+extern "C" kvb_status kvb_embed(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t T_max,
+                                const int32_t* n_rows, const int32_t* row_tok, const int32_t* tokens, int32_t vocab,
+                                const void* table, void* hidden) {
+  KVB_TRY(check_ctx(ctx));
+  KVB_TRY(check_desc(desc));
+  if (T_max < 0 || vocab <= 0) return fail(KVB_ERR_INVALID_ARG, "T_max < 0 or vocab <= 0");
+  if (T_max == 0) return KVB_OK;
+  KVB_CHECK_PTR(tokens, "tokens");
+  KVB_CHECK_PTR(table, "table");
+  KVB_CHECK_PTR(hidden, "hidden");
+  hipStream_t st = (hipStream_t)stream;
+  if (desc->dtype == KVB_BF16)
+    embed_kernel<bf16_t><<<T_max, 256, 0, st>>>(T_max, n_rows, row_tok, tokens, vocab, (const bf16_t*)table,
+                                                (bf16_t*)hidden, desc->d_model);
+  else
+    embed_kernel<float><<<T_max, 256, 0, st>>>(T_max, n_rows, row_tok, tokens, vocab, (const float*)table,
+                                               (float*)hidden, desc->d_model);
+  return check_launch("embed_kernel");
+}
+
+extern "C" kvb_status kvb_rope(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t T_max,
+                               const int32_t* n_rows, const int32_t* row_tok, const int32_t* tok_pos, void* q,
+                               void* k) {
+  KVB_TRY(check_ctx(ctx));
+  KVB_TRY(check_desc(desc));
+  if (T_max < 0) return fail(KVB_ERR_INVALID_ARG, "T_max < 0");
+  if (T_max == 0) return KVB_OK;
+  KVB_CHECK_PTR(tok_pos, "tok_pos");
+  KVB_CHECK_PTR(q, "q");
+  KVB_CHECK_PTR(k, "k");
+  hipStream_t st = (hipStream_t)stream;
+  if (desc->dtype == KVB_BF16) return launch_rope<bf16_t>(st, T_max, n_rows, row_tok, tok_pos, q, k, desc);
+  return launch_rope<float>(st, T_max, n_rows, row_tok, tok_pos, q, k, desc);
+}
+
+extern "C" kvb_status kvb_blend_scatter(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t T_max,
+                                        const int32_t* n_rows, const int32_t* row_tok, const void* k_rec,
+                                        const void* v_rec, void* k_pool, void* v_pool, int32_t n_pages,
+                                        const int32_t* src_slot, const int32_t* dst_slot, int32_t alpha_mode,
+                                        float* alpha, float* d_out, float* cksim_out) {
+  KVB_TRY(check_ctx(ctx));
+  KVB_TRY(check_desc(desc));
+  if (T_max < 0 || n_pages < 0) return fail(KVB_ERR_INVALID_ARG, "T_max or n_pages < 0");
+  if (alpha_mode < KVB_ALPHA_LAG || alpha_mode > KVB_ALPHA_ONE) return fail(KVB_ERR_INVALID_ARG, "bad alpha_mode");
+  if (!src_slot && (alpha_mode != KVB_ALPHA_ONE || d_out || cksim_out))
+    return fail(KVB_ERR_INVALID_ARG, "without src_slot only KVB_ALPHA_ONE with no d_out/cksim_out is allowed");
+  if (alpha_mode == KVB_ALPHA_LAG && !alpha) return fail(KVB_ERR_INVALID_ARG, "KVB_ALPHA_LAG needs alpha");
+  if ((long)n_pages * 16 > 0x7fffffffL) return fail(KVB_ERR_INVALID_ARG, "too many pages for int32 slots");
+  if (T_max == 0) return KVB_OK;
+  KVB_CHECK_PTR(k_rec, "k_rec");
+  KVB_CHECK_PTR(v_rec, "v_rec");
+  KVB_CHECK_PTR(k_pool, "k_pool");
+  KVB_CHECK_PTR(v_pool, "v_pool");
+  KVB_CHECK_PTR(dst_slot, "dst_slot");
+  const int Hkv = desc->n_kv_heads, hd = desc->head_dim;
+  const int nvec = Hkv * hd / 8;
+  if (nvec > 1024 || Hkv > 64) return fail(KVB_ERR_UNSUPPORTED, "n_kv_heads * head_dim must be <= 8192");
+  const int threads = ((nvec + 63) / 64) * 64;
+  hipStream_t st = (hipStream_t)stream;
+  const int ns = n_pages * 16;
+#define KVB_BLEND(T, VPH)                                                                                   \
+  blend_scatter_kernel<T, VPH><<<T_max, threads, 0, st>>>(T_max, n_rows, row_tok, (const T*)k_rec,         \
+                                                          (const T*)v_rec, (T*)k_pool, (T*)v_pool, ns, src_slot, \
+                                                          dst_slot, alpha_mode, alpha, d_out, cksim_out, Hkv, hd)
+  if (desc->dtype == KVB_BF16) {
+    if (hd == 128) KVB_BLEND(bf16_t, 16);
+    else KVB_BLEND(bf16_t, 8);
+  } else {
+    if (hd == 128) KVB_BLEND(float, 16);
+    else KVB_BLEND(float, 8);
+  }
+#undef KVB_BLEND
+  return check_launch("blend_scatter_kernel");
+}
+
+extern "C" kvb_status kvb_slot_map(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t B, int32_t n_tok,
+                                   int32_t T_max, const int32_t* cu_rows, const int32_t* row_tok,
+                                   const int32_t* reuse_slot, const int32_t* new_pages, const int32_t* cu_pages,
+                                   int32_t* slot_map, int32_t* dst_slot) {
+  KVB_TRY(check_ctx(ctx));
+  KVB_TRY(check_desc(desc));
+  if (B < 0 || n_tok < 0 || T_max < 0) return fail(KVB_ERR_INVALID_ARG, "negative size");
+  KVB_CHECK_PTR(slot_map, "slot_map");
+  hipStream_t st = (hipStream_t)stream;
+  if (n_tok > 0) {
+    copy_slots_kernel<<<cdiv(n_tok, 256), 256, 0, st>>>(n_tok, reuse_slot, slot_map);
+    KVB_TRY(check_launch("copy_slots_kernel"));
+  }
+  if (B == 0 || T_max == 0) return KVB_OK;
+  KVB_CHECK_PTR(cu_rows, "cu_rows");
+  KVB_CHECK_PTR(new_pages, "new_pages");
+  KVB_CHECK_PTR(cu_pages, "cu_pages");
+  scatter_slots_kernel<<<cdiv(T_max, 256), 256, 0, st>>>(B, T_max, cu_rows, row_tok, new_pages, cu_pages, slot_map,
+                                                         dst_slot, n_tok);
+  return check_launch("scatter_slots_kernel");
+}

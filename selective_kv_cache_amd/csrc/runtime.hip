@@ -1,0 +1,187 @@
+// Host runtime of the kvb library: status strings, thread-local errors,
+// context, argument checks, workspace sizing and the deterministic page
+// allocator (lowest free id first, SLIDE's preallocated new pages).
+#include <algorithm>
+#include <set>
+#include <string>
+#include <vector>
+
+#include "common.h"
+
+namespace kvb {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+kvb_status fail(kvb_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+kvb_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KVB_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return KVB_OK;
+}
+
+kvb_status check_ctx(const kvb_ctx* c) {
+  if (!c) return fail(KVB_ERR_INVALID_ARG, "ctx is NULL");
+  return KVB_OK;
+}
+
+kvb_status check_desc(const kvb_model_desc* d) {
+  if (!d) return fail(KVB_ERR_INVALID_ARG, "desc is NULL");
+  if (d->d_model <= 0 || d->n_q_heads <= 0 || d->n_kv_heads <= 0 || d->ffn <= 0)
+    return fail(KVB_ERR_INVALID_ARG, "model sizes must be positive");
+  if (d->n_kv_heads > 64) return fail(KVB_ERR_UNSUPPORTED, "n_kv_heads must be <= 64");
+  if (d->n_q_heads % d->n_kv_heads)
+    return fail(KVB_ERR_INVALID_ARG, "n_q_heads must be a multiple of n_kv_heads");
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(KVB_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (d->page_size != 16) return fail(KVB_ERR_UNSUPPORTED, "page_size must be 16");
+  if (d->dtype != KVB_F32 && d->dtype != KVB_BF16) return fail(KVB_ERR_UNSUPPORTED, "dtype must be KVB_F32 or KVB_BF16");
+  if (!(d->rms_eps >= 0.f) || !(d->rope_base > 0.f)) return fail(KVB_ERR_INVALID_ARG, "rms_eps / rope_base out of range");
+  if (d->dtype == KVB_BF16) {
+    if (d->d_model % 64 || d->ffn % 64 || (d->n_q_heads * d->head_dim) % 64)
+      return fail(KVB_ERR_UNSUPPORTED, "bf16 path needs d_model, ffn and n_q_heads*head_dim to be multiples of 64");
+  }
+  return KVB_OK;
+}
+
+static size_t esize(const kvb_model_desc* d) { return d->dtype == KVB_BF16 ? 2 : 4; }
+
+size_t ws_mlp_bytes(const kvb_model_desc* d, int32_t max_rows) {
+  // h1 [T, d] and u [T, F] in storage type
+  return align_up((size_t)max_rows * d->d_model * esize(d), 256) +
+         align_up((size_t)max_rows * d->ffn * esize(d), 256);
+}
+
+size_t ws_topk_bytes(int32_t max_tokens, int32_t max_requests) {
+  // sorted keys u64 [n_tok + pad], rank/flag int32 [n_tok], counts int32 [2B + 2]
+  size_t n = (size_t)max_tokens;
+  return align_up(n * 8 + 2048 * 8, 256) + align_up(n * 4, 256) + align_up(((size_t)max_requests * 2 + 2) * 4, 256);
+}
+
+size_t ws_refresh_bytes(int32_t max_tokens, int32_t max_requests) {
+  return align_up((size_t)max_tokens * 4, 256) + align_up(((size_t)max_requests * 2 + 2) * 4, 256);
+}
+
+size_t ws_attn_bytes(const kvb_model_desc*, int32_t, int32_t) { return 0; }
+
+}  // namespace kvb
+
+using namespace kvb;
+
+extern "C" {
+
+const char* kvb_status_string(kvb_status s) {
+  switch (s) {
+    case KVB_OK: return "ok";
+    case KVB_ERR_INVALID_ARG: return "invalid argument";
+    case KVB_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KVB_ERR_HIP: return "HIP error";
+    case KVB_ERR_CAPACITY: return "page pool exhausted";
+    case KVB_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+const char* kvb_last_error(void) { return g_last_error.c_str(); }
+
+kvb_status kvb_create(int32_t device, kvb_ctx** out) {
+  if (!out) return fail(KVB_ERR_INVALID_ARG, "out is NULL");
+  int n = 0;
+  hipError_t e = hipGetDeviceCount(&n);
+  if (e != hipSuccess) return fail(KVB_ERR_HIP, std::string("hipGetDeviceCount: ") + hipGetErrorString(e));
+  if (device < 0 || device >= n) return fail(KVB_ERR_INVALID_ARG, "device index out of range");
+  Ctx* c = new Ctx();
+  c->device = device;
+  int cu = 0;
+  if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, device) == hipSuccess && cu > 0) c->n_cu = cu;
+  *out = reinterpret_cast<kvb_ctx*>(c);
+  return KVB_OK;
+}
+
+kvb_status kvb_destroy(kvb_ctx* ctx) {
+  delete reinterpret_cast<Ctx*>(ctx);
+  return KVB_OK;
+}
+
+kvb_status kvb_workspace_size(kvb_ctx* ctx, const kvb_model_desc* desc, int32_t max_rows, int32_t max_tokens,
+                              int32_t max_requests, size_t* bytes) {
+  KVB_TRY(check_ctx(ctx));
+  KVB_TRY(check_desc(desc));
+  KVB_CHECK_PTR(bytes, "bytes");
+  if (max_rows < 0 || max_tokens < 0 || max_requests < 0) return fail(KVB_ERR_INVALID_ARG, "negative size");
+  size_t b = ws_mlp_bytes(desc, max_rows);
+  b = std::max(b, ws_topk_bytes(max_tokens, max_requests));
+  b = std::max(b, ws_refresh_bytes(max_tokens, max_requests));
+  b = std::max(b, ws_attn_bytes(desc, max_rows, max_tokens));
+  *bytes = b;
+  return KVB_OK;
+}
+
+// ------------------------------------------------------------ page allocator
+
+struct kvb_pool {
+  int32_t n_pages;
+  std::set<int32_t> free_ids;
+  std::vector<uint8_t> used;
+};
+
+kvb_status kvb_pool_create(int32_t n_pages, kvb_pool** out) {
+  if (!out) return fail(KVB_ERR_INVALID_ARG, "out is NULL");
+  if (n_pages < 0) return fail(KVB_ERR_INVALID_ARG, "n_pages < 0");
+  kvb_pool* p = new kvb_pool();
+  p->n_pages = n_pages;
+  p->used.assign(n_pages, 0);
+  for (int32_t i = 0; i < n_pages; i++) p->free_ids.insert(p->free_ids.end(), i);
+  *out = p;
+  return KVB_OK;
+}
+
+kvb_status kvb_pool_destroy(kvb_pool* pool) {
+  delete pool;
+  return KVB_OK;
+}
+
+kvb_status kvb_pool_alloc(kvb_pool* pool, int32_t n, int32_t* out_ids) {
+  if (!pool) return fail(KVB_ERR_INVALID_ARG, "pool is NULL");
+  if (n < 0) return fail(KVB_ERR_INVALID_ARG, "n < 0");
+  if (n > 0 && !out_ids) return fail(KVB_ERR_INVALID_ARG, "out_ids is NULL");
+  if ((size_t)n > pool->free_ids.size())
+    return fail(KVB_ERR_CAPACITY, "page pool exhausted: need " + std::to_string(n) + ", free " +
+                                      std::to_string(pool->free_ids.size()));
+  auto it = pool->free_ids.begin();
+  for (int32_t i = 0; i < n; i++) {
+    out_ids[i] = *it;
+    pool->used[*it] = 1;
+    it = pool->free_ids.erase(it);
+  }
+  return KVB_OK;
+}
+
+kvb_status kvb_pool_release(kvb_pool* pool, int32_t n, const int32_t* ids) {
+  if (!pool) return fail(KVB_ERR_INVALID_ARG, "pool is NULL");
+  if (n < 0) return fail(KVB_ERR_INVALID_ARG, "n < 0");
+  if (n > 0 && !ids) return fail(KVB_ERR_INVALID_ARG, "ids is NULL");
+  for (int32_t i = 0; i < n; i++) {
+    int32_t id = ids[i];
+    if (id < 0 || id >= pool->n_pages || !pool->used[id])
+      return fail(KVB_ERR_INVALID_ARG, "releasing page " + std::to_string(id) + " that is not allocated");
+  }
+  for (int32_t i = 0; i < n; i++) {
+    pool->used[ids[i]] = 0;
+    pool->free_ids.insert(ids[i]);
+  }
+  return KVB_OK;
+}
+
+kvb_status kvb_pool_free_count(const kvb_pool* pool, int32_t* out) {
+  if (!pool || !out) return fail(KVB_ERR_INVALID_ARG, "pool or out is NULL");
+  *out = (int32_t)pool->free_ids.size();
+  return KVB_OK;
+}
+
+}  // extern "C"

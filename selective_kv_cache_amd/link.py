@@ -1,0 +1,312 @@
+"""Host orchestration of the compile and link steps on the HIP path.
+
+This module only plans memory (page allocation through the library's C++
+allocator, index arrays) and issues the C-ABI calls in order on one HIP
+stream; every step of the method runs in the library's kernels.  There is no
+host synchronisation inside a link step: selection sizes produced on the
+device (|S_k| after the top-k and after each refresh) reach the later kernels
+as device-side row counts.
+
+Token spaces.  Compile: the unique chunk instances concatenated, each its own
+segment (positions from 0, keys visible from the chunk start).  Link: the
+requests concatenated (token g of request b at position g - cu_tok[b], keys
+visible from cu_tok[b]).
+
+Page plan (CacheSlide page, SLIDE implementation paragraph; 16-token pages):
+compile pages per chunk instance and layer, then per request and layer the
+link's new pages, N_r tokens' worth at layer 1 and floor(ratio * N_r) at later
+layers (CacheSlide), or |S_r| at every layer (LegoLink).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import Callable, List, Optional
+
+import numpy as np
+import torch
+
+from . import _lib as K
+
+PAGE = 16
+
+
+def _i32(x, device) -> torch.Tensor:
+    return torch.as_tensor(np.asarray(x, dtype=np.int32), device=device)
+
+
+def _npages(n: int) -> int:
+    return (int(n) + PAGE - 1) // PAGE
+
+
+class Model:
+    """Weights of a decoder stack resident on the device (caller-provided tensors)."""
+
+    def __init__(self, shape, embedding: torch.Tensor, layers: List[dict]):
+        self.shape = shape
+        self.embedding = embedding
+        self.layers = layers
+
+
+@dataclass
+class LinkConfig:
+    mode: str = "cacheslide"          # "cacheslide" or "legolink"
+    ratio: float = 0.26
+    tau: float = 0.12
+    period: int = 4
+    lego_k: int = 32
+    alpha_mode: int = K.KVB_ALPHA_LAG
+    refresh_rule: int = K.KVB_REFRESH_LITERAL
+
+
+class LinkEngine:
+    """Plans and runs the compile and link steps of a batch of requests.
+
+    requests: objects with `.chunks`, each chunk with `.uid` and `.tokens`
+    (int array); chunks sharing a uid are compiled once and their pages are
+    shared read-only by every request that splices them.
+    """
+
+    def __init__(self, model: Model, requests, cfg: LinkConfig, device="cuda:0", stream=None):
+        self.model, self.cfg, self.device = model, cfg, torch.device(device)
+        s = model.shape
+        self.shape = s
+        self.L = s.n_layers
+        self.desc = K.model_desc(s)
+        self.ctx = K.kvb_create(self.device.index or 0)
+        self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
+        self.sh = K.stream_handle(self.stream)
+        self.tdtype = torch.bfloat16 if s.dtype == "bf16" else torch.float32
+        self.scale = 1.0 / math.sqrt(s.head_dim)
+        dev = self.device
+
+        # ---------------- token spaces
+        chunks, seen = [], set()
+        for r in requests:
+            for c in r.chunks:
+                if c.uid not in seen:
+                    seen.add(c.uid)
+                    chunks.append(c)
+        self.chunks = chunks
+        self.B = len(requests)
+        lens_c = [len(c.tokens) for c in chunks]
+        self.Nc = int(sum(lens_c))
+        cu_c = np.concatenate([[0], np.cumsum(lens_c)]).astype(np.int64)
+        self.req_lens = [int(sum(len(c.tokens) for c in r.chunks)) for r in requests]
+        self.N = int(sum(self.req_lens))
+        cu_t = np.concatenate([[0], np.cumsum(self.req_lens)]).astype(np.int64)
+        self.cu_tok_h = cu_t
+        tok_c = np.concatenate([np.asarray(c.tokens, dtype=np.int32) for c in chunks])
+        tok_l = np.concatenate([np.asarray(c.tokens, dtype=np.int32) for r in requests for c in r.chunks])
+        pos_c = np.concatenate([np.arange(n) for n in lens_c])
+        lo_c = np.concatenate([np.full(n, cu_c[i]) for i, n in enumerate(lens_c)])
+        pos_l = np.concatenate([np.arange(n) for n in self.req_lens])
+        lo_l = np.concatenate([np.full(n, cu_t[b]) for b, n in enumerate(self.req_lens)])
+
+        # ---------------- page plan (host allocator in the library)
+        if cfg.mode == "cacheslide":
+            self.k_cap = [int(math.floor(cfg.ratio * n)) for n in self.req_lens]
+            per_layer = lambda l, b: self.req_lens[b] if l == 1 else self.k_cap[b]
+        elif cfg.mode == "legolink":
+            rows = []
+            for r, start in zip(requests, cu_t[:-1]):
+                s0 = 0
+                rr = []
+                for ci, c in enumerate(r.chunks):
+                    if ci > 0:
+                        rr.extend(range(s0, s0 + min(cfg.lego_k, len(c.tokens))))
+                    s0 += len(c.tokens)
+                rows.append(np.asarray(rr, dtype=np.int64) + start)
+            self.lego_rows = rows
+            self.k_cap = [len(x) for x in rows]
+            per_layer = lambda l, b: self.k_cap[b]
+        else:
+            raise ValueError(cfg.mode)
+        n_compile_pages = sum(_npages(n) for n in lens_c) * self.L
+        n_link_pages = sum(_npages(per_layer(l, b)) for l in range(1, self.L + 1) for b in range(self.B))
+        self.n_pages = n_compile_pages + n_link_pages
+        self.pool = K.kvb_pool_create(self.n_pages)
+        comp_pages = {}
+        for c in chunks:
+            comp_pages[c.uid] = [K.kvb_pool_alloc(self.pool, _npages(len(c.tokens))) for _ in range(self.L)]
+        link_pages = [[None] * (self.L + 1) for _ in range(self.B)]
+        for b in range(self.B):
+            for l in range(1, self.L + 1):
+                link_pages[b][l] = K.kvb_pool_alloc(self.pool, _npages(per_layer(l, b)))
+        self.comp_pages, self.link_pages = comp_pages, link_pages
+
+        def slots(pages, n):
+            j = np.arange(n)
+            return np.asarray(pages, dtype=np.int64)[j // PAGE] * PAGE + j % PAGE
+
+        comp_slot = np.zeros((self.L, self.Nc), dtype=np.int32)
+        for i, c in enumerate(chunks):
+            for l in range(self.L):
+                comp_slot[l, cu_c[i]:cu_c[i + 1]] = slots(comp_pages[c.uid][l], len(c.tokens))
+        reuse_slot = np.zeros((self.L, self.N), dtype=np.int32)
+        for b, r in enumerate(requests):
+            g = cu_t[b]
+            for c in r.chunks:
+                n = len(c.tokens)
+                for l in range(self.L):
+                    reuse_slot[l, g:g + n] = slots(comp_pages[c.uid][l], n)
+                g += n
+        self.comp_slot_h, self.reuse_slot_h = comp_slot, reuse_slot
+        new_pages, cu_pages = [None], [None]
+        for l in range(1, self.L + 1):
+            pl = [link_pages[b][l] for b in range(self.B)]
+            new_pages.append(_i32(np.concatenate([np.asarray(p, dtype=np.int64) for p in pl]) if sum(map(len, pl))
+                                  else np.zeros(1), dev))
+            cu_pages.append(_i32(np.concatenate([[0], np.cumsum([len(p) for p in pl])]), dev))
+        self.new_pages, self.cu_pages = new_pages, cu_pages
+
+        # ---------------- device arrays
+        self.tok_c = _i32(tok_c, dev)
+        self.tok_l = _i32(tok_l, dev)
+        self.pos_c, self.lo_c = _i32(pos_c, dev), _i32(lo_c, dev)
+        self.pos_l, self.lo_l = _i32(pos_l, dev), _i32(lo_l, dev)
+        self.cu_tok = _i32(cu_t, dev)
+        self.comp_slot = _i32(comp_slot, dev)
+        self.reuse_slot = _i32(reuse_slot, dev)
+        self.k_cap_d = _i32(self.k_cap, dev)
+        self.T_sel = int(sum(self.k_cap))
+        if cfg.mode == "legolink":
+            sel = np.concatenate(self.lego_rows) if self.T_sel else np.zeros(1)
+            self.lego_sel = _i32(sel, dev)
+            self.lego_cu = _i32(np.concatenate([[0], np.cumsum(self.k_cap)]), dev)
+
+        # ---------------- buffers
+        d, Hq, Hkv, hd = s.d_model, s.n_q_heads, s.n_kv_heads, s.head_dim
+        rows_max = max(self.Nc, self.N, 1)
+        td = self.tdtype
+        self.k_pool = torch.zeros((self.n_pages, Hkv, PAGE, hd), dtype=td, device=dev)
+        self.v_pool = torch.zeros_like(self.k_pool)
+        self.hidden_c = torch.zeros((max(self.Nc, 1), d), dtype=td, device=dev)
+        self.hidden = torch.zeros((max(self.N, 1), d), dtype=td, device=dev)
+        self.q = torch.empty((rows_max, Hq, hd), dtype=td, device=dev)
+        self.k = torch.empty((rows_max, Hkv, hd), dtype=td, device=dev)
+        self.v = torch.empty((rows_max, Hkv, hd), dtype=td, device=dev)
+        self.o = torch.empty((rows_max, Hq * hd), dtype=td, device=dev)
+        nt = max(self.N, 1)
+        self.alpha = torch.zeros(nt, dtype=torch.float32, device=dev)
+        self.d = torch.zeros(nt, dtype=torch.float32, device=dev)
+        self.ranking = torch.zeros(nt, dtype=torch.int32, device=dev)
+        self.s_count = torch.zeros(self.B, dtype=torch.int32, device=dev)
+        self.cursor = torch.zeros(self.B, dtype=torch.int32, device=dev)
+        self.sel = [torch.zeros(nt, dtype=torch.int32, device=dev) for _ in range(2)]
+        self.cu_rows = [torch.zeros(self.B + 1, dtype=torch.int32, device=dev) for _ in range(2)]
+        self.dev_l = torch.zeros(max(self.T_sel, 1), dtype=torch.float32, device=dev)
+        self.cksim = torch.zeros(max(self.T_sel, 1), dtype=torch.float32, device=dev)
+        self.slot_map = torch.zeros(nt, dtype=torch.int32, device=dev)
+        self.dst_slot = torch.zeros(rows_max, dtype=torch.int32, device=dev)
+        self.ws_bytes = K.kvb_workspace_size(self.ctx, self.desc, rows_max, max(self.N, self.Nc), self.B)
+        self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
+        self.cur = 0
+
+    # ------------------------------------------------------------------ helpers
+    def close(self):
+        if getattr(self, "pool", None) is not None:
+            K.kvb_pool_destroy(self.pool)
+            self.pool = None
+        if getattr(self, "ctx", None) is not None:
+            K.kvb_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _n_rows_ptr(self, which: int) -> int:
+        return self.cu_rows[which].data_ptr() + 4 * self.B
+
+    # ------------------------------------------------------------------ compile step
+    def run_compile(self):
+        """Prefill every chunk instance alone from position 0 into its compile pages."""
+        c, sh, ds, Nc = self.ctx, self.sh, self.desc, self.Nc
+        if Nc == 0:
+            return
+        m = self.model
+        K.kvb_embed(c, sh, ds, Nc, None, None, self.tok_c, self.shape.vocab, m.embedding, self.hidden_c)
+        for l in range(1, self.L + 1):
+            W = m.layers[l - 1]
+            K.kvb_qkv_proj(c, sh, ds, Nc, None, None, self.hidden_c, W["norm1"], W["w_qkv"], self.pos_c,
+                           self.q, self.k, self.v)
+            K.kvb_blend_scatter(c, sh, ds, Nc, None, None, self.k, self.v, self.k_pool, self.v_pool, self.n_pages,
+                                None, self.comp_slot[l - 1], K.KVB_ALPHA_ONE, None, None, None)
+            if l < self.L:
+                K.kvb_sparse_query_attn(c, sh, ds, Nc, None, None, self.lo_c, self.q, self.k_pool, self.v_pool,
+                                        self.n_pages, self.comp_slot[l - 1], self.scale, self.o, self.ws,
+                                        self.ws_bytes)
+                K.kvb_mlp(c, sh, ds, Nc, None, None, self.o, W["w_o"], self.hidden_c, W["norm2"], W["w_gate_up"],
+                          W["w_down"], self.ws, self.ws_bytes)
+
+    # ------------------------------------------------------------------ link step
+    def run_link(self, hook: Optional[Callable] = None):
+        if self.cfg.mode == "cacheslide":
+            self._link_cacheslide(hook)
+        else:
+            self._link_static(hook)
+
+    def _layer_rows(self, l, T, n_rows, rows, cu_rows, src_slot, alpha_mode, alpha, d_out, cksim_out):
+        """One recompute layer for the given rows: slot map, Q/K/V + RoPE, fusion and
+        scatter into new pages, attention over the spliced KV, O-proj + MLP."""
+        c, sh, ds, W = self.ctx, self.sh, self.desc, self.model.layers[l - 1]
+        K.kvb_slot_map(c, sh, ds, self.B, self.N, T, cu_rows, rows, self.reuse_slot[l - 1], self.new_pages[l],
+                       self.cu_pages[l], self.slot_map, self.dst_slot)
+        K.kvb_qkv_proj(c, sh, ds, T, n_rows, rows, self.hidden, W["norm1"], W["w_qkv"], self.pos_l, self.q, self.k,
+                       self.v)
+        K.kvb_blend_scatter(c, sh, ds, T, n_rows, rows, self.k, self.v, self.k_pool, self.v_pool, self.n_pages,
+                            src_slot, self.dst_slot, alpha_mode, alpha, d_out, cksim_out)
+        K.kvb_sparse_query_attn(c, sh, ds, T, n_rows, rows, self.lo_l, self.q, self.k_pool, self.v_pool,
+                                self.n_pages, self.slot_map, self.scale, self.o, self.ws, self.ws_bytes)
+        K.kvb_mlp(c, sh, ds, T, n_rows, rows, self.o, W["w_o"], self.hidden, W["norm2"], W["w_gate_up"],
+                  W["w_down"], self.ws, self.ws_bytes)
+
+    def _link_cacheslide(self, hook):
+        c, sh, ds, N, B = self.ctx, self.sh, self.desc, self.N, self.B
+        cfg = self.cfg
+        K.kvb_embed(c, sh, ds, N, None, None, self.tok_l, self.shape.vocab, self.model.embedding, self.hidden)
+        # layer 1: every token recomputed at its spliced position, written to layer-1 new pages
+        self._layer_rows(1, N, None, None, self.cu_tok, None, K.KVB_ALPHA_ONE, None, None, None)
+        K.kvb_deviation_topk(c, sh, ds, B, N, self.cu_tok, self.k, self.k_pool, self.n_pages, self.reuse_slot[0],
+                             self.k_cap_d, self.d, self.alpha, self.ranking, self.s_count, self.sel[0],
+                             self.cu_rows[0], self.cursor, self.ws, self.ws_bytes)
+        self.cur = 0
+        if hook:
+            hook(1, self)
+        T = self.T_sel
+        for l in range(2, self.L + 1):
+            cur = self.cur
+            refresh = (l % cfg.period == 0) and l < self.L
+            self._layer_rows(l, T, self._n_rows_ptr(cur), self.sel[cur], self.cu_rows[cur], self.reuse_slot[l - 1],
+                             cfg.alpha_mode, self.alpha, self.dev_l, self.cksim if refresh else None)
+            if hook:
+                hook(l, self)
+            if refresh:
+                K.kvb_cosine_refresh(c, sh, ds, B, N, self.cu_tok, T, self.cu_rows[cur], self.sel[cur], self.cksim,
+                                     cfg.tau, cfg.refresh_rule, self.ranking, self.s_count, self.cursor,
+                                     self.sel[1 - cur], self.cu_rows[1 - cur], self.ws, self.ws_bytes)
+                self.cur = 1 - cur
+                if hook:
+                    hook(("refresh", l), self)
+
+    def _link_static(self, hook):
+        c, sh, ds, T = self.ctx, self.sh, self.desc, self.T_sel
+        if T == 0:
+            return
+        K.kvb_embed(c, sh, ds, T, None, self.lego_sel, self.tok_l, self.shape.vocab, self.model.embedding,
+                    self.hidden)
+        for l in range(1, self.L + 1):
+            self._layer_rows(l, T, None, self.lego_sel, self.lego_cu, None, K.KVB_ALPHA_ONE, None, None, None)
+            if hook:
+                hook(l, self)
+
+    # ------------------------------------------------------------------ results
+    def selected(self, which: Optional[int] = None) -> List[np.ndarray]:
+        """Current S_k per request (host copy, synchronises)."""
+        w = self.cur if which is None else which
+        cu = self.cu_rows[w].cpu().numpy()
+        sel = self.sel[w].cpu().numpy()
+        return [sel[cu[b]:cu[b + 1]].copy() for b in range(self.B)]
