@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Link-step benchmark on one MI355X.
+
+One step = one whole link step (splice + slot maps, layer-1 full recompute,
+deviation + top-k, selective recompute of layers 2..L with fusion, scatter
+into new pages, attention and MLP, cosine refreshes) of one batch of the
+workload, with weights, the compiled cache and all index arrays already
+resident in HBM.  The compile step and the page plan are done before timing.
+
+Prints one JSON line: selected-tokens/s and latency, the roofline of the
+dominant kernel (its average launch duration measured with HIP events on the
+engine's stream during the timed steps), a per-kernel breakdown, and the CPU
+oracle timed on a bounded sample on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mistral7b-cacheslide-8k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-only", action="store_true", help="warmup + timed steps only (for rocprofv3)")
+    return ap.parse_args()
+
+
+def kernel_work(eng, layer_rows, layer_pos, shape):
+    """Algorithmic FLOPs / bytes per kernel for one link step, from the realised rows per layer."""
+    s = shape
+    d, F, Hq, Hkv, hd = s.d_model, s.ffn, s.n_q_heads, s.n_kv_heads, s.head_dim
+    esz = 2 if s.dtype == "bf16" else 4
+    w = {k: 0.0 for k in ("gemm_qkv", "gemm_oproj", "gemm_swiglu", "gemm_down", "attention", "blend_scatter",
+                          "deviation", "rope", "embed")}
+    rows_per_layer = []
+    for l, (T, pos_lo) in enumerate(zip(layer_rows, layer_pos), start=1):
+        rows_per_layer.append(T)
+        w["gemm_qkv"] += 2.0 * T * d * (Hq + 2 * Hkv) * hd
+        w["gemm_oproj"] += 2.0 * T * Hq * hd * d
+        w["gemm_swiglu"] += 2.0 * T * d * 2 * F
+        w["gemm_down"] += 2.0 * T * F * d
+        w["attention"] += 4.0 * Hq * hd * float(pos_lo)
+        w["blend_scatter"] += T * (6.0 * Hkv * hd * esz + 16.0)
+        w["rope"] += T * 2.0 * (Hq + Hkv) * hd * esz
+    w["deviation"] += eng.N * (2.0 * Hkv * hd * esz + 16.0)
+    w["embed"] += eng.N * 2.0 * d * esz
+    return w, rows_per_layer
+
+
+BOUND = {"gemm_qkv": "mfma", "gemm_oproj": "mfma", "gemm_swiglu": "mfma", "gemm_down": "mfma", "attention": "mfma",
+         "blend_scatter": "hbm", "deviation": "hbm", "rope": "hbm", "embed": "hbm"}
+
+
+def cpu_baseline(w, eng, rec_state, budget_note):
+    """Time the oracle as it stands on a bounded sample: one selective layer (l = 2)
+    over every selected row, fed the GPU's layer-1 state; scale to the link step."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    import workloads as wl
+    from oracle import link as OL
+
+    s = w.shape
+    st = rec_state
+    sel = st["sel"]
+    W2 = {k: OL.as_f64(v) for k, v in wl.layer_weights(w, 2, "cuda:0").items()}
+    sm = eng.reuse_slot_h[1]
+    idx = torch.as_tensor(sm, device=eng.k_pool.device, dtype=torch.int64)
+    Kr = OL.as_f64(eng.k_pool[idx // 16, :, idx % 16, :])
+    Vr = OL.as_f64(eng.v_pool[idx // 16, :, idx % 16, :])
+    state = OL.WCAState(h=OL.as_f64(st["hidden"]), alpha=OL.as_f64(st["alpha"]), d=OL.as_f64(st["d"]),
+                        ranking=[], cursor=0, S_k=[int(x) for x in sel])
+    t0 = time.perf_counter()
+    OL.wca_layer(state, 2, s, W2, Kr, Vr, w.tau, w.period, s.n_layers)
+    t2 = time.perf_counter() - t0
+    info = threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    d, F, Hq, Hkv, hd = s.d_model, s.ffn, s.n_q_heads, s.n_kv_heads, s.head_dim
+    N, k = eng.N, len(sel)
+    per_row = 2.0 * (d * (Hq + 2 * Hkv) * hd + Hq * hd * d + 3 * d * F)
+    f2 = k * per_row + 4.0 * Hq * hd * float(np.sum(np.asarray(sel) + 1))
+    f1 = N * per_row + 2.0 * Hq * hd * N * (N + 1)
+    t_link = t2 * (s.n_layers - 1) + t2 * f1 / f2
+    return {"value": k / t_link, "unit": "selected-tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"oracle layer 2 over all {k} selected rows of the {N}-token request (float64 numpy, "
+                       f"{threads} BLAS threads): {t2:.2f} s; link time scaled as T2*(L-1) + T2*FLOPs(layer 1)/"
+                       f"FLOPs(layer 2) = {t_link:.1f} s"),
+            "measured_s": t2, "extrapolated_link_s": t_link}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    from selective_kv_cache_amd import _lib as K
+    from selective_kv_cache_amd.link import LinkConfig, LinkEngine, Model
+
+    K.load()  # fails loudly if the HIP library is not built
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = "cuda:0"
+    w = wl.NAMED[args.workload]()
+    s = w.shape
+    t_setup = time.perf_counter()
+    E = wl.embedding_table(w, dev)
+    layers = [wl.layer_weights(w, l, dev) for l in range(1, s.n_layers + 1)]
+    cfg = LinkConfig(mode=w.mode, ratio=w.ratio, tau=w.tau, period=w.period, lego_k=w.lego_k)
+    eng = LinkEngine(Model(s, E, layers), w.requests, cfg, device=dev)
+    eng.run_compile()
+    torch.cuda.synchronize()
+    print(f"# setup {time.perf_counter() - t_setup:.1f}s: {w.name}, N={eng.N}, pages={eng.n_pages}", file=sys.stderr,
+          flush=True)
+
+    # realised rows / positions per layer (deterministic): one recorded run
+    layer_rows, layer_pos, state1 = [], [], {}
+
+    def hook(key, e):
+        if isinstance(key, tuple):
+            return
+        torch.cuda.synchronize()
+        if key == 1 and cfg.mode == "cacheslide":
+            layer_rows.append(e.N)
+            layer_pos.append(float(sum(n * (n + 1) / 2 for n in e.req_lens)))
+            cu = e.cu_rows[e.cur].cpu().numpy()
+            state1.update(hidden=e.hidden.clone(), alpha=e.alpha.clone(), d=e.d.clone(),
+                          sel=e.sel[e.cur][:cu[-1]].cpu().numpy().copy())
+            return
+        if cfg.mode == "cacheslide":
+            cu = e.cu_rows[e.cur].cpu().numpy()
+            sel = e.sel[e.cur][:cu[-1]].cpu().numpy()
+        else:
+            cu = e.lego_cu.cpu().numpy()
+            sel = e.lego_sel[:cu[-1]].cpu().numpy()
+        lo = e.lo_l.cpu().numpy()
+        layer_rows.append(int(cu[-1]))
+        layer_pos.append(float(np.sum(sel - lo[sel] + 1)))
+
+    eng.run_link(hook=hook)
+    torch.cuda.synchronize()
+    work, rows_per_layer = kernel_work(eng, layer_rows, layer_pos, s)
+    # selected tokens of the link step: |S_k| chosen at layer 1 (CacheSlide) or the static set (LegoLink)
+    n_selected = len(state1["sel"]) if cfg.mode == "cacheslide" else eng.T_sel
+
+    # per-kernel breakdown (untimed pass, every launch bracketed)
+    for _ in range(max(args.warmup, 1)):
+        eng.run_link()
+    K.kvb_timing_enable(eng.ctx, "")
+    eng.run_link()
+    breakdown = K.kvb_timing_read(eng.ctx)
+    K.kvb_timing_enable(eng.ctx, None)
+    dominant = max(breakdown, key=lambda k: breakdown[k]["ms"])
+
+    # timed steps: HIP events on the engine stream around each step; the dominant
+    # kernel's launches are bracketed with events as they run
+    st = eng.stream
+    torch.cuda.synchronize()
+    K.kvb_timing_enable(eng.ctx, dominant)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(st)
+        eng.run_link()
+        b.record(st)
+    torch.cuda.synchronize()
+    step_ms = [a.elapsed_time(b) for a, b in ev]
+    dom = K.kvb_timing_read(eng.ctx)[dominant]
+    K.kvb_timing_enable(eng.ctx, None)
+    if args.profile_only:
+        print(json.dumps({"profile_only": True, "ms_per_step": float(np.mean(step_ms))}), flush=True)
+        return
+    ms = float(np.mean(step_ms))
+    dom_avg_ms = dom["ms"] / dom["count"]
+    launches_per_step = dom["count"] / args.steps
+    dom_work_per_launch = work[dominant] / launches_per_step
+    bound = BOUND.get(dominant, "mfma")
+    if bound == "mfma":
+        achieved = dom_work_per_launch / (dom_avg_ms * 1e-3) / 1e12
+        peak = PEAK_BF16_TFLOPS if s.dtype == "bf16" else PEAK_FP32_TFLOPS
+        unit = "TFLOP/s"
+    else:
+        achieved = dom_work_per_launch / (dom_avg_ms * 1e-3) / 1e9
+        peak, unit = PEAK_HBM_GBS, "GB/s"
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tfile):
+        try:
+            import hashlib
+            t = json.load(open(tfile))
+            src = os.path.join(ROOT, "selective_kv_cache_amd", "csrc", t.get("source", ""))
+            cur = hashlib.sha256(open(src, "rb").read()).hexdigest() if os.path.exists(src) else None
+            if t.get("kernel") == dominant and t.get("workload") == w.name and t.get("source_sha256") == cur:
+                traffic = t.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+    per_kernel = {}
+    for name, v in breakdown.items():
+        b = BOUND.get(name)
+        entry = {"ms_per_step": round(v["ms"], 4), "launches": v["count"]}
+        if b and work.get(name):
+            if b == "mfma":
+                a_ = work[name] / (v["ms"] * 1e-3) / 1e12
+                entry.update(achieved_tflops=round(a_, 1), frac=round(a_ / PEAK_BF16_TFLOPS, 4))
+            else:
+                a_ = work[name] / (v["ms"] * 1e-3) / 1e9
+                entry.update(achieved_gbs=round(a_, 1), frac=round(a_ / PEAK_HBM_GBS, 4))
+        per_kernel[name] = entry
+    B = eng.B
+    out = {
+        "metric": "link-step selected-tokens/s",
+        "value": n_selected / (ms * 1e-3),
+        "unit": "selected-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "latency_ms_per_request": ms / B,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": s.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "mode": cfg.mode, "requests": B, "n_tokens": eng.N, "n_layers": s.n_layers,
+                   "selected": n_selected, "ratio": w.ratio, "tau": w.tau,
+                   "recomputed_row_layers": int(sum(rows_per_layer))},
+        "roofline": {"kernel": dominant, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+                     "frac": achieved / peak, "traffic": traffic, "avg_launch_ms": dom_avg_ms,
+                     "work_per_launch": dom_work_per_launch},
+        "kernels": per_kernel,
+        "step_ms_min_max": [float(np.min(step_ms)), float(np.max(step_ms))],
+    }
+    if not args.no_cpu_baseline and cfg.mode == "cacheslide":
+        try:
+            out["cpu_baseline"] = cpu_baseline(w, eng, state1, None)
+        except Exception as e:  # the GPU figure stands; say why the CPU leg is missing
+            out["cpu_baseline"] = {"value": None, "error": repr(e)}
+    print(json.dumps(out), flush=True)
+    eng.close()
+
+
+if __name__ == "__main__":
+    main()

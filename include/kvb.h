@@ -107,6 +107,20 @@ kvb_status kvb_destroy(kvb_ctx* ctx);
 kvb_status kvb_workspace_size(kvb_ctx* ctx, const kvb_model_desc* desc, int32_t max_rows,
                               int32_t max_tokens, int32_t max_requests, size_t* bytes);
 
+/* Launch timing (tracing).  With filter != NULL, every later kernel launch of
+ * this context whose kernel name contains `filter` ("" = all) is bracketed with
+ * HIP events on its stream; filter == NULL turns timing off.  Kernel names:
+ * embed, gemm_qkv, rope, blend_scatter, attention, gemm_oproj, gemm_swiglu,
+ * gemm_down, deviation, topk_sort, topk_rank, topk_compact, refresh_flag,
+ * refresh_compact, slot_copy, slot_scatter. */
+kvb_status kvb_timing_enable(kvb_ctx* ctx, const char* filter);
+/* Waits for the recorded events and folds them into per-kernel totals, then
+ * sets *needed to the size of the JSON text {"name": {"count": n, "ms": t}, ...}
+ * (first-seen order, NUL included).  If buf holds at least that many bytes the
+ * text is copied and the totals are cleared; otherwise they are kept (call
+ * again with a large enough buffer). */
+kvb_status kvb_timing_read(kvb_ctx* ctx, char* buf, size_t len, size_t* needed);
+
 /* --------------------------------------------------- host page allocator
  * Deterministic allocator over page ids 0..n_pages-1: kvb_pool_alloc hands out
  * the n lowest free ids in ascending order, or fails with KVB_ERR_CAPACITY

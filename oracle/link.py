@@ -126,7 +126,7 @@ def wca_layer1(request, shape, E, W1: dict, reuse_K1: np.ndarray, k_cap: int):
     d = Sel.deviation(k, reuse_K1)
     alpha = Sel.alpha_of(d, Sel.row_sq(reuse_K1))
     ranking, S_k, cursor = Sel.top_k(d, k_cap)
-    out = dict(q=q, k=k, v=v, o=o, h=h2, d=d, alpha=alpha, ranking=ranking, S_k=S_k, cursor=cursor)
+    out = dict(q=q, k=k, v=v, o=o, h=h2.copy(), d=d, alpha=alpha, ranking=ranking, S_k=S_k, cursor=cursor)
     return WCAState(h=h2, alpha=alpha.copy(), d=d, ranking=ranking, cursor=cursor, S_k=S_k), out
 
 

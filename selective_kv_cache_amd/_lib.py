@@ -45,6 +45,8 @@ _SIGS = {
     "kvb_create": ([I, POINTER(c_void_p)], I),
     "kvb_destroy": ([P], I),
     "kvb_workspace_size": ([P, P, I, I, I, POINTER(c_size_t)], I),
+    "kvb_timing_enable": ([P, ctypes.c_char_p], I),
+    "kvb_timing_read": ([P, ctypes.c_char_p, c_size_t, POINTER(c_size_t)], I),
     "kvb_pool_create": ([I, POINTER(c_void_p)], I),
     "kvb_pool_destroy": ([P], I),
     "kvb_pool_alloc": ([P, I, P], I),
@@ -149,6 +151,21 @@ def kvb_workspace_size(ctx, desc, max_rows: int, max_tokens: int, max_requests: 
     _check("kvb_workspace_size", load().kvb_workspace_size(ctx, ctypes.addressof(desc), max_rows, max_tokens,
                                                            max_requests, ctypes.byref(out)))
     return out.value
+
+
+def kvb_timing_enable(ctx, filter_) -> None:
+    """filter_: None = off, "" = every kernel, else a substring of kernel names."""
+    _check("kvb_timing_enable", load().kvb_timing_enable(ctx, None if filter_ is None else filter_.encode()))
+
+
+def kvb_timing_read(ctx) -> dict:
+    """Per-kernel {"name": {"count", "ms"}} since the last read (synchronises on the events)."""
+    import json
+    need = c_size_t()
+    _check("kvb_timing_read", load().kvb_timing_read(ctx, None, 0, ctypes.byref(need)))
+    buf = ctypes.create_string_buffer(max(need.value, 2))
+    _check("kvb_timing_read", load().kvb_timing_read(ctx, buf, len(buf), ctypes.byref(need)))
+    return json.loads(buf.value.decode() or "{}")
 
 
 def kvb_pool_create(n_pages: int) -> c_void_p:

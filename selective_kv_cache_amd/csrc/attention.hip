@@ -331,8 +331,10 @@ extern "C" kvb_status kvb_sparse_query_attn(kvb_ctx* ctx, void* stream, const kv
   if ((long)n_pages * 16 > 0x7fffffffL) return fail(KVB_ERR_INVALID_ARG, "too many pages for int32 slots");
   const int Hq = desc->n_q_heads, Hkv = desc->n_kv_heads, hd = desc->head_dim;
   const int G = Hq / Hkv;
+  CtxScope scope(ctx);
   hipStream_t st = (hipStream_t)stream;
   const int ns = n_pages * 16;
+  LaunchTimer lt(st, "attention");
   if (desc->dtype == KVB_BF16) {
     if (G > AQ || AQ % G) return fail(KVB_ERR_UNSUPPORTED, "GQA group size must divide 128");
     const int TB = AQ / G;

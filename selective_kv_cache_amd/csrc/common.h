@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <string>
+#include <vector>
 
 #include "../../include/kvb.h"
 
@@ -17,9 +18,40 @@ void set_error(const std::string& msg);
 kvb_status fail(kvb_status s, const std::string& msg);
 kvb_status check_launch(const char* what);
 
+// Per-context launch timing (tracing): when enabled, kernels whose name
+// contains the filter string are bracketed with HIP events on their stream.
+struct TimingRec {
+  const char* name;
+  hipEvent_t a, b;
+};
 struct Ctx {
   int device = 0;
   int n_cu = 256;
+  bool timing = false;
+  std::string filter;
+  std::vector<TimingRec> recs;
+  std::vector<hipEvent_t> spare;
+  std::vector<std::string> pend_names;  // totals not yet read by kvb_timing_read
+  std::vector<double> pend_ms;
+  std::vector<long> pend_count;
+};
+
+// The context of the entry point running on this thread (set by CtxScope).
+Ctx* current_ctx();
+struct CtxScope {
+  Ctx* prev;
+  explicit CtxScope(kvb_ctx* c);
+  ~CtxScope();
+};
+
+// Bracket one kernel launch with timing events when the current context asks for it.
+struct LaunchTimer {
+  Ctx* c = nullptr;
+  hipStream_t st;
+  const char* name;
+  hipEvent_t a = nullptr;
+  LaunchTimer(hipStream_t s, const char* n);
+  ~LaunchTimer();
 };
 
 // Validates the model description; returns KVB_OK or an error with message.

@@ -237,7 +237,7 @@ __global__ void __launch_bounds__(GEMM_THREADS) gemm_bf16_kernel(GemmArgs<bf16_t
 }
 
 template <int MODE, bool DUAL, bool NORM>
-static kvb_status run_bf16(hipStream_t st, const GemmArgs<bf16_t>& p) {
+static kvb_status run_bf16(hipStream_t st, const GemmArgs<bf16_t>& p, const char* name) {
   if (p.M_max == 0 || p.N == 0) return KVB_OK;
   dim3 grid(cdiv(p.M_max, BM), cdiv(p.N, BN));
   const size_t lds = (size_t)2 * (BM + BN * (DUAL ? 2 : 1)) * LDK * sizeof(bf16_t);
@@ -248,7 +248,10 @@ static kvb_status run_bf16(hipStream_t st, const GemmArgs<bf16_t>& p) {
     if (e != hipSuccess) return fail(KVB_ERR_HIP, std::string("hipFuncSetAttribute: ") + hipGetErrorString(e));
     attr_set = true;
   }
-  gemm_bf16_kernel<MODE, DUAL, NORM><<<grid, GEMM_THREADS, lds, st>>>(p);
+  {
+    LaunchTimer lt(st, name);
+    gemm_bf16_kernel<MODE, DUAL, NORM><<<grid, GEMM_THREADS, lds, st>>>(p);
+  }
   return check_launch("gemm_bf16_kernel");
 }
 
@@ -336,10 +339,13 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmArgs<float> p) {
 }
 
 template <int MODE, bool DUAL, bool NORM>
-static kvb_status run_f32(hipStream_t st, const GemmArgs<float>& p) {
+static kvb_status run_f32(hipStream_t st, const GemmArgs<float>& p, const char* name) {
   if (p.M_max == 0 || p.N == 0) return KVB_OK;
   dim3 grid(cdiv(p.M_max, FB), cdiv(p.N, FB));
-  gemm_f32_kernel<MODE, DUAL, NORM><<<grid, 256, 0, st>>>(p);
+  {
+    LaunchTimer lt(st, name);
+    gemm_f32_kernel<MODE, DUAL, NORM><<<grid, 256, 0, st>>>(p);
+  }
   return check_launch("gemm_f32_kernel");
 }
 
@@ -366,8 +372,8 @@ static kvb_status qkv_impl(hipStream_t st, const kvb_model_desc* d, int T_max, c
   p.out0 = (T*)q;
   p.out1 = (T*)k;
   p.out2 = (T*)v;
-  if constexpr (sizeof(T) == 2) KVB_TRY((run_bf16<EPI_QKV, false, true>(st, p)));
-  else KVB_TRY((run_f32<EPI_QKV, false, true>(st, p)));
+  if constexpr (sizeof(T) == 2) KVB_TRY((run_bf16<EPI_QKV, false, true>(st, p, "gemm_qkv")));
+  else KVB_TRY((run_f32<EPI_QKV, false, true>(st, p, "gemm_qkv")));
   if (tok_pos) return launch_rope<T>(st, T_max, n_rows, row_tok, tok_pos, q, k, d);
   return KVB_OK;
 }
@@ -419,13 +425,13 @@ static kvb_status mlp_impl(hipStream_t st, const kvb_model_desc* d, int T_max, c
   c.ldr = D;
   c.out_rows = row_tok;
   if constexpr (sizeof(T) == 2) {
-    KVB_TRY((run_bf16<EPI_RESID, false, false>(st, a)));
-    KVB_TRY((run_bf16<EPI_SWIGLU, true, true>(st, b)));
-    return run_bf16<EPI_SCATTER, false, false>(st, c);
+    KVB_TRY((run_bf16<EPI_RESID, false, false>(st, a, "gemm_oproj")));
+    KVB_TRY((run_bf16<EPI_SWIGLU, true, true>(st, b, "gemm_swiglu")));
+    return run_bf16<EPI_SCATTER, false, false>(st, c, "gemm_down");
   } else {
-    KVB_TRY((run_f32<EPI_RESID, false, false>(st, a)));
-    KVB_TRY((run_f32<EPI_SWIGLU, true, true>(st, b)));
-    return run_f32<EPI_SCATTER, false, false>(st, c);
+    KVB_TRY((run_f32<EPI_RESID, false, false>(st, a, "gemm_oproj")));
+    KVB_TRY((run_f32<EPI_SWIGLU, true, true>(st, b, "gemm_swiglu")));
+    return run_f32<EPI_SCATTER, false, false>(st, c, "gemm_down");
   }
 }
 
@@ -446,6 +452,7 @@ extern "C" kvb_status kvb_qkv_proj(kvb_ctx* ctx, void* stream, const kvb_model_d
   KVB_CHECK_PTR(q, "q");
   KVB_CHECK_PTR(k, "k");
   KVB_CHECK_PTR(v, "v");
+  CtxScope scope(ctx);
   hipStream_t st = (hipStream_t)stream;
   if (desc->dtype == KVB_BF16)
     return qkv_impl<bf16_t>(st, desc, T_max, n_rows, row_tok, hidden, norm_w, w_qkv, tok_pos, q, k, v);
@@ -466,6 +473,7 @@ extern "C" kvb_status kvb_mlp(kvb_ctx* ctx, void* stream, const kvb_model_desc* 
   KVB_CHECK_PTR(w_gate_up, "w_gate_up");
   KVB_CHECK_PTR(w_down, "w_down");
   if (!ws || ws_bytes < ws_mlp_bytes(desc, T_max)) return fail(KVB_ERR_WORKSPACE, "kvb_mlp workspace too small");
+  CtxScope scope(ctx);
   hipStream_t st = (hipStream_t)stream;
   if (desc->dtype == KVB_BF16)
     return mlp_impl<bf16_t>(st, desc, T_max, n_rows, row_tok, attn_o, w_o, hidden, norm2_w, w_gate_up, w_down, ws);

@@ -262,6 +262,7 @@ kvb_status launch_deviation(hipStream_t st, int n_tok, const void* k_rec, const 
   const int nvec = Hkv * hd / 8;
   const int threads = ((nvec + 63) / 64) * 64;
   if (n_tok == 0) return KVB_OK;
+  LaunchTimer lt(st, "deviation");
   if (hd == 128)
     deviation_kernel<T, 16><<<n_tok, threads, 0, st>>>(n_tok, (const T*)k_rec, (const T*)k_pool, n_pages * 16,
                                                         reuse_slot, d, alpha, Hkv, hd);
@@ -279,6 +280,7 @@ template <class T>
 kvb_status launch_rope(hipStream_t st, int T_max, const int32_t* n_rows, const int32_t* row_tok,
                        const int32_t* tok_pos, void* q, void* k, const kvb_model_desc* d) {
   if (T_max == 0) return KVB_OK;
+  LaunchTimer lt(st, "rope");
   rope_kernel<T><<<T_max, 256, 0, st>>>(T_max, n_rows, row_tok, tok_pos, (T*)q, (T*)k, d->n_q_heads, d->n_kv_heads,
                                         d->head_dim, d->rope_base);
   return check_launch("rope_kernel");
@@ -333,7 +335,9 @@ extern "C" kvb_status kvb_embed(kvb_ctx* ctx, void* stream, const kvb_model_desc
   KVB_CHECK_PTR(tokens, "tokens");
   KVB_CHECK_PTR(table, "table");
   KVB_CHECK_PTR(hidden, "hidden");
+  CtxScope scope(ctx);
   hipStream_t st = (hipStream_t)stream;
+  LaunchTimer lt(st, "embed");
   if (desc->dtype == KVB_BF16)
     embed_kernel<bf16_t><<<T_max, 256, 0, st>>>(T_max, n_rows, row_tok, tokens, vocab, (const bf16_t*)table,
                                                 (bf16_t*)hidden, desc->d_model);
@@ -353,6 +357,7 @@ extern "C" kvb_status kvb_rope(kvb_ctx* ctx, void* stream, const kvb_model_desc*
   KVB_CHECK_PTR(tok_pos, "tok_pos");
   KVB_CHECK_PTR(q, "q");
   KVB_CHECK_PTR(k, "k");
+  CtxScope scope(ctx);
   hipStream_t st = (hipStream_t)stream;
   if (desc->dtype == KVB_BF16) return launch_rope<bf16_t>(st, T_max, n_rows, row_tok, tok_pos, q, k, desc);
   return launch_rope<float>(st, T_max, n_rows, row_tok, tok_pos, q, k, desc);
@@ -381,8 +386,10 @@ extern "C" kvb_status kvb_blend_scatter(kvb_ctx* ctx, void* stream, const kvb_mo
   const int nvec = Hkv * hd / 8;
   if (nvec > 1024 || Hkv > 64) return fail(KVB_ERR_UNSUPPORTED, "n_kv_heads * head_dim must be <= 8192");
   const int threads = ((nvec + 63) / 64) * 64;
+  CtxScope scope(ctx);
   hipStream_t st = (hipStream_t)stream;
   const int ns = n_pages * 16;
+  LaunchTimer lt(st, "blend_scatter");
 #define KVB_BLEND(T, VPH)                                                                                   \
   blend_scatter_kernel<T, VPH><<<T_max, threads, 0, st>>>(T_max, n_rows, row_tok, (const T*)k_rec,         \
                                                           (const T*)v_rec, (T*)k_pool, (T*)v_pool, ns, src_slot, \
@@ -406,8 +413,10 @@ extern "C" kvb_status kvb_slot_map(kvb_ctx* ctx, void* stream, const kvb_model_d
   KVB_TRY(check_desc(desc));
   if (B < 0 || n_tok < 0 || T_max < 0) return fail(KVB_ERR_INVALID_ARG, "negative size");
   KVB_CHECK_PTR(slot_map, "slot_map");
+  CtxScope scope(ctx);
   hipStream_t st = (hipStream_t)stream;
   if (n_tok > 0) {
+    LaunchTimer lt(st, "slot_copy");
     copy_slots_kernel<<<cdiv(n_tok, 256), 256, 0, st>>>(n_tok, reuse_slot, slot_map);
     KVB_TRY(check_launch("copy_slots_kernel"));
   }
@@ -415,6 +424,7 @@ extern "C" kvb_status kvb_slot_map(kvb_ctx* ctx, void* stream, const kvb_model_d
   KVB_CHECK_PTR(cu_rows, "cu_rows");
   KVB_CHECK_PTR(new_pages, "new_pages");
   KVB_CHECK_PTR(cu_pages, "cu_pages");
+  LaunchTimer lt(st, "slot_scatter");
   scatter_slots_kernel<<<cdiv(T_max, 256), 256, 0, st>>>(B, T_max, cu_rows, row_tok, new_pages, cu_pages, slot_map,
                                                          dst_slot, n_tok);
   return check_launch("scatter_slots_kernel");

@@ -2,6 +2,7 @@
 // context, argument checks, workspace sizing and the deterministic page
 // allocator (lowest free id first, SLIDE's preallocated new pages).
 #include <algorithm>
+#include <cstdio>
 #include <set>
 #include <string>
 #include <vector>
@@ -23,6 +24,49 @@ kvb_status check_launch(const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KVB_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
   return KVB_OK;
+}
+
+static thread_local Ctx* g_current = nullptr;
+
+Ctx* current_ctx() { return g_current; }
+
+CtxScope::CtxScope(kvb_ctx* c) : prev(g_current) { g_current = reinterpret_cast<Ctx*>(c); }
+CtxScope::~CtxScope() { g_current = prev; }
+
+static hipEvent_t take_event(Ctx* c) {
+  if (!c->spare.empty()) {
+    hipEvent_t e = c->spare.back();
+    c->spare.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+LaunchTimer::LaunchTimer(hipStream_t s, const char* n) : st(s), name(n) {
+  Ctx* cur = g_current;
+  if (!cur || !cur->timing) return;
+  if (!cur->filter.empty() && std::string(n).find(cur->filter) == std::string::npos) return;
+  a = take_event(cur);
+  if (!a) return;
+  if (hipEventRecord(a, st) != hipSuccess) {
+    cur->spare.push_back(a);
+    a = nullptr;
+    return;
+  }
+  c = cur;
+}
+
+LaunchTimer::~LaunchTimer() {
+  if (!c) return;
+  hipEvent_t b = take_event(c);
+  if (!b || hipEventRecord(b, st) != hipSuccess) {
+    c->spare.push_back(a);
+    if (b) c->spare.push_back(b);
+    return;
+  }
+  c->recs.push_back(TimingRec{name, a, b});
 }
 
 kvb_status check_ctx(const kvb_ctx* c) {
@@ -104,7 +148,64 @@ kvb_status kvb_create(int32_t device, kvb_ctx** out) {
 }
 
 kvb_status kvb_destroy(kvb_ctx* ctx) {
-  delete reinterpret_cast<Ctx*>(ctx);
+  Ctx* c = reinterpret_cast<Ctx*>(ctx);
+  if (c) {
+    for (auto& r : c->recs) {
+      hipEventDestroy(r.a);
+      hipEventDestroy(r.b);
+    }
+    for (auto e : c->spare) hipEventDestroy(e);
+  }
+  delete c;
+  return KVB_OK;
+}
+
+kvb_status kvb_timing_enable(kvb_ctx* ctx, const char* filter) {
+  KVB_TRY(check_ctx(ctx));
+  Ctx* c = reinterpret_cast<Ctx*>(ctx);
+  c->timing = filter != nullptr;
+  c->filter = filter ? filter : "";
+  return KVB_OK;
+}
+
+kvb_status kvb_timing_read(kvb_ctx* ctx, char* buf, size_t len, size_t* needed) {
+  KVB_TRY(check_ctx(ctx));
+  Ctx* c = reinterpret_cast<Ctx*>(ctx);
+  // fold the finished records into the pending per-name totals (first-seen order)
+  for (auto& r : c->recs) {
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e != hipSuccess) return fail(KVB_ERR_HIP, std::string("hipEventSynchronize: ") + hipGetErrorString(e));
+    float t = 0.f;
+    e = hipEventElapsedTime(&t, r.a, r.b);
+    if (e != hipSuccess) return fail(KVB_ERR_HIP, std::string("hipEventElapsedTime: ") + hipGetErrorString(e));
+    size_t i = 0;
+    while (i < c->pend_names.size() && c->pend_names[i] != r.name) i++;
+    if (i == c->pend_names.size()) {
+      c->pend_names.push_back(r.name);
+      c->pend_ms.push_back(0.0);
+      c->pend_count.push_back(0);
+    }
+    c->pend_ms[i] += t;
+    c->pend_count[i] += 1;
+    c->spare.push_back(r.a);
+    c->spare.push_back(r.b);
+  }
+  c->recs.clear();
+  std::string out = "{";
+  for (size_t i = 0; i < c->pend_names.size(); i++) {
+    char item[256];
+    snprintf(item, sizeof item, "%s\"%s\": {\"count\": %ld, \"ms\": %.6f}", i ? ", " : "",
+             c->pend_names[i].c_str(), c->pend_count[i], c->pend_ms[i]);
+    out += item;
+  }
+  out += "}";
+  if (needed) *needed = out.size() + 1;
+  if (buf && len >= out.size() + 1) {
+    memcpy(buf, out.c_str(), out.size() + 1);
+    c->pend_names.clear();
+    c->pend_ms.clear();
+    c->pend_count.clear();
+  }
   return KVB_OK;
 }
 

@@ -250,6 +250,7 @@ extern "C" kvb_status kvb_deviation_topk(kvb_ctx* ctx, void* stream, const kvb_m
   }
   if (!ws || ws_bytes < ws_topk_bytes(n_tok, B)) return fail(KVB_ERR_WORKSPACE, "kvb_deviation_topk workspace too small");
   if (desc->n_kv_heads * desc->head_dim / 8 > 1024) return fail(KVB_ERR_UNSUPPORTED, "n_kv_heads * head_dim > 8192");
+  CtxScope scope(ctx);
   hipStream_t st = (hipStream_t)stream;
   TopkWs w = topk_ws(ws, n_tok);
   if (desc->dtype == KVB_BF16)
@@ -260,12 +261,21 @@ extern "C" kvb_status kvb_deviation_topk(kvb_ctx* ctx, void* stream, const kvb_m
                                     desc->head_dim));
   if (n_tok > 0) {
     const int n_chunks = n_tok / CHUNK + B;  // >= sum over requests of cdiv(N_b, CHUNK)
-    chunk_sort_kernel<<<n_chunks, SORT_THREADS, 0, st>>>(B, cu_tok, d, w.sorted);
+    {
+      LaunchTimer lt(st, "topk_sort");
+      chunk_sort_kernel<<<n_chunks, SORT_THREADS, 0, st>>>(B, cu_tok, d, w.sorted);
+    }
     KVB_TRY(check_launch("chunk_sort_kernel"));
-    rank_kernel<<<cdiv(n_tok, 256), 256, 0, st>>>(B, n_tok, cu_tok, d, w.sorted, k_cap, ranking, w.flag);
+    {
+      LaunchTimer lt(st, "topk_rank");
+      rank_kernel<<<cdiv(n_tok, 256), 256, 0, st>>>(B, n_tok, cu_tok, d, w.sorted, k_cap, ranking, w.flag);
+    }
     KVB_TRY(check_launch("rank_kernel"));
   }
-  compact_kernel<<<B, CT, 0, st>>>(B, cu_tok, w.flag, sel, cu_rows, cursor, d, s_count);
+  {
+    LaunchTimer lt(st, "topk_compact");
+    compact_kernel<<<B, CT, 0, st>>>(B, cu_tok, w.flag, sel, cu_rows, cursor, d, s_count);
+  }
   return check_launch("compact_kernel");
 }
 
@@ -292,11 +302,18 @@ extern "C" kvb_status kvb_cosine_refresh(kvb_ctx* ctx, void* stream, const kvb_m
   }
   if (sel_in && sel_in == sel_out) return fail(KVB_ERR_INVALID_ARG, "sel_in and sel_out must not overlap");
   if (!ws || ws_bytes < ws_refresh_bytes(n_tok, B)) return fail(KVB_ERR_WORKSPACE, "kvb_cosine_refresh workspace too small");
+  CtxScope scope(ctx);
   hipStream_t st = (hipStream_t)stream;
   int32_t* flag = (int32_t*)ws;
-  refresh_flag_kernel<<<B, CT, 0, st>>>(B, cu_tok, cu_rows_in, sel_in, cksim, tau, rule, ranking, s_count, cursor,
-                                        flag);
+  {
+    LaunchTimer lt(st, "refresh_flag");
+    refresh_flag_kernel<<<B, CT, 0, st>>>(B, cu_tok, cu_rows_in, sel_in, cksim, tau, rule, ranking, s_count, cursor,
+                                          flag);
+  }
   KVB_TRY(check_launch("refresh_flag_kernel"));
-  compact_kernel<<<B, CT, 0, st>>>(B, cu_tok, flag, sel_out, cu_rows_out, nullptr, nullptr, nullptr);
+  {
+    LaunchTimer lt(st, "refresh_compact");
+    compact_kernel<<<B, CT, 0, st>>>(B, cu_tok, flag, sel_out, cu_rows_out, nullptr, nullptr, nullptr);
+  }
   return check_launch("compact_kernel");
 }
