@@ -110,7 +110,7 @@ kvb_status kvb_workspace_size(kvb_ctx* ctx, const kvb_model_desc* desc, int32_t 
 /* Launch timing (tracing).  With filter != NULL, every later kernel launch of
  * this context whose kernel name contains `filter` ("" = all) is bracketed with
  * HIP events on its stream; filter == NULL turns timing off.  Kernel names:
- * embed, gemm_qkv, rope, blend_scatter, attention, gemm_oproj, gemm_swiglu,
+ * embed, gemm_qkv, rope, blend_scatter, attention, attention_merge, gemm_oproj, gemm_swiglu,
  * gemm_down, deviation, topk_sort, topk_rank, topk_compact, refresh_flag,
  * refresh_compact, slot_copy, slot_scatter. */
 kvb_status kvb_timing_enable(kvb_ctx* ctx, const char* filter);

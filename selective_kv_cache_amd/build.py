@@ -22,12 +22,8 @@ HIPCC_FLAGS = [
     "-Wno-unused-result", "-Wno-unused-command-line-argument",
 ]
 
-# Per-source overrides.  ROCm 7.2's clang segfaults in its machine copy
-# propagation / post-RA expansion on the MFMA attention kernel at -O2/-O3;
-# -O1 compiles it fully unrolled with no scratch.
-PER_FILE_FLAGS = {
-    "attention.hip": ["-O1"],
-}
+# Per-source flag overrides (none needed at present).
+PER_FILE_FLAGS = {}
 
 
 def sources():

@@ -65,7 +65,7 @@ inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 size_t ws_mlp_bytes(const kvb_model_desc* d, int32_t max_rows);
 size_t ws_topk_bytes(int32_t max_tokens, int32_t max_requests);
 size_t ws_refresh_bytes(int32_t max_tokens, int32_t max_requests);
-size_t ws_attn_bytes(const kvb_model_desc* d, int32_t max_rows, int32_t max_tokens);
+size_t ws_attn_bytes(const kvb_model_desc* d, int32_t max_rows, int n_cu);
 
 }  // namespace kvb
 
@@ -83,13 +83,8 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// float -> bfloat16, round to nearest even (NaN kept quiet)
-__device__ __forceinline__ bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
-}
+// float -> bfloat16, round to nearest even (gfx950 v_cvt_pk_bf16_f32)
+__device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 // storage-type traits: T is float (KVB_F32) or bf16_t (KVB_BF16)
 template <class T> struct Store;

@@ -72,8 +72,18 @@ __device__ __forceinline__ void epilogue(const GemmArgs<T>& p, int m, int n, flo
 }
 
 // ====================================================================== bf16 MFMA
+//
+// Block = 4 waves in a 2 x 2 grid; wave tile = (32 TM) x (32 TN) outputs as
+// TM x TN tiles of v_mfma_f32_32x32x16_bf16; block tile BM = 64 TM, BN = 64 TN
+// rows of B.  K advances in 64-wide steps through double-buffered LDS (row
+// stride 72 elements: conflict-free 16-byte fragment reads); the next step's
+// tiles are fetched into registers while the current one feeds the MFMAs.
+//
+// SwiGLU (DUAL): the B tile interleaves 32-row subtiles of the gate and up
+// matrices (gate cols c..c+31, up cols c..c+31, ...), so a wave holds gate
+// and up of the same outputs in neighbouring accumulators; BN/2 outputs wide.
 
-constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8;  // LDS row stride in bf16 elements
+constexpr int BK = 64, LDK = BK + 8;  // LDS row stride in bf16 elements
 constexpr int GEMM_THREADS = 256;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -103,113 +113,138 @@ __device__ __forceinline__ float sumsq8(const uint4& a) {
   return s;
 }
 
-template <int MODE, bool DUAL, bool NORM>
-__global__ void __launch_bounds__(GEMM_THREADS) gemm_bf16_kernel(GemmArgs<bf16_t> p) {
+template <int TM, int TN>
+struct Tile {
+  static constexpr int BM = 64 * TM, BN = 64 * TN;
+  static constexpr int A_LD = BM / 32, B_LD = BN / 32;  // 16-byte loads per thread per K step
+  static constexpr size_t LDS = (size_t)2 * (BM + BN) * LDK * sizeof(bf16_t);
+  // the epilogue reuses the same LDS for a [BM/2][OUT_N + 8] float tile
+  static_assert((size_t)(BM / 2) * (BN + 8) * 4 <= LDS, "epilogue tile must fit the K-loop buffers");
+};
+
+template <int MODE, bool DUAL, bool NORM, bool GAIN, int TM, int TN>
+__global__ void __launch_bounds__(GEMM_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm_bf16_kernel(GemmArgs<bf16_t> p) {
+  using TL = Tile<TM, TN>;
+  constexpr int BM = TL::BM, BN = TL::BN, A_LD = TL::A_LD, B_LD = TL::B_LD;
+  constexpr int OUT_N = DUAL ? BN / 2 : BN;  // output columns per block
   extern __shared__ __align__(16) uint8_t smem[];
-  bf16_t* sA = reinterpret_cast<bf16_t*>(smem);             // [2][BM][LDK]
-  bf16_t* sB = sA + 2 * BM * LDK;                           // [2][BN][LDK]
-  bf16_t* sB2 = sB + 2 * BN * LDK;                          // [2][BN][LDK] (DUAL)
-  __shared__ float s_rinv[BM];
+  bf16_t* sA = reinterpret_cast<bf16_t*>(smem);  // [2][BM][LDK]
+  bf16_t* sB = sA + 2 * BM * LDK;                // [2][BN][LDK]
+  __shared__ float s_rinv[NORM ? BM : 1];
 
   const int M = row_count(p.n_rows, p.M_max);
-  const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
+  const int m0 = blockIdx.x * BM, n0 = blockIdx.y * OUT_N;
   if (m0 >= M) return;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int wm = (wave >> 1) * (32 * TM), wn = (wave & 1) * (32 * TN);
 
-  // global -> register loaders: chunk c = t + 256 i, row c / 8 (= t/8 + 32 i), k-chunk c % 8 (= t % 8)
+  // loaders: chunk c = t + 256 i -> tile row c / 8 = t / 8 + 32 i, k-chunk c % 8 = t % 8
   const int lrow = t >> 3, lkc = t & 7;
-  const bf16_t* a_ptr[4];
-  const bf16_t* b_ptr[4];
-  const bf16_t* b2_ptr[4];
+  const bf16_t* a_src[A_LD];
+  const bf16_t* b_src[B_LD];
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
+  for (int i = 0; i < A_LD; i++) {
     int m = m0 + lrow + 32 * i;
     m = m < M ? m : M - 1;
     const int ar = p.a_rows ? p.a_rows[m] : m;
-    a_ptr[i] = p.A + (size_t)ar * p.K + lkc * 8;
-    int n = n0 + lrow + 32 * i;
-    n = n < p.N ? n : p.N - 1;
-    b_ptr[i] = p.B + (size_t)n * p.K + lkc * 8;
-    if (DUAL) b2_ptr[i] = p.B2 + (size_t)n * p.K + lkc * 8;
+    a_src[i] = p.A + (size_t)ar * p.K + lkc * 8;
   }
-  uint4 ra[4], rb[4], rb2[4];
-  float ssq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < B_LD; i++) {
+    const int b = lrow + 32 * i;  // B-tile row; subtile b / 32 == i
+    const bf16_t* base = p.B;
+    int n;
+    if (DUAL) {
+      base = (i & 1) ? p.B2 : p.B;
+      n = n0 + (i >> 1) * 32 + (b & 31);
+    } else {
+      n = n0 + b;
+    }
+    n = n < p.N ? n : p.N - 1;
+    b_src[i] = base + (size_t)n * p.K + lkc * 8;
+  }
+  uint4 ra[A_LD], rb[B_LD];
+  float ssq[A_LD];
+#pragma unroll
+  for (int i = 0; i < A_LD; i++) ssq[i] = 0.f;
 
-  auto gload = [&](int kt) {
-    const int ko = kt * BK;
+  f32x16_t acc[TM][TN];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      ra[i] = *reinterpret_cast<const uint4*>(a_ptr[i] + ko);
-      rb[i] = *reinterpret_cast<const uint4*>(b_ptr[i] + ko);
-      if (DUAL) rb2[i] = *reinterpret_cast<const uint4*>(b2_ptr[i] + ko);
-    }
-  };
-  auto sstore = [&](int kt, int buf) {
-    uint4 g;
-    if (NORM) {
-      if (p.norm_w) g = *reinterpret_cast<const uint4*>(p.norm_w + kt * BK + lkc * 8);
-    }
+  for (int i = 0; i < TM; i++)
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      uint4 a = ra[i];
-      if (NORM) {
-        ssq[i] += sumsq8(a);
-        if (p.norm_w) a = mul_gain(a, g);
-      }
-      const int r = lrow + 32 * i;
-      *reinterpret_cast<uint4*>(sA + (buf * BM + r) * LDK + lkc * 8) = a;
-      *reinterpret_cast<uint4*>(sB + (buf * BN + r) * LDK + lkc * 8) = rb[i];
-      if (DUAL) *reinterpret_cast<uint4*>(sB2 + (buf * BN + r) * LDK + lkc * 8) = rb2[i];
-    }
-  };
-
-  f32x16_t acc[2][2], acc2[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; i++)
-#pragma unroll
-    for (int j = 0; j < 2; j++) {
-      acc[i][j] = (f32x16_t){};
-      acc2[i][j] = (f32x16_t){};
-    }
+    for (int j = 0; j < TN; j++) acc[i][j] = (f32x16_t){};
 
   const int KT = p.K / BK;
-  gload(0);
-  sstore(0, 0);
+  // prologue: tile 0 -> LDS buffer 0
+#pragma unroll
+  for (int i = 0; i < A_LD; i++) ra[i] = *reinterpret_cast<const uint4*>(a_src[i]);
+#pragma unroll
+  for (int i = 0; i < B_LD; i++) rb[i] = *reinterpret_cast<const uint4*>(b_src[i]);
+  {
+    uint4 g = make_uint4(0, 0, 0, 0);
+    if (GAIN) g = *reinterpret_cast<const uint4*>(p.norm_w + lkc * 8);
+#pragma unroll
+    for (int i = 0; i < A_LD; i++) {
+      uint4 a = ra[i];
+      if (NORM) ssq[i] += sumsq8(a);
+      if (GAIN) a = mul_gain(a, g);
+      *reinterpret_cast<uint4*>(sA + (lrow + 32 * i) * LDK + lkc * 8) = a;
+    }
+#pragma unroll
+    for (int i = 0; i < B_LD; i++) *reinterpret_cast<uint4*>(sB + (lrow + 32 * i) * LDK + lkc * 8) = rb[i];
+  }
   __syncthreads();
-  const int fr = lane & 31, fk = (lane >> 5) * 8;  // fragment row and k offset inside a 16-wide k slice
+
+  const int fr = lane & 31, fk = (lane >> 5) * 8;  // fragment row, k offset in a 16-wide slice
   for (int kt = 0; kt < KT; kt++) {
     const int buf = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
-    const bf16_t* a_s = sA + buf * BM * LDK;
-    const bf16_t* b_s = sB + buf * BN * LDK;
-    const bf16_t* b2_s = sB2 + buf * BN * LDK;
+    // next K step (the last iteration re-fetches its own step; the copy is never read)
+    const int kn = kt + 1 < KT ? kt + 1 : kt;
+    {
+      const int ko = kn * BK;
+#pragma unroll
+      for (int i = 0; i < A_LD; i++) ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + ko);
+#pragma unroll
+      for (int i = 0; i < B_LD; i++) rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + ko);
+    }
+    const bf16_t* a_s = sA + buf * BM * LDK + (wm + fr) * LDK + fk;
+    const bf16_t* b_s = sB + buf * BN * LDK + (wn + fr) * LDK + fk;
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8_t af[2], bfr[2], bf2[2];
+      bf16x8_t af[TM], bfr[TN];
 #pragma unroll
-      for (int i = 0; i < 2; i++)
-        af[i] = as_bf16x8(*reinterpret_cast<const uint4*>(a_s + (wm + i * 32 + fr) * LDK + kk + fk));
+      for (int i = 0; i < TM; i++) af[i] = as_bf16x8(*reinterpret_cast<const uint4*>(a_s + i * 32 * LDK + kk));
 #pragma unroll
-      for (int j = 0; j < 2; j++) {
-        bfr[j] = as_bf16x8(*reinterpret_cast<const uint4*>(b_s + (wn + j * 32 + fr) * LDK + kk + fk));
-        if (DUAL) bf2[j] = as_bf16x8(*reinterpret_cast<const uint4*>(b2_s + (wn + j * 32 + fr) * LDK + kk + fk));
+      for (int j = 0; j < TN; j++) bfr[j] = as_bf16x8(*reinterpret_cast<const uint4*>(b_s + j * 32 * LDK + kk));
+#pragma unroll
+      for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    {
+      const int nb = buf ^ 1;
+      const bool fresh = kt + 1 < KT;  // only a real next step adds to the row sums
+      uint4 g = make_uint4(0, 0, 0, 0);
+      if (GAIN) g = *reinterpret_cast<const uint4*>(p.norm_w + kn * BK + lkc * 8);
+#pragma unroll
+      for (int i = 0; i < A_LD; i++) {
+        uint4 a = ra[i];
+        if (NORM) ssq[i] += fresh ? sumsq8(a) : 0.f;
+        if (GAIN) a = mul_gain(a, g);
+        *reinterpret_cast<uint4*>(sA + (nb * BM + lrow + 32 * i) * LDK + lkc * 8) = a;
       }
 #pragma unroll
-      for (int i = 0; i < 2; i++)
-#pragma unroll
-        for (int j = 0; j < 2; j++) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-          if (DUAL) acc2[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf2[j], acc2[i][j], 0, 0, 0);
-        }
+      for (int i = 0; i < B_LD; i++)
+        *reinterpret_cast<uint4*>(sB + (nb * BN + lrow + 32 * i) * LDK + lkc * 8) = rb[i];
     }
-    if (kt + 1 < KT) sstore(kt + 1, buf ^ 1);
     __syncthreads();
   }
 
   if (NORM) {
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 0; i < A_LD; i++) {
       float s = ssq[i];
       s += __shfl_xor(s, 1, 64);
       s += __shfl_xor(s, 2, 64);
@@ -219,40 +254,123 @@ __global__ void __launch_bounds__(GEMM_THREADS) gemm_bf16_kernel(GemmArgs<bf16_t
     __syncthreads();
   }
 
-  // epilogue: acc[i][j][r] -> row wm + 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4, col wn + 32 j + lane % 32
+  // Epilogue, staged through LDS in two halves of BM/2 rows: the waves owning a
+  // half write their float accumulators (SwiGLU already combined) to an
+  // [BM/2][OUT_N] tile, then all threads read 8 consecutive outputs of a row,
+  // apply the mode (scale, residual, scatter) and store 16 bytes at a time.
+  // acc[i][j][r] sits at tile row wm + 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4,
+  // tile col wn + 32 j + lane % 32 (DUAL: output col (wn / 32 + j) / 2 * 32 + lane % 32).
+  constexpr int HR = BM / 2;
+  constexpr int LDC = OUT_N + 8;  // floats; rows 4 apart land 32 banks apart
+  float* sC = reinterpret_cast<float*>(smem);
+  const int lc = lane & 31;
+  const int my_half = wave >> 1;
 #pragma unroll
-  for (int i = 0; i < 2; i++)
+  for (int half = 0; half < 2; half++) {
+    if (my_half == half) {
 #pragma unroll
-    for (int r = 0; r < 16; r++) {
-      const int ml = wm + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      const int m = m0 + ml;
-      if (m >= M) continue;
-      const float rinv = NORM ? s_rinv[ml] : 1.f;
+      for (int j = 0; j < TN; j += (DUAL ? 2 : 1)) {
+        const int cl = DUAL ? ((wn / 32 + j) >> 1) * 32 + lc : wn + j * 32 + lc;
 #pragma unroll
-      for (int j = 0; j < 2; j++) {
-        const int n = n0 + wn + j * 32 + (lane & 31);
-        if (n < p.N) epilogue<MODE, bf16_t>(p, m, n, acc[i][j][r], DUAL ? acc2[i][j][r] : 0.f, rinv);
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+          for (int r = 0; r < 16; r++) {
+            const int rl = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);  // row inside the half
+            float v = acc[i][j][r];
+            if (DUAL) {
+              const float rinv = s_rinv[half * HR + rl];
+              v = silu(v * rinv) * (acc[i][j + 1][r] * rinv);
+            }
+            sC[rl * LDC + cl] = v;
+          }
       }
     }
+    __syncthreads();
+    constexpr int CPR = OUT_N / 8;  // 8-output chunks per row
+    for (int c = t; c < HR * CPR; c += GEMM_THREADS) {
+      const int rl = c / CPR, cc = (c % CPR) * 8;
+      const int ml = half * HR + rl, m = m0 + ml, n = n0 + cc;
+      if (m >= M || n >= p.N) continue;
+      const float4 lo = *reinterpret_cast<const float4*>(sC + rl * LDC + cc);
+      const float4 hi = *reinterpret_cast<const float4*>(sC + rl * LDC + cc + 4);
+      float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      bf16_t* dst;
+      if (MODE == EPI_QKV) {
+        const float rinv = s_rinv[ml];
+#pragma unroll
+        for (int e = 0; e < 8; e++) v[e] *= rinv;
+        if (n < p.n0) dst = p.out0 + (size_t)m * p.n0 + n;
+        else if (n < p.n1) dst = p.out1 + (size_t)m * (p.n1 - p.n0) + (n - p.n0);
+        else dst = p.out2 + (size_t)m * (p.N - p.n1) + (n - p.n1);
+      } else if (MODE == EPI_SWIGLU) {
+        dst = p.out0 + (size_t)m * p.ldo + n;
+      } else {
+        const int rr = (MODE == EPI_RESID && p.resid_rows) ? p.resid_rows[m] : m;
+        const uint4 h = *reinterpret_cast<const uint4*>(p.resid + (size_t)rr * p.ldr + n);
+        const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          v[2 * e] += __uint_as_float(hw[e] << 16);
+          v[2 * e + 1] += __uint_as_float(hw[e] & 0xffff0000u);
+        }
+        const int orow = (MODE == EPI_SCATTER && p.out_rows) ? p.out_rows[m] : m;
+        dst = p.out0 + (size_t)orow * p.ldo + n;
+      }
+      uint4 o;
+      o.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+      o.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+      o.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
+      o.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+      *reinterpret_cast<uint4*>(dst) = o;
+    }
+    __syncthreads();
+  }
 }
 
-template <int MODE, bool DUAL, bool NORM>
-static kvb_status run_bf16(hipStream_t st, const GemmArgs<bf16_t>& p, const char* name) {
-  if (p.M_max == 0 || p.N == 0) return KVB_OK;
-  dim3 grid(cdiv(p.M_max, BM), cdiv(p.N, BN));
-  const size_t lds = (size_t)2 * (BM + BN * (DUAL ? 2 : 1)) * LDK * sizeof(bf16_t);
+template <int MODE, bool DUAL, bool NORM, bool GAIN, int TM, int TN>
+static kvb_status launch_bf16(hipStream_t st, const GemmArgs<bf16_t>& p, const char* name) {
+  using TL = Tile<TM, TN>;
+  constexpr int OUT_N = DUAL ? TL::BN / 2 : TL::BN;
+  dim3 grid(cdiv(p.M_max, TL::BM), cdiv(p.N, OUT_N));
   static bool attr_set = false;  // opt in to > 64 KiB of dynamic LDS once per instantiation
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<MODE, DUAL, NORM>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<MODE, DUAL, NORM, GAIN, TM, TN>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)TL::LDS);
     if (e != hipSuccess) return fail(KVB_ERR_HIP, std::string("hipFuncSetAttribute: ") + hipGetErrorString(e));
     attr_set = true;
   }
   {
     LaunchTimer lt(st, name);
-    gemm_bf16_kernel<MODE, DUAL, NORM><<<grid, GEMM_THREADS, lds, st>>>(p);
+    gemm_bf16_kernel<MODE, DUAL, NORM, GAIN, TM, TN><<<grid, GEMM_THREADS, TL::LDS, st>>>(p);
   }
   return check_launch("gemm_bf16_kernel");
+}
+
+// Tile choice: the per-element reduction order (64-wide K steps, 16-wide MFMA
+// slices in order) is the same for every tile shape, so picking the shape from
+// the launch bound keeps every row's result independent of the batch.
+template <int MODE, bool DUAL, bool NORM, bool GAIN>
+static kvb_status run_bf16_g(hipStream_t st, const GemmArgs<bf16_t>& p, const char* name) {
+  const Ctx* c = current_ctx();
+  const long cus = c ? c->n_cu : 256;
+  const long big_blocks = (long)cdiv(p.M_max, 256) * cdiv(p.N, DUAL ? 128 : 256);
+  if (big_blocks >= cus) return launch_bf16<MODE, DUAL, NORM, GAIN, 4, 4>(st, p, name);
+  const long mid_blocks = (long)cdiv(p.M_max, 256) * cdiv(p.N, DUAL ? 64 : 128);
+  if (mid_blocks >= cus) return launch_bf16<MODE, DUAL, NORM, GAIN, 4, 2>(st, p, name);
+  return launch_bf16<MODE, DUAL, NORM, GAIN, 2, 2>(st, p, name);
+}
+
+// Tile choice: the per-element reduction order (64-wide K steps, 16-wide MFMA
+// slices in order) is the same for every tile shape, so picking the shape from
+// the launch bound keeps every row's result independent of the batch.  RMSNorm
+// gains are applied to A only when given (NULL = unit gains).
+template <int MODE, bool DUAL, bool NORM>
+static kvb_status run_bf16(hipStream_t st, const GemmArgs<bf16_t>& p, const char* name) {
+  if (p.M_max == 0 || p.N == 0) return KVB_OK;
+  if constexpr (NORM) {
+    if (p.norm_w) return run_bf16_g<MODE, DUAL, NORM, true>(st, p, name);
+  }
+  return run_bf16_g<MODE, DUAL, NORM, false>(st, p, name);
 }
 
 // ====================================================================== fp32 FMA

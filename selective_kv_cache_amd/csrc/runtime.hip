@@ -111,7 +111,6 @@ size_t ws_refresh_bytes(int32_t max_tokens, int32_t max_requests) {
   return align_up((size_t)max_tokens * 4, 256) + align_up(((size_t)max_requests * 2 + 2) * 4, 256);
 }
 
-size_t ws_attn_bytes(const kvb_model_desc*, int32_t, int32_t) { return 0; }
 
 }  // namespace kvb
 
@@ -218,7 +217,7 @@ kvb_status kvb_workspace_size(kvb_ctx* ctx, const kvb_model_desc* desc, int32_t 
   size_t b = ws_mlp_bytes(desc, max_rows);
   b = std::max(b, ws_topk_bytes(max_tokens, max_requests));
   b = std::max(b, ws_refresh_bytes(max_tokens, max_requests));
-  b = std::max(b, ws_attn_bytes(desc, max_rows, max_tokens));
+  b = std::max(b, ws_attn_bytes(desc, max_rows, reinterpret_cast<Ctx*>(ctx)->n_cu));
   *bytes = b;
   return KVB_OK;
 }
