@@ -110,7 +110,7 @@ kvb_status kvb_workspace_size(kvb_ctx* ctx, const kvb_model_desc* desc, int32_t 
 /* Launch timing (tracing).  With filter != NULL, every later kernel launch of
  * this context whose kernel name contains `filter` ("" = all) is bracketed with
  * HIP events on its stream; filter == NULL turns timing off.  Kernel names:
- * embed, gemm_qkv, rope, blend_scatter, attention, attention_merge, gemm_oproj, gemm_swiglu,
+ * embed, rmsnorm, gemm_qkv, rope, blend_scatter, attention, attention_merge, gemm_oproj, gemm_swiglu,
  * gemm_down, deviation, topk_sort, topk_rank, topk_compact, refresh_flag,
  * refresh_compact, slot_copy, slot_scatter. */
 kvb_status kvb_timing_enable(kvb_ctx* ctx, const char* filter);
@@ -151,11 +151,14 @@ kvb_status kvb_embed(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int
  * If tok_pos != NULL, rotate-half RoPE at position tok_pos[row_tok[r]] is
  * applied to q and k (as kvb_rope).  The per-row result does not depend on
  * T, on the row's place in the batch or on the other rows (a chunk seen at
- * the same positions in compile and link gets bitwise-equal keys). */
+ * the same positions in compile and link gets bitwise-equal keys).
+ * norm_w == NULL means unit gains.  With bf16 storage a_r is written to the
+ * workspace rounded to bf16 once (ws_bytes >= kvb_workspace_size for T_max
+ * rows); float32 storage needs no workspace (ws may be NULL). */
 kvb_status kvb_qkv_proj(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t T_max,
                         const int32_t* n_rows, const int32_t* row_tok, const void* hidden,
                         const void* norm_w, const void* w_qkv, const int32_t* tok_pos, void* q,
-                        void* k, void* v);
+                        void* k, void* v, void* ws, size_t ws_bytes);
 
 /* In-place rotate-half RoPE of q [T, Hq, hd] and k [T, Hkv, hd] at positions
  * tok_pos[row_tok[r]]: pair (j, j + hd/2) rotated by pos * base^(-2j/hd).

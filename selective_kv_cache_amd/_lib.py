@@ -53,7 +53,7 @@ _SIGS = {
     "kvb_pool_release": ([P, I, P], I),
     "kvb_pool_free_count": ([P, POINTER(c_int32)], I),
     "kvb_embed": ([P, P, P, I, P, P, P, I, P, P], I),
-    "kvb_qkv_proj": ([P, P, P, I, P, P, P, P, P, P, P, P, P], I),
+    "kvb_qkv_proj": ([P, P, P, I, P, P, P, P, P, P, P, P, P, P, c_size_t], I),
     "kvb_rope": ([P, P, P, I, P, P, P, P, P], I),
     "kvb_blend_scatter": ([P, P, P, I, P, P, P, P, P, P, I, P, P, I, P, P, P], I),
     "kvb_sparse_query_attn": ([P, P, P, I, P, P, P, P, P, P, I, P, c_float, P, P, c_size_t], I),
@@ -202,9 +202,10 @@ def kvb_embed(ctx, stream, desc, T_max, n_rows, row_tok, tokens, vocab, table, h
     _call("kvb_embed", ctx, stream, desc, T_max, n_rows, row_tok, tokens, vocab, table, hidden)
 
 
-def kvb_qkv_proj(ctx, stream, desc, T_max, n_rows, row_tok, hidden, norm_w, w_qkv, tok_pos, q, k, v):
+def kvb_qkv_proj(ctx, stream, desc, T_max, n_rows, row_tok, hidden, norm_w, w_qkv, tok_pos, q, k, v,
+                 ws=None, ws_bytes=0):
     _call("kvb_qkv_proj", ctx, stream, desc, T_max, n_rows, row_tok, hidden, norm_w, w_qkv,
-          tok_pos, q, k, v)
+          tok_pos, q, k, v, ws, ws_bytes)
 
 
 def kvb_rope(ctx, stream, desc, T_max, n_rows, row_tok, tok_pos, q, k):

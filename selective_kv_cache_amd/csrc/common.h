@@ -63,6 +63,7 @@ inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 
 // workspace layouts (bytes), shared by kvb_workspace_size and the entry points
 size_t ws_mlp_bytes(const kvb_model_desc* d, int32_t max_rows);
+size_t ws_qkv_bytes(const kvb_model_desc* d, int32_t max_rows);
 size_t ws_topk_bytes(int32_t max_tokens, int32_t max_requests);
 size_t ws_refresh_bytes(int32_t max_tokens, int32_t max_requests);
 size_t ws_attn_bytes(const kvb_model_desc* d, int32_t max_rows, int n_cu);
@@ -102,6 +103,8 @@ template <> struct Store<bf16_t> {
 template <class T> __device__ __forceinline__ float to_f(T v);
 template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
 template <> __device__ __forceinline__ float to_f<bf16_t>(bf16_t v) { return bf2f(v); }
+
+__device__ __forceinline__ int cdiv_dev(int a, int b) { return (a + b - 1) / b; }
 
 __device__ __forceinline__ int row_count(const int32_t* n_rows, int T_max) {
   if (!n_rows) return T_max;

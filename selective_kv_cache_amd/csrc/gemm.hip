@@ -74,100 +74,212 @@ __device__ __forceinline__ void epilogue(const GemmArgs<T>& p, int m, int n, flo
 // ====================================================================== bf16 MFMA
 //
 // Block = 4 waves in a 2 x 2 grid; wave tile = (32 TM) x (32 TN) outputs as
-// TM x TN tiles of v_mfma_f32_32x32x16_bf16; block tile BM = 64 TM, BN = 64 TN
-// rows of B.  K advances in 64-wide steps through double-buffered LDS (row
-// stride 72 elements: conflict-free 16-byte fragment reads); the next step's
-// tiles are fetched into registers while the current one feeds the MFMAs.
+// TM x TN tiles of v_mfma_f32_32x32x16_bf16; block tile BM = 64 TM rows of A
+// and BN = 64 TN rows of B.  K advances 32 at a time through a ring of four
+// LDS stages filled by direct-to-LDS loads (global_load_lds_dwordx4) three
+// stages ahead, so global latency is hidden without staging registers.
+//
+// LDS stage layout: rows of 64 bytes (32 bf16 = four 16-byte chunks); chunk c
+// of row r is stored at position c ^ ((r >> 2) & 3), which makes the 16-byte
+// fragment reads of 16 consecutive rows hit 16 distinct bank groups.  A wave's
+// load instruction fills 1 KiB = 16 rows; its lane j fetches row j / 4, chunk
+// (j % 4) ^ swizzle(row), and lands at position j % 4.
 //
 // SwiGLU (DUAL): the B tile interleaves 32-row subtiles of the gate and up
 // matrices (gate cols c..c+31, up cols c..c+31, ...), so a wave holds gate
 // and up of the same outputs in neighbouring accumulators; BN/2 outputs wide.
+//
+// RMSNorm is not fused here: rmsnorm_rows_kernel writes the normalised rows
+// (bf16, one rounding) to workspace and the GEMM reads them as a plain A.
+// Carrying the row sums and the gains through the K loop cost registers that
+// the 4 x 4 tile does not have.
 
-constexpr int BK = 64, LDK = BK + 8;  // LDS row stride in bf16 elements
+constexpr int KB = 32;          // K per stage
+constexpr int NSTAGE = 4;       // LDS ring depth (prefetch distance 3)
 constexpr int GEMM_THREADS = 256;
+
+// One direct-to-LDS load: 16 bytes per lane from `g`, landing at LDS address
+// lds_base + 16 * lane (lds_base must be wave-uniform).  Issued as inline
+// assembly so that the compiler does not drain these loads before every LDS
+// read (it cannot tell the ring stages apart); completion is tracked with
+// explicit vmcnt waits before the barrier that publishes a stage.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_base) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(size_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// workgroup barrier that orders LDS accesses without draining outstanding
+// global (and LDS-DMA) loads, unlike __syncthreads: this wave's LDS reads and
+// writes complete (lgkmcnt 0) before it arrives
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-// multiply 8 bf16 by 8 bf16 gains, round back to bf16
-__device__ __forceinline__ uint4 mul_gain(const uint4& a, const uint4& g) {
-  const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, gw[4] = {g.x, g.y, g.z, g.w};
-  uint32_t o[4];
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const float lo = __uint_as_float(aw[i] << 16) * __uint_as_float(gw[i] << 16);
-    const float hi = __uint_as_float(aw[i] & 0xffff0000u) * __uint_as_float(gw[i] & 0xffff0000u);
-    o[i] = (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
-  }
-  return make_uint4(o[0], o[1], o[2], o[3]);
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){a, b}, b2_t));
 }
 
-__device__ __forceinline__ float sumsq8(const uint4& a) {
+__device__ __forceinline__ void unpack8(const uint4& a, float (&f)[8]) {
   const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-  float s = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    const float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xffff0000u);
-    s += lo * lo;
-    s += hi * hi;
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
   }
-  return s;
+}
+
+// y[r] = x[a_rows[r]] * rinv_r * g (bf16, one rounding), rinv_r =
+// 1 / sqrt(mean(x^2) + eps), for r < *n_rows; g == NULL means unit gains.
+// One wave per row: lane l sums the 16-byte chunks l, l + 64, ... in order,
+// then a fixed butterfly; the result depends on the row's values only.
+__global__ void __launch_bounds__(256) rmsnorm_rows_kernel(const bf16_t* __restrict__ x,
+                                                           const int32_t* __restrict__ a_rows,
+                                                           const int32_t* __restrict__ n_rows, int T_max, int K,
+                                                           const bf16_t* __restrict__ g, float eps,
+                                                           bf16_t* __restrict__ y) {
+  const int r = blockIdx.x * 4 + (int)(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (r >= row_count(n_rows, T_max)) return;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)(a_rows ? a_rows[r] : r) * K);
+  uint4* yr = reinterpret_cast<uint4*>(y + (size_t)r * K);
+  const int C = K / 8;
+  float s = 0.f;
+  for (int c = lane; c < C; c += 64) {
+    float f[8];
+    unpack8(xr[c], f);
+#pragma unroll
+    for (int e = 0; e < 8; e++) s += f[e] * f[e];
+  }
+  s = wave_sum(s);
+  const float rinv = 1.f / sqrtf(s / (float)K + eps);
+  for (int c = lane; c < C; c += 64) {
+    float f[8], w[8];
+    unpack8(xr[c], f);
+    if (g) unpack8(reinterpret_cast<const uint4*>(g)[c], w);
+#pragma unroll
+    for (int e = 0; e < 8; e++) f[e] = g ? f[e] * rinv * w[e] : f[e] * rinv;
+    yr[c] = make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7]));
+  }
+}
+
+static kvb_status rmsnorm_rows(hipStream_t st, const bf16_t* x, const int32_t* a_rows, const int32_t* n_rows,
+                               int T_max, int K, const bf16_t* g, float eps, bf16_t* y) {
+  {
+    LaunchTimer lt(st, "rmsnorm");
+    rmsnorm_rows_kernel<<<cdiv(T_max, 4), 256, 0, st>>>(x, a_rows, n_rows, T_max, K, g, eps, y);
+  }
+  return check_launch("rmsnorm_rows_kernel");
 }
 
 template <int TM, int TN>
 struct Tile {
   static constexpr int BM = 64 * TM, BN = 64 * TN;
-  static constexpr int A_LD = BM / 32, B_LD = BN / 32;  // 16-byte loads per thread per K step
-  static constexpr size_t LDS = (size_t)2 * (BM + BN) * LDK * sizeof(bf16_t);
-  // the epilogue reuses the same LDS for a [BM/2][OUT_N + 8] float tile
-  static_assert((size_t)(BM / 2) * (BN + 8) * 4 <= LDS, "epilogue tile must fit the K-loop buffers");
+  static constexpr int A_I = BM / 64, B_I = BN / 64;  // load instructions per wave per stage
+  static constexpr int PER = A_I + B_I;
+  static constexpr int STAGE_BYTES = (BM + BN) * 64;
+  static constexpr int EPI_BYTES = 32 * (BN + 8) * 4;  // one 32-row epilogue phase
+  static constexpr int ARR = STAGE_BYTES > EPI_BYTES ? STAGE_BYTES : EPI_BYTES;
 };
 
-template <int MODE, bool DUAL, bool NORM, bool GAIN, int TM, int TN>
+// The four ring stages are separate LDS objects and the K loop is unrolled by
+// four, so the compiler can see that a stage being read is not the one the
+// in-flight loads are filling (one shared object would make it drain every
+// outstanding load before each LDS read).
+template <int TM, int TN, int S>
+struct StageLds {
+  __device__ static uint8_t* ptr() {
+    __shared__ __align__(16) uint8_t buf[Tile<TM, TN>::ARR];
+    return buf;
+  }
+};
+
+template <int MODE, bool DUAL, int TM, int TN>
 __global__ void __launch_bounds__(GEMM_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_bf16_kernel(GemmArgs<bf16_t> p) {
   using TL = Tile<TM, TN>;
-  constexpr int BM = TL::BM, BN = TL::BN, A_LD = TL::A_LD, B_LD = TL::B_LD;
+  constexpr int BM = TL::BM, BN = TL::BN, A_I = TL::A_I, B_I = TL::B_I, PER = TL::PER;
   constexpr int OUT_N = DUAL ? BN / 2 : BN;  // output columns per block
-  extern __shared__ __align__(16) uint8_t smem[];
-  bf16_t* sA = reinterpret_cast<bf16_t*>(smem);  // [2][BM][LDK]
-  bf16_t* sB = sA + 2 * BM * LDK;                // [2][BN][LDK]
-  __shared__ float s_rinv[NORM ? BM : 1];
+  uint8_t* const stg[NSTAGE] = {StageLds<TM, TN, 0>::ptr(), StageLds<TM, TN, 1>::ptr(), StageLds<TM, TN, 2>::ptr(),
+                                StageLds<TM, TN, 3>::ptr()};
 
   const int M = row_count(p.n_rows, p.M_max);
-  const int m0 = blockIdx.x * BM, n0 = blockIdx.y * OUT_N;
+  // Tile rasterisation.  Workgroups go to the 8 XCDs round-robin (id % 8), each
+  // XCD with its own L2: give every XCD a contiguous run of a grouped tile
+  // order (GM m-tiles sweeping all n-tiles), so the tiles an XCD runs at the
+  // same time share A and B panels in its L2.
+  int tm, tn;
+  {
+    const int num_m = cdiv_dev(p.M_max, BM), num_n = cdiv_dev(p.N, OUT_N);
+    const int total = num_m * num_n;
+    const int per = (total + 7) >> 3;
+    const int tid = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+    if (tid >= total) return;
+    const int GM = num_m <= 16 ? num_m : 8;
+    const int gsize = GM * num_n;
+    const int grp = tid / gsize, first = grp * GM;
+    const int gm = min(GM, num_m - first);
+    const int in = tid - grp * gsize;
+    tm = first + in % gm;
+    tn = in / gm;
+  }
+  const int m0 = tm * BM, n0 = tn * OUT_N;
   if (m0 >= M) return;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = (wave >> 1) * (32 * TM), wn = (wave & 1) * (32 * TN);
 
-  // loaders: chunk c = t + 256 i -> tile row c / 8 = t / 8 + 32 i, k-chunk c % 8 = t % 8
-  const int lrow = t >> 3, lkc = t & 7;
-  const bf16_t* a_src[A_LD];
-  const bf16_t* b_src[B_LD];
+  // ---- direct-to-LDS loaders: instruction i of this wave covers tile rows
+  //      (wave * X_I + i) * 16 + lane / 4, lane position lane % 4
+  const int lrow = lane >> 2, lpos = lane & 3;
+  const bf16_t* a_src[A_I];
+  const bf16_t* b_src[B_I];
 #pragma unroll
-  for (int i = 0; i < A_LD; i++) {
-    int m = m0 + lrow + 32 * i;
+  for (int i = 0; i < A_I; i++) {
+    const int r = (wave * A_I + i) * 16 + lrow;
+    int m = m0 + r;
     m = m < M ? m : M - 1;
     const int ar = p.a_rows ? p.a_rows[m] : m;
-    a_src[i] = p.A + (size_t)ar * p.K + lkc * 8;
+    a_src[i] = p.A + (size_t)ar * p.K + ((lpos ^ ((r >> 2) & 3)) * 8);
   }
 #pragma unroll
-  for (int i = 0; i < B_LD; i++) {
-    const int b = lrow + 32 * i;  // B-tile row; subtile b / 32 == i
+  for (int i = 0; i < B_I; i++) {
+    const int r = (wave * B_I + i) * 16 + lrow;  // B-tile row; 32-row subtile r / 32
     const bf16_t* base = p.B;
     int n;
     if (DUAL) {
-      base = (i & 1) ? p.B2 : p.B;
-      n = n0 + (i >> 1) * 32 + (b & 31);
+      base = ((r >> 5) & 1) ? p.B2 : p.B;
+      n = n0 + (r >> 6) * 32 + (r & 31);
     } else {
-      n = n0 + b;
+      n = n0 + r;
     }
     n = n < p.N ? n : p.N - 1;
-    b_src[i] = base + (size_t)n * p.K + lkc * 8;
+    b_src[i] = base + (size_t)n * p.K + ((lpos ^ ((r >> 2) & 3)) * 8);
   }
-  uint4 ra[A_LD], rb[B_LD];
-  float ssq[A_LD];
-#pragma unroll
-  for (int i = 0; i < A_LD; i++) ssq[i] = 0.f;
+  const int KT = p.K / KB;
+#define KVB_ISSUE(KT_, ST_)                                                                       \
+  do {                                                                                            \
+    uint8_t* st_ = (ST_);                                                                         \
+    const int ko_ = (KT_) * KB;                                                                   \
+    _Pragma("unroll") for (int i = 0; i < A_I; i++)                                               \
+      dma16(a_src[i] + ko_, __builtin_amdgcn_readfirstlane(lds_addr(st_ + (wave * A_I + i) * 1024))); \
+    _Pragma("unroll") for (int i = 0; i < B_I; i++)                                               \
+      dma16(b_src[i] + ko_, __builtin_amdgcn_readfirstlane(lds_addr(st_ + BM * 64 + (wave * B_I + i) * 1024))); \
+  } while (0)
 
   f32x16_t acc[TM][TN];
 #pragma unroll
@@ -175,130 +287,107 @@ gemm_bf16_kernel(GemmArgs<bf16_t> p) {
 #pragma unroll
     for (int j = 0; j < TN; j++) acc[i][j] = (f32x16_t){};
 
-  const int KT = p.K / BK;
-  // prologue: tile 0 -> LDS buffer 0
-#pragma unroll
-  for (int i = 0; i < A_LD; i++) ra[i] = *reinterpret_cast<const uint4*>(a_src[i]);
-#pragma unroll
-  for (int i = 0; i < B_LD; i++) rb[i] = *reinterpret_cast<const uint4*>(b_src[i]);
-  {
-    uint4 g = make_uint4(0, 0, 0, 0);
-    if (GAIN) g = *reinterpret_cast<const uint4*>(p.norm_w + lkc * 8);
-#pragma unroll
-    for (int i = 0; i < A_LD; i++) {
-      uint4 a = ra[i];
-      if (NORM) ssq[i] += sumsq8(a);
-      if (GAIN) a = mul_gain(a, g);
-      *reinterpret_cast<uint4*>(sA + (lrow + 32 * i) * LDK + lkc * 8) = a;
-    }
-#pragma unroll
-    for (int i = 0; i < B_LD; i++) *reinterpret_cast<uint4*>(sB + (lrow + 32 * i) * LDK + lkc * 8) = rb[i];
-  }
-  __syncthreads();
+  // fragment addressing: lane reads row (l % 32) of a 32-row subtile, chunk 2 s + l / 32
+  const int fr = lane & 31, fh = lane >> 5, fswz = (fr >> 2) & 3;
+  const int foff0 = fr * 64 + (((0 + fh) ^ fswz) * 16);  // k16 step 0
+  const int foff1 = fr * 64 + (((2 + fh) ^ fswz) * 16);  // k16 step 1
 
-  const int fr = lane & 31, fk = (lane >> 5) * 8;  // fragment row, k offset in a 16-wide slice
-  for (int kt = 0; kt < KT; kt++) {
-    const int buf = kt & 1;
-    // next K step (the last iteration re-fetches its own step; the copy is never read)
-    const int kn = kt + 1 < KT ? kt + 1 : kt;
-    {
-      const int ko = kn * BK;
-#pragma unroll
-      for (int i = 0; i < A_LD; i++) ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + ko);
-#pragma unroll
-      for (int i = 0; i < B_LD; i++) rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + ko);
-    }
-    const bf16_t* a_s = sA + buf * BM * LDK + (wm + fr) * LDK + fk;
-    const bf16_t* b_s = sB + buf * BN * LDK + (wn + fr) * LDK + fk;
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8_t af[TM], bfr[TN];
-#pragma unroll
-      for (int i = 0; i < TM; i++) af[i] = as_bf16x8(*reinterpret_cast<const uint4*>(a_s + i * 32 * LDK + kk));
-#pragma unroll
-      for (int j = 0; j < TN; j++) bfr[j] = as_bf16x8(*reinterpret_cast<const uint4*>(b_s + j * 32 * LDK + kk));
-#pragma unroll
-      for (int i = 0; i < TM; i++)
-#pragma unroll
-        for (int j = 0; j < TN; j++)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    {
-      const int nb = buf ^ 1;
-      const bool fresh = kt + 1 < KT;  // only a real next step adds to the row sums
-      uint4 g = make_uint4(0, 0, 0, 0);
-      if (GAIN) g = *reinterpret_cast<const uint4*>(p.norm_w + kn * BK + lkc * 8);
-#pragma unroll
-      for (int i = 0; i < A_LD; i++) {
-        uint4 a = ra[i];
-        if (NORM) ssq[i] += fresh ? sumsq8(a) : 0.f;
-        if (GAIN) a = mul_gain(a, g);
-        *reinterpret_cast<uint4*>(sA + (nb * BM + lrow + 32 * i) * LDK + lkc * 8) = a;
-      }
-#pragma unroll
-      for (int i = 0; i < B_LD; i++)
-        *reinterpret_cast<uint4*>(sB + (nb * BN + lrow + 32 * i) * LDK + lkc * 8) = rb[i];
-    }
-    __syncthreads();
-  }
+  // Fragments are double-buffered in registers: while the MFMAs of one k16
+  // step run, the reads of the next step (in the same stage, or step 0 of the
+  // next stage) are in flight.  Stage kt+1 is therefore published (vmcnt wait
+  // + barrier) at the start of step kt, and the ring is refilled three stages
+  // ahead into the stage consumed in the previous step.
+  uint4 fa[2][TM], fb[2][TN];
+#define KVB_FRAGS(BUF, STG, FO)                                                                   \
+  do {                                                                                            \
+    const uint8_t* sa_ = (STG) + wm * 64 + (FO);                                                  \
+    const uint8_t* sb_ = (STG) + BM * 64 + wn * 64 + (FO);                                        \
+    _Pragma("unroll") for (int i = 0; i < TM; i++) fa[BUF][i] = *reinterpret_cast<const uint4*>(sa_ + i * 2048); \
+    _Pragma("unroll") for (int j = 0; j < TN; j++) fb[BUF][j] = *reinterpret_cast<const uint4*>(sb_ + j * 2048); \
+  } while (0)
+#define KVB_MMA(BUF)                                                                              \
+  do {                                                                                            \
+    _Pragma("unroll") for (int i = 0; i < TM; i++)                                                \
+      _Pragma("unroll") for (int j = 0; j < TN; j++)                                              \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[BUF][i]), as_bf16x8(fb[BUF][j]), acc[i][j], 0, 0, 0); \
+  } while (0)
+  // one K step on ring stage S (compile-time), with stage S+1 published on entry
+#define KVB_STEP(S, KT_)                                                                          \
+  do {                                                                                            \
+    const int kt_ = (KT_);                                                                        \
+    if (kt_ + 2 < KT) wait_vmcnt<PER>();                                                          \
+    else wait_vmcnt<0>();                                                                         \
+    lds_barrier();                                                                                \
+    if (kt_ + 3 < KT) KVB_ISSUE(kt_ + 3, stg[((S) + 3) & 3]);                                     \
+    KVB_FRAGS(1, stg[S], foff1);                                                                  \
+    KVB_MMA(0);                                                                                   \
+    if (kt_ + 1 < KT) KVB_FRAGS(0, stg[((S) + 1) & 3], foff0);                                    \
+    KVB_MMA(1);                                                                                   \
+  } while (0)
 
-  if (NORM) {
-#pragma unroll
-    for (int i = 0; i < A_LD; i++) {
-      float s = ssq[i];
-      s += __shfl_xor(s, 1, 64);
-      s += __shfl_xor(s, 2, 64);
-      s += __shfl_xor(s, 4, 64);
-      if (lkc == 0) s_rinv[lrow + 32 * i] = 1.f / sqrtf(s / (float)p.K + p.eps);
-    }
-    __syncthreads();
+  if (KT > 0) KVB_ISSUE(0, stg[0]);
+  if (KT > 1) KVB_ISSUE(1, stg[1]);
+  if (KT > 2) KVB_ISSUE(2, stg[2]);
+  // publish stage 0, read its step-0 fragments
+  if (KT > 2) wait_vmcnt<2 * PER>();
+  else if (KT > 1) wait_vmcnt<PER>();
+  else wait_vmcnt<0>();
+  lds_barrier();
+  if (KT > 0) KVB_FRAGS(0, stg[0], foff0);
+  int kt = 0;
+  for (; kt + 4 <= KT; kt += 4) {
+    KVB_STEP(0, kt);
+    KVB_STEP(1, kt + 1);
+    KVB_STEP(2, kt + 2);
+    KVB_STEP(3, kt + 3);
   }
+  if (kt < KT) KVB_STEP(0, kt);
+  if (kt + 1 < KT) KVB_STEP(1, kt + 1);
+  if (kt + 2 < KT) KVB_STEP(2, kt + 2);
+#undef KVB_STEP
+#undef KVB_MMA
+#undef KVB_FRAGS
+#undef KVB_ISSUE
+  wait_vmcnt<0>();
+  lds_barrier();  // every wave is done with the ring before the epilogue reuses LDS
 
-  // Epilogue, staged through LDS in two halves of BM/2 rows: the waves owning a
-  // half write their float accumulators (SwiGLU already combined) to an
-  // [BM/2][OUT_N] tile, then all threads read 8 consecutive outputs of a row,
-  // apply the mode (scale, residual, scatter) and store 16 bytes at a time.
+  // Epilogue, staged through LDS in 2 TM phases of 32 rows: the two waves
+  // owning a phase's rows (subtile i of their half) write their float
+  // accumulators (SwiGLU already combined) to a [32][OUT_N] tile, then all
+  // threads read 8 consecutive outputs of a row, apply the mode (scale,
+  // residual, scatter) and store 16 bytes at a time.
   // acc[i][j][r] sits at tile row wm + 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4,
   // tile col wn + 32 j + lane % 32 (DUAL: output col (wn / 32 + j) / 2 * 32 + lane % 32).
-  constexpr int HR = BM / 2;
   constexpr int LDC = OUT_N + 8;  // floats; rows 4 apart land 32 banks apart
-  float* sC = reinterpret_cast<float*>(smem);
+  float* sC = reinterpret_cast<float*>(stg[0]);
   const int lc = lane & 31;
-  const int my_half = wave >> 1;
 #pragma unroll
-  for (int half = 0; half < 2; half++) {
-    if (my_half == half) {
+  for (int ph = 0; ph < 2 * TM; ph++) {
+    const int i = ph % TM;
+    if ((wave >> 1) == ph / TM) {
 #pragma unroll
       for (int j = 0; j < TN; j += (DUAL ? 2 : 1)) {
         const int cl = DUAL ? ((wn / 32 + j) >> 1) * 32 + lc : wn + j * 32 + lc;
 #pragma unroll
-        for (int i = 0; i < TM; i++)
-#pragma unroll
-          for (int r = 0; r < 16; r++) {
-            const int rl = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);  // row inside the half
-            float v = acc[i][j][r];
-            if (DUAL) {
-              const float rinv = s_rinv[half * HR + rl];
-              v = silu(v * rinv) * (acc[i][j + 1][r] * rinv);
-            }
-            sC[rl * LDC + cl] = v;
-          }
+        for (int r = 0; r < 16; r++) {
+          const int rl = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);  // row inside the phase
+          float v = acc[i][j][r];
+          if (DUAL) v = silu(v) * acc[i][j + 1][r];
+          sC[rl * LDC + cl] = v;
+        }
       }
     }
     __syncthreads();
     constexpr int CPR = OUT_N / 8;  // 8-output chunks per row
-    for (int c = t; c < HR * CPR; c += GEMM_THREADS) {
+    for (int c = t; c < 32 * CPR; c += GEMM_THREADS) {
       const int rl = c / CPR, cc = (c % CPR) * 8;
-      const int ml = half * HR + rl, m = m0 + ml, n = n0 + cc;
+      const int ml = ph * 32 + rl, m = m0 + ml, n = n0 + cc;
       if (m >= M || n >= p.N) continue;
       const float4 lo = *reinterpret_cast<const float4*>(sC + rl * LDC + cc);
       const float4 hi = *reinterpret_cast<const float4*>(sC + rl * LDC + cc + 4);
       float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
       bf16_t* dst;
       if (MODE == EPI_QKV) {
-        const float rinv = s_rinv[ml];
-#pragma unroll
-        for (int e = 0; e < 8; e++) v[e] *= rinv;
         if (n < p.n0) dst = p.out0 + (size_t)m * p.n0 + n;
         else if (n < p.n1) dst = p.out1 + (size_t)m * (p.n1 - p.n0) + (n - p.n0);
         else dst = p.out2 + (size_t)m * (p.N - p.n1) + (n - p.n1);
@@ -316,61 +405,39 @@ gemm_bf16_kernel(GemmArgs<bf16_t> p) {
         const int orow = (MODE == EPI_SCATTER && p.out_rows) ? p.out_rows[m] : m;
         dst = p.out0 + (size_t)orow * p.ldo + n;
       }
-      uint4 o;
-      o.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-      o.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
-      o.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
-      o.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
-      *reinterpret_cast<uint4*>(dst) = o;
+      *reinterpret_cast<uint4*>(dst) = make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]),
+                                                  pack2(v[6], v[7]));
     }
     __syncthreads();
   }
 }
 
-template <int MODE, bool DUAL, bool NORM, bool GAIN, int TM, int TN>
+template <int MODE, bool DUAL, int TM, int TN>
 static kvb_status launch_bf16(hipStream_t st, const GemmArgs<bf16_t>& p, const char* name) {
   using TL = Tile<TM, TN>;
   constexpr int OUT_N = DUAL ? TL::BN / 2 : TL::BN;
-  dim3 grid(cdiv(p.M_max, TL::BM), cdiv(p.N, OUT_N));
-  static bool attr_set = false;  // opt in to > 64 KiB of dynamic LDS once per instantiation
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<MODE, DUAL, NORM, GAIN, TM, TN>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)TL::LDS);
-    if (e != hipSuccess) return fail(KVB_ERR_HIP, std::string("hipFuncSetAttribute: ") + hipGetErrorString(e));
-    attr_set = true;
-  }
+  const int total = cdiv(p.M_max, TL::BM) * cdiv(p.N, OUT_N);
+  dim3 grid(((total + 7) / 8) * 8);
   {
     LaunchTimer lt(st, name);
-    gemm_bf16_kernel<MODE, DUAL, NORM, GAIN, TM, TN><<<grid, GEMM_THREADS, TL::LDS, st>>>(p);
+    gemm_bf16_kernel<MODE, DUAL, TM, TN><<<grid, GEMM_THREADS, 0, st>>>(p);
   }
   return check_launch("gemm_bf16_kernel");
 }
 
-// Tile choice: the per-element reduction order (64-wide K steps, 16-wide MFMA
+// Tile choice: the per-element reduction order (32-wide K stages, 16-wide MFMA
 // slices in order) is the same for every tile shape, so picking the shape from
 // the launch bound keeps every row's result independent of the batch.
-template <int MODE, bool DUAL, bool NORM, bool GAIN>
-static kvb_status run_bf16_g(hipStream_t st, const GemmArgs<bf16_t>& p, const char* name) {
+template <int MODE, bool DUAL>
+static kvb_status run_bf16(hipStream_t st, const GemmArgs<bf16_t>& p, const char* name) {
+  if (p.M_max == 0 || p.N == 0) return KVB_OK;
   const Ctx* c = current_ctx();
   const long cus = c ? c->n_cu : 256;
   const long big_blocks = (long)cdiv(p.M_max, 256) * cdiv(p.N, DUAL ? 128 : 256);
-  if (big_blocks >= cus) return launch_bf16<MODE, DUAL, NORM, GAIN, 4, 4>(st, p, name);
+  if (big_blocks >= cus) return launch_bf16<MODE, DUAL, 4, 4>(st, p, name);
   const long mid_blocks = (long)cdiv(p.M_max, 256) * cdiv(p.N, DUAL ? 64 : 128);
-  if (mid_blocks >= cus) return launch_bf16<MODE, DUAL, NORM, GAIN, 4, 2>(st, p, name);
-  return launch_bf16<MODE, DUAL, NORM, GAIN, 2, 2>(st, p, name);
-}
-
-// Tile choice: the per-element reduction order (64-wide K steps, 16-wide MFMA
-// slices in order) is the same for every tile shape, so picking the shape from
-// the launch bound keeps every row's result independent of the batch.  RMSNorm
-// gains are applied to A only when given (NULL = unit gains).
-template <int MODE, bool DUAL, bool NORM>
-static kvb_status run_bf16(hipStream_t st, const GemmArgs<bf16_t>& p, const char* name) {
-  if (p.M_max == 0 || p.N == 0) return KVB_OK;
-  if constexpr (NORM) {
-    if (p.norm_w) return run_bf16_g<MODE, DUAL, NORM, true>(st, p, name);
-  }
-  return run_bf16_g<MODE, DUAL, NORM, false>(st, p, name);
+  if (mid_blocks >= cus) return launch_bf16<MODE, DUAL, 4, 2>(st, p, name);
+  return launch_bf16<MODE, DUAL, 2, 2>(st, p, name);
 }
 
 // ====================================================================== fp32 FMA
@@ -474,12 +541,9 @@ kvb_status launch_rope(hipStream_t st, int T_max, const int32_t* n_rows, const i
 template <class T>
 static kvb_status qkv_impl(hipStream_t st, const kvb_model_desc* d, int T_max, const int32_t* n_rows,
                            const int32_t* row_tok, const void* hidden, const void* norm_w, const void* w_qkv,
-                           const int32_t* tok_pos, void* q, void* k, void* v) {
+                           const int32_t* tok_pos, void* q, void* k, void* v, void* ws) {
   GemmArgs<T> p{};
-  p.A = (const T*)hidden;
-  p.a_rows = row_tok;
   p.B = (const T*)w_qkv;
-  p.norm_w = (const T*)norm_w;
   p.M_max = T_max;
   p.n_rows = n_rows;
   p.K = d->d_model;
@@ -490,8 +554,19 @@ static kvb_status qkv_impl(hipStream_t st, const kvb_model_desc* d, int T_max, c
   p.out0 = (T*)q;
   p.out1 = (T*)k;
   p.out2 = (T*)v;
-  if constexpr (sizeof(T) == 2) KVB_TRY((run_bf16<EPI_QKV, false, true>(st, p, "gemm_qkv")));
-  else KVB_TRY((run_f32<EPI_QKV, false, true>(st, p, "gemm_qkv")));
+  if constexpr (sizeof(T) == 2) {
+    // normalised rows a [T, d] in workspace, then a plain GEMM
+    bf16_t* a = (bf16_t*)ws;
+    KVB_TRY(rmsnorm_rows(st, (const bf16_t*)hidden, row_tok, n_rows, T_max, d->d_model, (const bf16_t*)norm_w,
+                         d->rms_eps, a));
+    p.A = a;
+    KVB_TRY((run_bf16<EPI_QKV, false>(st, p, "gemm_qkv")));
+  } else {
+    p.A = (const T*)hidden;
+    p.a_rows = row_tok;
+    p.norm_w = (const T*)norm_w;
+    KVB_TRY((run_f32<EPI_QKV, false, true>(st, p, "gemm_qkv")));
+  }
   if (tok_pos) return launch_rope<T>(st, T_max, n_rows, row_tok, tok_pos, q, k, d);
   return KVB_OK;
 }
@@ -501,8 +576,11 @@ static kvb_status mlp_impl(hipStream_t st, const kvb_model_desc* d, int T_max, c
                            const int32_t* row_tok, const void* attn_o, const void* w_o, void* hidden,
                            const void* norm2_w, const void* w_gate_up, const void* w_down, void* ws) {
   const int D = d->d_model, F = d->ffn, QD = d->n_q_heads * d->head_dim;
+  // workspace: h1 [T, d], u [T, F], then (bf16) the normalised h1 [T, d]
+  const size_t h1_bytes = align_up((size_t)T_max * D * sizeof(T), 256);
   T* h1 = (T*)ws;
-  T* u = (T*)((char*)ws + align_up((size_t)T_max * D * sizeof(T), 256));
+  T* u = (T*)((char*)ws + h1_bytes);
+  T* hn = (T*)((char*)ws + h1_bytes + align_up((size_t)T_max * F * sizeof(T), 256));
   // h1 = hidden[row] + o W_o^T
   GemmArgs<T> a{};
   a.A = (const T*)attn_o;
@@ -543,9 +621,12 @@ static kvb_status mlp_impl(hipStream_t st, const kvb_model_desc* d, int T_max, c
   c.ldr = D;
   c.out_rows = row_tok;
   if constexpr (sizeof(T) == 2) {
-    KVB_TRY((run_bf16<EPI_RESID, false, false>(st, a, "gemm_oproj")));
-    KVB_TRY((run_bf16<EPI_SWIGLU, true, true>(st, b, "gemm_swiglu")));
-    return run_bf16<EPI_SCATTER, false, false>(st, c, "gemm_down");
+    KVB_TRY((run_bf16<EPI_RESID, false>(st, a, "gemm_oproj")));
+    KVB_TRY(rmsnorm_rows(st, h1, nullptr, n_rows, T_max, D, (const bf16_t*)norm2_w, d->rms_eps, hn));
+    b.A = hn;
+    b.norm_w = nullptr;
+    KVB_TRY((run_bf16<EPI_SWIGLU, true>(st, b, "gemm_swiglu")));
+    return run_bf16<EPI_SCATTER, false>(st, c, "gemm_down");
   } else {
     KVB_TRY((run_f32<EPI_RESID, false, false>(st, a, "gemm_oproj")));
     KVB_TRY((run_f32<EPI_SWIGLU, true, true>(st, b, "gemm_swiglu")));
@@ -560,7 +641,7 @@ using namespace kvb;
 extern "C" kvb_status kvb_qkv_proj(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t T_max,
                                    const int32_t* n_rows, const int32_t* row_tok, const void* hidden,
                                    const void* norm_w, const void* w_qkv, const int32_t* tok_pos, void* q, void* k,
-                                   void* v) {
+                                   void* v, void* ws, size_t ws_bytes) {
   KVB_TRY(check_ctx(ctx));
   KVB_TRY(check_desc(desc));
   if (T_max < 0) return fail(KVB_ERR_INVALID_ARG, "T_max < 0");
@@ -570,11 +651,13 @@ extern "C" kvb_status kvb_qkv_proj(kvb_ctx* ctx, void* stream, const kvb_model_d
   KVB_CHECK_PTR(q, "q");
   KVB_CHECK_PTR(k, "k");
   KVB_CHECK_PTR(v, "v");
+  const size_t need = ws_qkv_bytes(desc, T_max);
+  if (need && (!ws || ws_bytes < need)) return fail(KVB_ERR_WORKSPACE, "kvb_qkv_proj workspace too small");
   CtxScope scope(ctx);
   hipStream_t st = (hipStream_t)stream;
   if (desc->dtype == KVB_BF16)
-    return qkv_impl<bf16_t>(st, desc, T_max, n_rows, row_tok, hidden, norm_w, w_qkv, tok_pos, q, k, v);
-  return qkv_impl<float>(st, desc, T_max, n_rows, row_tok, hidden, norm_w, w_qkv, tok_pos, q, k, v);
+    return qkv_impl<bf16_t>(st, desc, T_max, n_rows, row_tok, hidden, norm_w, w_qkv, tok_pos, q, k, v, ws);
+  return qkv_impl<float>(st, desc, T_max, n_rows, row_tok, hidden, norm_w, w_qkv, tok_pos, q, k, v, ws);
 }
 
 extern "C" kvb_status kvb_mlp(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t T_max,

@@ -232,7 +232,7 @@ class LinkEngine:
         for l in range(1, self.L + 1):
             W = m.layers[l - 1]
             K.kvb_qkv_proj(c, sh, ds, Nc, None, None, self.hidden_c, W["norm1"], W["w_qkv"], self.pos_c,
-                           self.q, self.k, self.v)
+                           self.q, self.k, self.v, self.ws, self.ws_bytes)
             K.kvb_blend_scatter(c, sh, ds, Nc, None, None, self.k, self.v, self.k_pool, self.v_pool, self.n_pages,
                                 None, self.comp_slot[l - 1], K.KVB_ALPHA_ONE, None, None, None)
             if l < self.L:
@@ -256,7 +256,7 @@ class LinkEngine:
         K.kvb_slot_map(c, sh, ds, self.B, self.N, T, cu_rows, rows, self.reuse_slot[l - 1], self.new_pages[l],
                        self.cu_pages[l], self.slot_map, self.dst_slot)
         K.kvb_qkv_proj(c, sh, ds, T, n_rows, rows, self.hidden, W["norm1"], W["w_qkv"], self.pos_l, self.q, self.k,
-                       self.v)
+                       self.v, self.ws, self.ws_bytes)
         K.kvb_blend_scatter(c, sh, ds, T, n_rows, rows, self.k, self.v, self.k_pool, self.v_pool, self.n_pages,
                             src_slot, self.dst_slot, alpha_mode, alpha, d_out, cksim_out)
         K.kvb_sparse_query_attn(c, sh, ds, T, n_rows, rows, self.lo_l, self.q, self.k_pool, self.v_pool,

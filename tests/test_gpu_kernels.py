@@ -49,6 +49,11 @@ def sh():
     return K.stream_handle()
 
 
+def workspace(ctx, desc, T_max, n_tok=1, B=1):
+    wsb = K.kvb_workspace_size(ctx, desc, T_max, n_tok, B)
+    return torch.empty(max(wsb, 1), dtype=torch.uint8, device=DEV), wsb
+
+
 def weights(shape, g):
     d, F = shape.d_model, shape.ffn
     dt = tdt(shape)
@@ -79,8 +84,9 @@ def test_qkv_proj_rope(ctx, name):
     q = torch.full((T_max, s.n_q_heads, s.head_dim), 7.0, dtype=dt, device=DEV)
     k = torch.full((T_max, s.n_kv_heads, s.head_dim), 7.0, dtype=dt, device=DEV)
     v = torch.full((T_max, s.n_kv_heads, s.head_dim), 7.0, dtype=dt, device=DEV)
+    ws, wsb = workspace(ctx, desc, T_max)
     K.kvb_qkv_proj(ctx, sh(), desc, T_max, i32([n_valid]), i32(rows), hidden, W["norm1"], W["w_qkv"], i32(pos),
-                   q, k, v)
+                   q, k, v, ws, wsb)
     torch.cuda.synchronize()
     Wn = {kk: np64(vv) for kk, vv in W.items()}
     rq, rk, rv = OM.qkv(np64(hidden)[rows[:n_valid]], pos[rows[:n_valid]], Wn, s)
@@ -107,7 +113,8 @@ def test_qkv_rows_are_batch_invariant(ctx, name):
         q = torch.empty((T, s.n_q_heads, s.head_dim), dtype=dt, device=DEV)
         k = torch.empty((T, s.n_kv_heads, s.head_dim), dtype=dt, device=DEV)
         v = torch.empty((T, s.n_kv_heads, s.head_dim), dtype=dt, device=DEV)
-        K.kvb_qkv_proj(ctx, sh(), desc, T, None, i32(rows), hidden, W["norm1"], W["w_qkv"], pos, q, k, v)
+        ws, wsb = workspace(ctx, desc, T)
+        K.kvb_qkv_proj(ctx, sh(), desc, T, None, i32(rows), hidden, W["norm1"], W["w_qkv"], pos, q, k, v, ws, wsb)
         outs.append((q, k, v))
     torch.cuda.synchronize()
     for a, b in zip(outs[0], outs[1]):

@@ -121,6 +121,10 @@ def test_null_and_size_checks_enqueue_nothing(lib):
     with pytest.raises(K.KvbError) as e:
         K.kvb_deviation_topk(FAKE_CTX, None, d, 1, 16, 1, 1, 1, 4, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 8)
     assert e.value.status == K.KVB_ERR_WORKSPACE
+    with pytest.raises(K.KvbError) as e:  # bf16 normalises into the workspace
+        K.kvb_qkv_proj(FAKE_CTX, None, _desc(dtype=K.KVB_BF16, d_model=512, ffn=1536, n_q_heads=8, head_dim=128),
+                       4, None, None, 1, 1, 1, None, 1, 1, 1, None, 0)
+    assert e.value.status == K.KVB_ERR_WORKSPACE
     # zero-size calls are valid no-ops
     K.kvb_qkv_proj(FAKE_CTX, None, d, 0, None, None, None, None, None, None, None, None, None)
     K.kvb_mlp(FAKE_CTX, None, d, 0, None, None, None, None, None, None, None, None, None, 0)
