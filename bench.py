@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+COPY_BYTES = 256 << 20         # copy probe of --profile-only (fp32 multiply by 1, out of place)
 
 
 def parse():
@@ -66,9 +67,10 @@ BOUND = {"gemm_qkv": "mfma", "gemm_oproj": "mfma", "gemm_swiglu": "mfma", "gemm_
          "blend_scatter": "hbm", "deviation": "hbm", "rope": "hbm", "embed": "hbm"}
 
 
-def cpu_baseline(w, eng, rec_state, budget_note):
+def cpu_baseline(w, eng, rec_state, step_flops):
     """Time the oracle as it stands on a bounded sample: one selective layer (l = 2)
-    over every selected row, fed the GPU's layer-1 state; scale to the link step."""
+    over every selected row, fed the GPU's layer-1 state; scale to the link step by
+    the step's algorithmic FLOPs (realised rows of every layer) over layer 2's."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_info
@@ -95,11 +97,10 @@ def cpu_baseline(w, eng, rec_state, budget_note):
     N, k = eng.N, len(sel)
     per_row = 2.0 * (d * (Hq + 2 * Hkv) * hd + Hq * hd * d + 3 * d * F)
     f2 = k * per_row + 4.0 * Hq * hd * float(np.sum(np.asarray(sel) + 1))
-    f1 = N * per_row + 2.0 * Hq * hd * N * (N + 1)
-    t_link = t2 * (s.n_layers - 1) + t2 * f1 / f2
+    t_link = t2 * step_flops / f2
     return {"value": k / t_link, "unit": "selected-tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": (f"oracle layer 2 over all {k} selected rows of the {N}-token request (float64 numpy, "
-                       f"{threads} BLAS threads): {t2:.2f} s; link time scaled as T2*(L-1) + T2*FLOPs(layer 1)/"
+                       f"{threads} BLAS threads): {t2:.2f} s; link time scaled as T2 * FLOPs(link step) / "
                        f"FLOPs(layer 2) = {t_link:.1f} s"),
             "measured_s": t2, "extrapolated_link_s": t_link}
 
@@ -189,7 +190,17 @@ def main():
     dom = K.kvb_timing_read(eng.ctx)[dominant]
     K.kvb_timing_enable(eng.ctx, None)
     if args.profile_only:
-        print(json.dumps({"profile_only": True, "ms_per_step": float(np.mean(step_ms))}), flush=True)
+        # plain copy of known size (read + write COPY_BYTES each): the yardstick
+        # that scales the FETCH_SIZE / WRITE_SIZE counters to bytes
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_only": True, "workload": w.name, "ms_per_step": float(np.mean(step_ms)),
+                          "dominant": dominant, "dominant_avg_ms": dom["ms"] / dom["count"],
+                          "dominant_launches_per_step": dom["count"] / args.steps, "steps": args.steps,
+                          "copy_bytes": COPY_BYTES}), flush=True)
         return
     ms = float(np.mean(step_ms))
     dom_avg_ms = dom["ms"] / dom["count"]
@@ -244,7 +255,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "mode": cfg.mode, "requests": B, "n_tokens": eng.N, "n_layers": s.n_layers,
                    "selected": n_selected, "ratio": w.ratio, "tau": w.tau,
-                   "recomputed_row_layers": int(sum(rows_per_layer))},
+                   "recomputed_row_layers": int(sum(rows_per_layer)), "rows_per_layer": rows_per_layer},
         "roofline": {"kernel": dominant, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": traffic, "avg_launch_ms": dom_avg_ms,
                      "work_per_launch": dom_work_per_launch},
@@ -253,7 +264,8 @@ def main():
     }
     if not args.no_cpu_baseline and cfg.mode == "cacheslide":
         try:
-            out["cpu_baseline"] = cpu_baseline(w, eng, state1, None)
+            step_flops = sum(work[k] for k, b in BOUND.items() if b == "mfma")
+            out["cpu_baseline"] = cpu_baseline(w, eng, state1, step_flops)
         except Exception as e:  # the GPU figure stands; say why the CPU leg is missing
             out["cpu_baseline"] = {"value": None, "error": repr(e)}
     print(json.dumps(out), flush=True)
