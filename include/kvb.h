@@ -194,8 +194,12 @@ kvb_status kvb_blend_scatter(kvb_ctx* ctx, void* stream, const kvb_model_desc* d
  * A = softmax(Q K_exp^T, causal) over all N tokens, O = A V_exp).  Row r
  * (token g = row_tok[r]) attends the keys j with tok_lo[g] <= j <= g, read
  * from slot slot_map[j] of the pools; query head h reads KV head
- * h / (Hq / Hkv); scores are scaled by `scale`.
- * q [T, Hq, hd]; slot_map [n_tok]; o [T, Hq * hd]. */
+ * h / (Hq / Hkv); scores are scaled by `scale`.  A key whose slot lies
+ * outside [0, 16 n_pages) is left out of the softmax, as if masked; a row
+ * with no key left gets O = 0.
+ * q [T, Hq, hd]; slot_map [n_tok]; o [T, Hq * hd].  bf16 splits long key
+ * ranges over several workgroups when ws holds the partial results
+ * (kvb_workspace_size); with less workspace it runs unsplit. */
 kvb_status kvb_sparse_query_attn(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc,
                                  int32_t T_max, const int32_t* n_rows, const int32_t* row_tok,
                                  const int32_t* tok_lo, const void* q, const void* k_pool,

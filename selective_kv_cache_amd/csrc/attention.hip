@@ -5,19 +5,19 @@
 // bf16 path (gfx950 MFMA, flash-style online softmax):
 //   * one block = one KV head x 256 query rows, a query row being a (token,
 //     query head of the GQA group) pair, so the whole group shares every K/V
-//     tile; 4 waves x 64 query rows (two 32-wide MFMA column tiles);
-//   * key tiles of 64 tokens are gathered row by row through the per-token
-//     slot map, prefetched into registers while the previous tile computes;
+//     tile; 8 waves x 32 query rows, two waves per SIMD;
+//   * key tiles of 64 tokens are gathered through the per-token slot map by
+//     direct-to-LDS loads into a 3-stage ring, two tiles ahead;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: a lane ends with 16 scores of
 //     one query, which is already the B-operand layout of O^T = V^T P^T, so
 //     probabilities stay in registers; softmax statistics need one xor-32
 //     exchange per query;
-//   * the V tile is stored transposed (dims x keys) with key bits 2 and 3
-//     swapped, so each V^T operand is one 16-byte LDS read;
-//   * only tiles that cross a query's causal edge or its lower bound are
-//     masked; blocks run longest first;
+//   * V stays row-major in LDS; V^T operands come from the transposing LDS
+//     read of gfx950;
+//   * only tiles that cross a query's causal edge or its lower bound, or that
+//     hold a key without a valid slot, are masked; blocks run longest first;
 //   * split-KV: with few query blocks the key range of each block is cut into
-//     n_split parts whose partial (O, max, sum) a merge kernel combines.
+//     n_split parts whose partial (O, offset, sum) a merge kernel combines.
 // fp32 path: one wave per (row, query head), plain online softmax.
 #include "common.h"
 
@@ -27,15 +27,11 @@ __device__ __forceinline__ size_t kv_off(int slot, int h, int Hkv, int hd) {
   return (((size_t)(slot >> 4) * Hkv + h) * 16 + (slot & 15)) * hd;
 }
 
-__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
-  typedef float f2_t __attribute__((ext_vector_type(2)));
-  typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){a, b}, b2_t));
-}
-
 constexpr int AQ = 256;        // query rows per block
 constexpr int AKT = 64;        // keys per tile
-constexpr int ATHREADS = 256;
+constexpr int ANST = 3;        // LDS ring stages (tiles in flight: 2 ahead)
+constexpr int AWAVES = 8;      // 32 query rows each
+constexpr int ATHREADS = 64 * AWAVES;
 
 struct AttnArgs {
   int T_max;
@@ -55,16 +51,63 @@ struct AttnArgs {
   float* part_ml;  // [n_split][T_max][Hq][2]
 };
 
+// K / V tile geometry in LDS: 64 key rows of HD bf16, row-major, the 16-byte
+// chunk c of row r stored at chunk position c ^ swizzle(r).  One direct-to-LDS
+// instruction fills 1 KiB = RPI rows; wave w fills rows 8 w .. 8 w + 7.
 template <int HD>
-__global__ void __launch_bounds__(ATHREADS) attn_bf16_kernel(AttnArgs a) {
-  constexpr int LDK_ = HD + 8;     // K tile row stride (bf16)
-  constexpr int LDV_ = AKT + 8;    // transposed V tile row stride (bf16)
-  constexpr int KS = HD / 16;      // k16 steps of Q K^T
-  constexpr int DT = HD / 32;      // 32-wide dim tiles of P V
-  constexpr int CPR = HD / 8;      // 16-byte chunks per K/V row
-  constexpr int LOADS = AKT * CPR / ATHREADS;
-  __shared__ __align__(16) bf16_t sK[AKT * LDK_];
-  __shared__ __align__(16) bf16_t sVt[HD * LDV_];
+struct AttnGeom {
+  static constexpr int ROWB = HD * 2;                // bytes per key row
+  static constexpr int CPR = HD / 8;                 // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;               // rows per 1 KiB instruction
+  static constexpr int TILE = AKT * ROWB;            // bytes of one K (or V) tile
+  static constexpr int IPW = TILE / 1024 / AWAVES;   // instructions per wave per tile
+  static constexpr int STAGE = 2 * TILE;             // K tile, then V tile
+  // K: the fragment read of 16 consecutive rows at one chunk hits 16 distinct
+  // bank groups.  V: the transposing read of 4 consecutive rows x 4 chunks
+  // hits 16 distinct bank groups.  Both depend on the low row bits only.
+  __device__ __forceinline__ static int swz_k(int r) { return HD == 128 ? (r & 15) : ((r >> 1) & 7); }
+  __device__ __forceinline__ static int swz_v(int r) { return HD == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2); }
+};
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// gfx950 transposing LDS read: in every 16-lane group, lane i receives element
+// i % 4 of the 8 bytes addressed by lanes i / 4 + 4 s of the group, s = 0..3.
+__device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// Block: one KV head x AQ query rows, a query row being a (token, query head of
+// the GQA group) pair; 8 waves x 32 rows.  At most 256 registers per wave, so
+// two waves share a SIMD and one's MFMAs overlap the other's softmax.
+//
+// Per 64-key tile (ring stage X % 3), in two 32-key halves:
+//   S^T = K Q^T       v_mfma_f32_32x32x16_bf16, A = K rows from LDS, B = Q held
+//                     in registers; a lane ends with 16 scores of one query
+//                     (keys 8 (r / 4) + 4 (lane / 32) + r % 4 of the half);
+//   softmax           base 2, scale folded into one FMA; the running offset
+//                     m only moves (and O is rescaled) when a half's maximum
+//                     exceeds it by more than 8, so rescales are rare;
+//   O^T += V^T P^T    P^T is the lane's own scores (bf16) with the key order
+//                     of each 16-key step permuted the same way on both sides;
+//                     V^T fragments come from the row-major V tile through the
+//                     transposing LDS read.
+// Tiles are gathered through the per-token slot map by direct-to-LDS loads two
+// tiles ahead; the slot indices of a tile arrive the same way one tile earlier,
+// so no load the compiler can see is waited on inside the loop.  A key whose
+// slot is outside the pool is excluded from every row's softmax.
+template <int HD>
+__global__ void __launch_bounds__(ATHREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_bf16_kernel(AttnArgs a) {
+  using Gm = AttnGeom<HD>;
+  constexpr int KS = HD / 16;  // k16 steps of Q K^T
+  constexpr int DT = HD / 32;  // 32-wide dim tiles of P V
+  constexpr int ROWB = Gm::ROWB, CPR = Gm::CPR, RPI = Gm::RPI, IPW = Gm::IPW, TILE = Gm::TILE;
+  static_assert(IPW * RPI == 8, "a wave loads 8 key rows");
+  __shared__ __align__(16) uint8_t s_kv[ANST * Gm::STAGE];
+  __shared__ __align__(16) int32_t s_slot[ANST][AWAVES][64];  // per stage, wave: keys 8 w + (lane % 8)
+  __shared__ uint32_t s_inval[ANST][AWAVES];                   // invalid-slot bits of the wave's 8 keys
   __shared__ int s_kmin, s_kmax, s_pmin, s_lomax;
 
   const int G = a.Hq / a.Hkv;
@@ -74,8 +117,9 @@ __global__ void __launch_bounds__(ATHREADS) attn_bf16_kernel(AttnArgs a) {
   const int h = blockIdx.y, split = blockIdx.z;
   const int r0 = qb * TB;
   if (r0 >= M) return;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int l32 = lane & 31, g2 = lane >> 5;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int l32 = lane & 31, g2 = lane >> 5, l16 = lane & 15;
 
   if (t == 0) {
     s_kmin = 0x7fffffff;
@@ -97,194 +141,233 @@ __global__ void __launch_bounds__(ATHREADS) attn_bf16_kernel(AttnArgs a) {
   const int kmin = s_kmin, kmax = s_kmax, pmin = s_pmin, lomax = s_lomax;
   const int ntiles = (kmax - kmin) / AKT + 1;
   const int t_begin = (int)((long)ntiles * split / a.n_split);
-  const int t_end = (int)((long)ntiles * (split + 1) / a.n_split);
+  const int nt = (int)((long)ntiles * (split + 1) / a.n_split) - t_begin;
+  const int kbase = kmin + t_begin * AKT;  // first key of tile 0
 
-  // this lane's queries: column l32 of query tiles qt = 0, 1
-  int qpos[2], qlo[2];
-  bool qvalid[2];
-  bf16x8_t qf[2][KS];
-#pragma unroll
-  for (int qt = 0; qt < 2; qt++) {
-    const int m = wave * 64 + qt * 32 + l32;
+  // this lane's query: column l32 of the wave's query tile
+  int qpos, qlo;
+  bool qvalid;
+  bf16x8_t qf[KS];
+  {
+    const int m = wave * 32 + l32;
     const int r = r0 + m / G, hq = h * G + m % G;
-    qvalid[qt] = r < M;
-    if (qvalid[qt]) {
+    qvalid = r < M;
+    if (qvalid) {
       const int g = a.row_tok ? a.row_tok[r] : r;
-      qpos[qt] = g;
-      qlo[qt] = a.tok_lo[g];
+      qpos = g;
+      qlo = a.tok_lo[g];
       const bf16_t* qp = a.q + ((size_t)r * a.Hq + hq) * HD + g2 * 8;
 #pragma unroll
       for (int ks = 0; ks < KS; ks++)
-        qf[qt][ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qp + ks * 16));
+        qf[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qp + ks * 16));
     } else {
-      qpos[qt] = -1;
-      qlo[qt] = 0x7fffffff;
+      qpos = -1;
+      qlo = 0x7fffffff;
 #pragma unroll
-      for (int ks = 0; ks < KS; ks++) qf[qt][ks] = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
+      for (int ks = 0; ks < KS; ks++) qf[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
     }
   }
 
-  f32x16_t oacc[DT][2];
+  // per-lane LDS byte offsets of the fragment reads inside a stage:
+  //   K fragment (half kt, step ks): row 32 kt + l32, chunk 2 ks + g2
+  //   V^T fragment (step c, dims 32 dt, part u): source row 16 c + 8 u + 4 g2 + l16 / 4,
+  //     dims 32 dt + 16 ((lane / 16) % 2) + 4 (l16 % 4) .. + 3
+  // the swizzles depend on the low row bits only, so kt, c and u are immediates.
+  int koff[KS], voff[DT];
 #pragma unroll
-  for (int dt = 0; dt < DT; dt++) oacc[dt][0] = oacc[dt][1] = (f32x16_t){};
-  float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
-
-  uint4 rk[LOADS], rv[LOADS];
-  // chunk c = t + 256 i: key c / CPR, part c % CPR
-#define ATTN_GLOAD(J0)                                                        \
-  _Pragma("unroll") for (int i = 0; i < LOADS; i++) {                         \
-    const int c = t + ATHREADS * i;                                           \
-    const int key = (J0) + c / CPR, part = c % CPR;                           \
-    int slot = -1;                                                            \
-    if (key <= kmax) slot = a.slot_map[key];                                  \
-    if (slot >= 0 && slot < a.n_slots) {                                      \
-      const size_t off = kv_off(slot, h, a.Hkv, HD) + part * 8;               \
-      rk[i] = *reinterpret_cast<const uint4*>(a.k_pool + off);                \
-      rv[i] = *reinterpret_cast<const uint4*>(a.v_pool + off);                \
-    } else {                                                                  \
-      rk[i] = rv[i] = make_uint4(0, 0, 0, 0);                                 \
-    }                                                                         \
+  for (int ks = 0; ks < KS; ks++) koff[ks] = l32 * ROWB + (((2 * ks + g2) ^ Gm::swz_k(l32)) * 16);
+  {
+    const int vr = 4 * g2 + (l16 >> 2);
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++) {
+      const int chunk = 4 * dt + 2 * ((lane >> 4) & 1) + ((l16 >> 1) & 1);
+      voff[dt] = TILE + vr * ROWB + ((chunk ^ Gm::swz_v(vr)) * 16) + 8 * (l16 & 1);
+    }
   }
 
-  if (t_begin < t_end) {
-    ATTN_GLOAD(kmin + t_begin * AKT);
-  }
-  for (int ti = t_begin; ti < t_end; ti++) {
-    const int j0 = kmin + ti * AKT;
-    __syncthreads();  // previous tile fully consumed
+  f32x16_t oacc[DT];
 #pragma unroll
-    for (int i = 0; i < LOADS; i++) {
-      const int c = t + ATHREADS * i;
-      const int key = c / CPR, part = c % CPR;
-      *reinterpret_cast<uint4*>(sK + key * LDK_ + part * 8) = rk[i];
-      // key k = 16 c + 8 h + 4 g + r goes to column 16 c + 8 g + 4 h + r (bits 2 and 3 swapped)
-      const int col = (key & ~15) | ((key & 4) << 1) | ((key & 8) >> 1) | (key & 3);
-      const uint32_t w[4] = {rv[i].x, rv[i].y, rv[i].z, rv[i].w};
+  for (int dt = 0; dt < DT; dt++) oacc[dt] = (f32x16_t){};
+  float moff = -INFINITY, lrow = 0.f;
+
+  // The per-lane parts of the load addresses are recomputed at every issue from
+  // `ln`, which the empty asm makes opaque: hoisted out of the loop they would
+  // take registers for the whole loop.
+  // slot indices of tile X's 8 keys of this wave -> s_slot[X % 3][wave] (1 load per lane)
+  auto issue_slots = [&](int X) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    int key = kbase + X * AKT + wave * 8 + (ln & 7);
+    key = key < kmax ? key : kmax;  // keys past the block's last query are masked anyway
+    dma4(a.slot_map + key, __builtin_amdgcn_readfirstlane(lds_addr(&s_slot[X % ANST][wave][0])));
+  };
+  // K and V rows of tile X's 8 keys of this wave (2 IPW loads per lane); needs
+  // s_slot[X % 3][wave] complete
+  auto issue_kv = [&](int X) {
+    const int st = X % ANST;
+    uint8_t* kb = s_kv + st * Gm::STAGE;
+    uint32_t bad = 0;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
-      for (int e = 0; e < 4; e++) {
-        sVt[(part * 8 + 2 * e) * LDV_ + col] = (bf16_t)(w[e] & 0xffffu);
-        sVt[(part * 8 + 2 * e + 1) * LDV_ + col] = (bf16_t)(w[e] >> 16);
+    for (int i = 0; i < IPW; i++) {
+      const int rl = i * RPI + ln / CPR;  // row among the wave's 8
+      const int row = wave * 8 + rl;
+      int slot = s_slot[st][wave][rl];
+      const bool ok = slot >= 0 && slot < a.n_slots;
+      const uint64_t bb = __ballot(!ok);
+#pragma unroll
+      for (int q = 0; q < RPI; q++) bad |= (uint32_t)((bb >> (q * CPR)) & 1u) << (i * RPI + q);
+      slot = ok ? slot : 0;
+      const size_t base = kv_off(slot, h, a.Hkv, HD);
+      const int pos = ln % CPR;
+      const uint32_t dst = (uint32_t)(wave * IPW + i) * 1024u;
+      dma16(a.k_pool + base + ((pos ^ Gm::swz_k(row)) * 8), __builtin_amdgcn_readfirstlane(lds_addr(kb + dst)));
+      dma16(a.v_pool + base + ((pos ^ Gm::swz_v(row)) * 8),
+            __builtin_amdgcn_readfirstlane(lds_addr(kb + TILE + dst)));
+    }
+    if (lane == 0) s_inval[st][wave] = bad;
+  };
+
+  // Issue order keeps vmcnt accounting fixed: ... D(X), S(X+2), D(X+1) are the
+  // last loads outstanding when tile X is waited for.
+  if (nt > 0) {
+    issue_slots(0);
+    if (nt > 1) {
+      issue_slots(1);
+      wait_vmcnt<1>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    issue_kv(0);
+    if (nt > 1) {
+      if (nt > 2) {
+        issue_slots(2);
+        wait_vmcnt<2 * IPW + 1>();
+      } else {
+        wait_vmcnt<2 * IPW>();
       }
+      issue_kv(1);
     }
-    __syncthreads();
-    if (ti + 1 < t_end) {
-      ATTN_GLOAD(j0 + AKT);
-    }
-    const bool need_mask = (j0 + AKT - 1 > pmin) || (j0 < lomax);
+  }
 
-    // S^T[kt][qt]: keys j0 + 32 kt + 8 (r / 4) + 4 g2 + r % 4, query column l32 of tile qt
-    f32x16_t st[2][2];
+  for (int X = 0; X < nt; X++) {
+    if (X + 1 < nt) wait_vmcnt<2 * IPW>();
+    else wait_vmcnt<0>();
+    lds_barrier();  // stage X published; every wave is done with stage X - 1
+    if (X + 3 < nt) issue_slots(X + 3);
+    if (X + 2 < nt) issue_kv(X + 2);
+
+    const int st = X % ANST;
+    const uint8_t* sb = s_kv + st * Gm::STAGE;
+    const int j0 = kbase + X * AKT;
+    uint64_t inval = 0;
+#pragma unroll
+    for (int w = 0; w < AWAVES; w++) inval |= (uint64_t)s_inval[st][w] << (8 * w);
+    const bool need_mask = (j0 + AKT - 1 > pmin) || (j0 < lomax) || inval != 0;
+
 #pragma unroll
     for (int kt = 0; kt < 2; kt++) {
-      st[kt][0] = st[kt][1] = (f32x16_t){};
+      // S^T: keys j0 + 32 kt + 8 (r / 4) + 4 g2 + r % 4, query column l32
+      f32x16_t sacc = (f32x16_t){};
 #pragma unroll
       for (int ks = 0; ks < KS; ks++) {
-        const bf16x8_t kf = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const uint4*>(sK + (kt * 32 + l32) * LDK_ + ks * 16 + g2 * 8));
-        st[kt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[0][ks], st[kt][0], 0, 0, 0);
-        st[kt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[1][ks], st[kt][1], 0, 0, 0);
+        const bf16x8_t kf =
+            __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(sb + kt * 32 * ROWB + koff[ks]));
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc, 0, 0, 0);
       }
-    }
-    // online softmax per query (its 64 scores: 32 in this lane, 32 in lane ^ 32)
-    uint4 pf[2][4];  // [qt][16-key step c]: bf16 B operand of the PV product
+      // softmax over the query's 32 keys of this half: 16 here, 16 in lane ^ 32
+      float sv[16];
 #pragma unroll
-    for (int qt = 0; qt < 2; qt++) {
-      float sv[32];
-#pragma unroll
-      for (int kt = 0; kt < 2; kt++) {
-        const f32x16_t x = st[kt][qt];
-#pragma unroll
-        for (int r = 0; r < 16; r++) sv[kt * 16 + r] = x[r] * a.scale_log2;
-      }
+      for (int r = 0; r < 16; r++) sv[r] = sacc[r];
       if (need_mask) {
 #pragma unroll
-        for (int i = 0; i < 32; i++) {
-          const int key = j0 + (i >> 4) * 32 + 8 * ((i & 15) >> 2) + 4 * g2 + (i & 3);
-          if (key > qpos[qt] || key < qlo[qt]) sv[i] = -INFINITY;
+        for (int r = 0; r < 16; r++) {
+          const int kk = kt * 32 + 8 * (r >> 2) + 4 * g2 + (r & 3);
+          const int key = j0 + kk;
+          if (key > qpos || key < qlo || ((inval >> kk) & 1u)) sv[r] = -INFINITY;
         }
       }
       float mx = sv[0];
 #pragma unroll
-      for (int i = 1; i < 32; i++) mx = fmaxf(mx, sv[i]);
+      for (int r = 1; r < 16; r++) mx = fmaxf(mx, sv[r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mnew = fmaxf(mrow[qt], mx);
-      const bool dead = mnew == -INFINITY;
-      const float corr = dead ? 1.f : exp2f(mrow[qt] - mnew);
-      mrow[qt] = mnew;
-      float ls = 0.f;
-#pragma unroll
-      for (int i = 0; i < 32; i++) {
-        sv[i] = dead ? 0.f : exp2f(sv[i] - mnew);
-        ls += sv[i];
-      }
-      lrow[qt] = lrow[qt] * corr + ls;
-      {
+      const float mxs = mx * a.scale_log2;
+      const bool grow = mxs > moff + 8.f;
+      const float corr = grow ? __builtin_amdgcn_exp2f(moff - mxs) : 1.f;
+      if (grow) moff = mxs;
+      if (__any(grow)) {
         // (a splat-vector product: the scalar form trips a backend crash in this toolchain)
         const f32x16_t cv = {corr, corr, corr, corr, corr, corr, corr, corr,
                              corr, corr, corr, corr, corr, corr, corr, corr};
 #pragma unroll
-        for (int dt = 0; dt < DT; dt++) oacc[dt][qt] = oacc[dt][qt] * cv;
+        for (int dt = 0; dt < DT; dt++) oacc[dt] = oacc[dt] * cv;
       }
-      // k step c covers keys 16 c .. 16 c + 15: tile kt = c / 2, registers r = 8 (c % 2) .. + 7
+      const float sub = moff == -INFINITY ? 0.f : moff;  // all scores -inf so far: p = 0
+      float ls = 0.f;
 #pragma unroll
-      for (int c = 0; c < 4; c++) {
-        const int b = (c >> 1) * 16 + (c & 1) * 8;
-        pf[qt][c] = make_uint4(pack2_bf16(sv[b + 0], sv[b + 1]), pack2_bf16(sv[b + 2], sv[b + 3]),
-                               pack2_bf16(sv[b + 4], sv[b + 5]), pack2_bf16(sv[b + 6], sv[b + 7]));
+      for (int r = 0; r < 16; r++) {
+        sv[r] = __builtin_amdgcn_exp2f(fmaf(sv[r], a.scale_log2, -sub));
+        ls += sv[r];
       }
-    }
-    // O^T[dt][qt] += V^T[dims dt*32 .. +31][keys of step c] P^T
+      lrow = lrow * corr + ls;
+      // k step c = 2 kt + cc covers keys 16 c .. 16 c + 15: registers r = 8 cc .. 8 cc + 7
+      uint4 pf[2];
 #pragma unroll
-    for (int c = 0; c < 4; c++) {
+      for (int cc = 0; cc < 2; cc++)
+        pf[cc] = make_uint4(pack2_bf16(sv[8 * cc + 0], sv[8 * cc + 1]), pack2_bf16(sv[8 * cc + 2], sv[8 * cc + 3]),
+                            pack2_bf16(sv[8 * cc + 4], sv[8 * cc + 5]), pack2_bf16(sv[8 * cc + 6], sv[8 * cc + 7]));
+      // O^T[dt] += V^T[dims 32 dt .. +31][keys of step c] P^T: lane l supplies, for its
+      // dim 32 dt + l % 32, keys 16 c + 4 g2 + 0..3 (u = 0) and 16 c + 8 + 4 g2 + 0..3 (u = 1)
 #pragma unroll
-      for (int dt = 0; dt < DT; dt++) {
-        const bf16x8_t vf = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const uint4*>(sVt + (dt * 32 + l32) * LDV_ + 16 * c + 8 * g2));
-        oacc[dt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, __builtin_bit_cast(bf16x8_t, pf[0][c]),
-                                                               oacc[dt][0], 0, 0, 0);
-        oacc[dt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, __builtin_bit_cast(bf16x8_t, pf[1][c]),
-                                                               oacc[dt][1], 0, 0, 0);
+      for (int cc = 0; cc < 2; cc++) {
+        const int c = 2 * kt + cc;
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++) {
+          const uint2 v0 = lds_read_tr16(sb + (16 * c) * ROWB + voff[dt]);
+          const uint2 v1 = lds_read_tr16(sb + (16 * c + 8) * ROWB + voff[dt]);
+          const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, __builtin_bit_cast(bf16x8_t, pf[cc]), oacc[dt],
+                                                             0, 0, 0);
+        }
       }
     }
   }
-#undef ATTN_GLOAD
+  wait_vmcnt<0>();
 
-  // oacc[dt][qt][r] = O[query l32 of tile qt][dim dt*32 + 8 (r / 4) + 4 g2 + r % 4]
+  // oacc[dt][r] = O[query l32][dim dt*32 + 8 (r / 4) + 4 g2 + r % 4]
+  float l = lrow;
+  l += __shfl_xor(l, 32, 64);
+  if (!qvalid) return;
+  const int m = wave * 32 + l32;
+  const int r = r0 + m / G, hq = h * G + m % G;
+  if (a.n_split == 1) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    bf16_t* op = a.o + ((size_t)r * a.Hq + hq) * HD;
 #pragma unroll
-  for (int qt = 0; qt < 2; qt++) {
-    float l = lrow[qt];
-    l += __shfl_xor(l, 32, 64);
-    if (!qvalid[qt]) continue;
-    const int m = wave * 64 + qt * 32 + l32;
-    const int r = r0 + m / G, hq = h * G + m % G;
-    if (a.n_split == 1) {
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-      bf16_t* op = a.o + ((size_t)r * a.Hq + hq) * HD;
+    for (int dt = 0; dt < DT; dt++)
 #pragma unroll
-      for (int dt = 0; dt < DT; dt++)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; q4++) {
-          const f32x16_t x = oacc[dt][qt];
-          uint2 w;
-          w.x = pack2_bf16(x[q4 * 4 + 0] * inv, x[q4 * 4 + 1] * inv);
-          w.y = pack2_bf16(x[q4 * 4 + 2] * inv, x[q4 * 4 + 3] * inv);
-          *reinterpret_cast<uint2*>(op + dt * 32 + 8 * q4 + 4 * g2) = w;
-        }
-    } else {
-      const size_t row = ((size_t)split * a.T_max + r) * a.Hq + hq;
-      float* op = a.part_o + row * HD;
-#pragma unroll
-      for (int dt = 0; dt < DT; dt++)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; q4++) {
-          const f32x16_t x = oacc[dt][qt];
-          *reinterpret_cast<float4*>(op + dt * 32 + 8 * q4 + 4 * g2) =
-              make_float4(x[q4 * 4 + 0], x[q4 * 4 + 1], x[q4 * 4 + 2], x[q4 * 4 + 3]);
-        }
-      if (g2 == 0) {
-        a.part_ml[row * 2 + 0] = mrow[qt];
-        a.part_ml[row * 2 + 1] = l;
+      for (int q4 = 0; q4 < 4; q4++) {
+        const f32x16_t x = oacc[dt];
+        uint2 w;
+        w.x = pack2_bf16(x[q4 * 4 + 0] * inv, x[q4 * 4 + 1] * inv);
+        w.y = pack2_bf16(x[q4 * 4 + 2] * inv, x[q4 * 4 + 3] * inv);
+        *reinterpret_cast<uint2*>(op + dt * 32 + 8 * q4 + 4 * g2) = w;
       }
+  } else {
+    const size_t row = ((size_t)split * a.T_max + r) * a.Hq + hq;
+    float* op = a.part_o + row * HD;
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; q4++) {
+        const f32x16_t x = oacc[dt];
+        *reinterpret_cast<float4*>(op + dt * 32 + 8 * q4 + 4 * g2) =
+            make_float4(x[q4 * 4 + 0], x[q4 * 4 + 1], x[q4 * 4 + 2], x[q4 * 4 + 3]);
+      }
+    if (g2 == 0) {
+      a.part_ml[row * 2 + 0] = moff;
+      a.part_ml[row * 2 + 1] = l;
     }
   }
 }
@@ -340,7 +423,7 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(int T_max, const int32_t* 
   float m = -INFINITY, l = 0.f;
   for (int j0 = lo; j0 <= g; j0 += 64) {
     const int j = j0 + lane;
-    float s = -INFINITY;
+    float s = -INFINITY;  // past the row's position, or no valid slot: excluded
     int slot = -1;
     if (j <= g) {
       slot = slot_map[j];
@@ -349,14 +432,12 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(int T_max, const int32_t* 
         float dot = 0.f;
         for (int i = 0; i < HD; i++) dot = fmaf(sq[i], kp[i], dot);
         s = dot * scale;
-      } else {
-        s = 0.f;  // unmapped key: zero vector
       }
     }
     const float mx = wave_max(s);
     const float mnew = fmaxf(m, mx);
-    const float corr = expf(m - mnew);
-    const float p = (j <= g) ? expf(s - mnew) : 0.f;
+    const float corr = mnew == -INFINITY ? 1.f : expf(m - mnew);
+    const float p = s == -INFINITY ? 0.f : expf(s - mnew);
     l = l * corr + wave_sum(p);
 #pragma unroll
     for (int dd = 0; dd < DPL; dd++) acc[dd] *= corr;

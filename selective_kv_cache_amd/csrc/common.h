@@ -112,6 +112,50 @@ __device__ __forceinline__ int row_count(const int32_t* n_rows, int T_max) {
   return n < T_max ? n : T_max;
 }
 
+// ---- direct-to-LDS loads (gfx950 global_load_lds_*), issued as inline
+// assembly so that the compiler, which cannot tell which LDS bytes such a load
+// writes, does not drain every outstanding load before each LDS read.  The
+// LDS base must be wave-uniform; completion is tracked with explicit vmcnt
+// waits before the barrier that publishes the data.
+
+// 16 bytes per lane from g, landing at LDS address lds_base + 16 * lane
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_base) : "memory");
+}
+
+// 4 bytes per lane from g, landing at LDS address lds_base + 4 * lane
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_base) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(size_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");  // LDS reads of the loaded data stay after the wait
+}
+
+// workgroup barrier that orders LDS accesses without draining outstanding
+// global (and LDS-DMA) loads, unlike __syncthreads: this wave's LDS reads and
+// writes complete (lgkmcnt 0) before it arrives
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){a, b}, b2_t));
+}
+
 // wave64 reductions
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -98,43 +98,7 @@ constexpr int KB = 32;          // K per stage
 constexpr int NSTAGE = 4;       // LDS ring depth (prefetch distance 3)
 constexpr int GEMM_THREADS = 256;
 
-// One direct-to-LDS load: 16 bytes per lane from `g`, landing at LDS address
-// lds_base + 16 * lane (lds_base must be wave-uniform).  Issued as inline
-// assembly so that the compiler does not drain these loads before every LDS
-// read (it cannot tell the ring stages apart); completion is tracked with
-// explicit vmcnt waits before the barrier that publishes a stage.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_base) : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(size_t)(__attribute__((address_space(3))) const void*)p;
-}
-
-// s_waitcnt with only vmcnt constrained (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// workgroup barrier that orders LDS accesses without draining outstanding
-// global (and LDS-DMA) loads, unlike __syncthreads: this wave's LDS reads and
-// writes complete (lgkmcnt 0) before it arrives
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unconstrained
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8_t, v); }
-
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-  typedef float f2_t __attribute__((ext_vector_type(2)));
-  typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){a, b}, b2_t));
-}
 
 __device__ __forceinline__ void unpack8(const uint4& a, float (&f)[8]) {
   const uint32_t w[4] = {a.x, a.y, a.z, a.w};
@@ -174,7 +138,7 @@ __global__ void __launch_bounds__(256) rmsnorm_rows_kernel(const bf16_t* __restr
     if (g) unpack8(reinterpret_cast<const uint4*>(g)[c], w);
 #pragma unroll
     for (int e = 0; e < 8; e++) f[e] = g ? f[e] * rinv * w[e] : f[e] * rinv;
-    yr[c] = make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7]));
+    yr[c] = make_uint4(pack2_bf16(f[0], f[1]), pack2_bf16(f[2], f[3]), pack2_bf16(f[4], f[5]), pack2_bf16(f[6], f[7]));
   }
 }
 
@@ -405,8 +369,8 @@ gemm_bf16_kernel(GemmArgs<bf16_t> p) {
         const int orow = (MODE == EPI_SCATTER && p.out_rows) ? p.out_rows[m] : m;
         dst = p.out0 + (size_t)orow * p.ldo + n;
       }
-      *reinterpret_cast<uint4*>(dst) = make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]),
-                                                  pack2(v[6], v[7]));
+      *reinterpret_cast<uint4*>(dst) = make_uint4(pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3]), pack2_bf16(v[4], v[5]),
+                                                  pack2_bf16(v[6], v[7]));
     }
     __syncthreads();
   }
