@@ -111,7 +111,7 @@ kvb_status kvb_workspace_size(kvb_ctx* ctx, const kvb_model_desc* desc, int32_t 
  * this context whose kernel name contains `filter` ("" = all) is bracketed with
  * HIP events on its stream; filter == NULL turns timing off.  Kernel names:
  * embed, rmsnorm, gemm_qkv, rope, blend_scatter, attention, attention_merge, gemm_oproj, gemm_swiglu,
- * gemm_down, deviation, topk_sort, topk_rank, topk_compact, refresh_flag,
+ * gemm_down, splitk_reduce, deviation, topk_sort, topk_rank, topk_compact, refresh_flag,
  * refresh_compact, slot_copy, slot_scatter. */
 kvb_status kvb_timing_enable(kvb_ctx* ctx, const char* filter);
 /* Waits for the recorded events and folds them into per-kernel totals, then

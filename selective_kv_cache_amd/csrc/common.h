@@ -62,7 +62,8 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 
 // workspace layouts (bytes), shared by kvb_workspace_size and the entry points
-size_t ws_mlp_bytes(const kvb_model_desc* d, int32_t max_rows);
+size_t ws_mlp_bytes(const kvb_model_desc* d, int32_t max_rows, int n_cu);
+size_t ws_gemm_sk_bytes(int n_cu);
 size_t ws_qkv_bytes(const kvb_model_desc* d, int32_t max_rows);
 size_t ws_topk_bytes(int32_t max_tokens, int32_t max_requests);
 size_t ws_refresh_bytes(int32_t max_tokens, int32_t max_requests);

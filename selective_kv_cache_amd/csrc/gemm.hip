@@ -4,22 +4,21 @@
 //
 //   C[m, n] = sum_k A[row(m), k] * W[n, k]      (W is [N, K], row-major)
 //
-// bf16 path: MFMA v_mfma_f32_32x32x16_bf16 on gfx950, 128x128x64 block tiles,
-// 4 waves of 64x64, LDS double buffering with a register prefetch of the next
-// K tile.  fp32 path: an LDS-tiled FMA kernel with the same prologue and
-// epilogues (used by the small float32 workload).
+// bf16 path: MFMA v_mfma_f32_32x32x16_bf16 on gfx950 (see the bf16 section).
+// fp32 path: an LDS-tiled FMA kernel with the same epilogues (used by the
+// small float32 workload), RMSNorm folded into its A loads.
 //
-// Fusions: RMSNorm of the A rows is folded in (sum of squares accumulated
-// while the tiles stream through, 1/rms applied in the epilogue, gains applied
-// to A before it reaches the matrix cores); epilogues split Q/K/V, add the
-// residual, apply SiLU(gate) * up on a dual-B tile, or scatter rows back to
-// the hidden buffer.
+// Fusions: epilogues split Q/K/V, add the residual, apply SiLU(gate) * up on a
+// dual-B tile, or scatter rows back to the hidden buffer.  For bf16, RMSNorm
+// runs as a row pre-pass (rmsnorm_rows_kernel) whose bf16 output the
+// projection reads.
 //
-// Row invariance: the reduction order of every output element (K tiles in
-// order, the MFMA's k slices in order) and of every row's sum of squares (a
-// fixed thread-to-k-chunk assignment reduced by xor shuffles) depends only on
-// k, never on the row's index or on M, so a row's result is the same whatever
-// batch it is computed in.
+// Row invariance: for the Q/K/V projection the reduction order of every output
+// element (K stages in order, the MFMA's k slices in order) and of every
+// row's sum of squares depends only on k, never on the row's index or on M,
+// so a row's result is the same whatever batch it is computed in.  The MLP
+// products may split K across blocks (stream-K); their results are
+// deterministic for a given batch.
 #include "common.h"
 
 namespace kvb {
@@ -73,30 +72,35 @@ __device__ __forceinline__ void epilogue(const GemmArgs<T>& p, int m, int n, flo
 
 // ====================================================================== bf16 MFMA
 //
-// Block = 4 waves in a 2 x 2 grid; wave tile = (32 TM) x (32 TN) outputs as
-// TM x TN tiles of v_mfma_f32_32x32x16_bf16; block tile BM = 64 TM rows of A
-// and BN = 64 TN rows of B.  K advances 32 at a time through a ring of four
-// LDS stages filled by direct-to-LDS loads (global_load_lds_dwordx4) three
-// stages ahead, so global latency is hidden without staging registers.
+// Block = 8 waves in a WM x WN grid (two waves per SIMD, at most 256 registers
+// each, so one wave's MFMAs run while the other waits on LDS or a barrier);
+// wave tile = (32 TM) x (32 TN) outputs as TM x TN tiles of
+// v_mfma_f32_32x32x16_bf16; block tile BM x BN.  K advances KB (32 or 64) per
+// stage through a ring of NST LDS stages filled by direct-to-LDS loads
+// (global_load_lds_dwordx4 with a scalar base and 32-bit lane offsets).  With
+// three or more stages the next stage is published one step ahead, so the
+// first MFMA fragments of a stage are read while the previous stage computes;
+// inside a stage the fragments of the next k16 step are read while the
+// current step's MFMAs run.
 //
-// LDS stage layout: rows of 64 bytes (32 bf16 = four 16-byte chunks); chunk c
-// of row r is stored at position c ^ ((r >> 2) & 3), which makes the 16-byte
-// fragment reads of 16 consecutive rows hit 16 distinct bank groups.  A wave's
-// load instruction fills 1 KiB = 16 rows; its lane j fetches row j / 4, chunk
-// (j % 4) ^ swizzle(row), and lands at position j % 4.
+// LDS stage layout: rows of 2 KB bytes; the 16-byte chunk c of row r is stored
+// at position c ^ swizzle(r), which makes the fragment reads of 16 consecutive
+// rows hit 16 distinct bank groups.  A wave's load instruction fills 1 KiB =
+// RPI rows; its lane j fetches row j / CPR, chunk (j % CPR) ^ swizzle(row).
 //
 // SwiGLU (DUAL): the B tile interleaves 32-row subtiles of the gate and up
 // matrices (gate cols c..c+31, up cols c..c+31, ...), so a wave holds gate
 // and up of the same outputs in neighbouring accumulators; BN/2 outputs wide.
 //
+// Split-K (SK): when whole tiles would fill the chip unevenly, each tile's K
+// steps are cut into S slices run by S blocks, each writing its float partial
+// [S][rows][cols]; splitk_reduce_kernel then adds the S partials in slice
+// order and applies the epilogue.  The reduction order depends on the launch,
+// so split-K is used only for the MLP products, never for the Q/K/V
+// projection (whose per-row results must not depend on the batch).
+//
 // RMSNorm is not fused here: rmsnorm_rows_kernel writes the normalised rows
 // (bf16, one rounding) to workspace and the GEMM reads them as a plain A.
-// Carrying the row sums and the gains through the K loop cost registers that
-// the 4 x 4 tile does not have.
-
-constexpr int KB = 32;          // K per stage
-constexpr int NSTAGE = 4;       // LDS ring depth (prefetch distance 3)
-constexpr int GEMM_THREADS = 256;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8_t, v); }
 
@@ -151,257 +155,426 @@ static kvb_status rmsnorm_rows(hipStream_t st, const bf16_t* x, const int32_t* a
   return check_launch("rmsnorm_rows_kernel");
 }
 
-template <int TM, int TN>
+constexpr int GEMM_WAVES = 8;
+constexpr int GEMM_THREADS = 64 * GEMM_WAVES;
+
+template <int BM_, int BN_, int WM_, int KB_, int NST_>
 struct Tile {
-  static constexpr int BM = 64 * TM, BN = 64 * TN;
-  static constexpr int A_I = BM / 64, B_I = BN / 64;  // load instructions per wave per stage
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = GEMM_WAVES / WM_, KB = KB_, NST = NST_;
+  static constexpr int TM = BM / WM / 32, TN = BN / WN / 32;  // MFMA tiles per wave
+  static constexpr int ROWB = KB * 2;                          // bytes per tile row per stage
+  static constexpr int CPR = ROWB / 16;                        // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;                         // rows per 1 KiB load instruction
+  static constexpr int A_I = BM / RPI / GEMM_WAVES, B_I = BN / RPI / GEMM_WAVES;  // loads per wave per stage
   static constexpr int PER = A_I + B_I;
-  static constexpr int STAGE_BYTES = (BM + BN) * 64;
-  static constexpr int EPI_BYTES = 32 * (BN + 8) * 4;  // one 32-row epilogue phase
+  static constexpr int STAGE_BYTES = (BM + BN) * ROWB;
+  static constexpr int KS = KB / 16;                           // k16 steps per stage
+  static constexpr int EPI_BYTES = 32 * (BN + 8) * 4;          // one 32-row epilogue phase
   static constexpr int ARR = STAGE_BYTES > EPI_BYTES ? STAGE_BYTES : EPI_BYTES;
+  static constexpr int NACC = TM * TN * 16;                    // accumulator floats per lane
+  static_assert(TM >= 1 && TN >= 1 && A_I >= 1 && B_I >= 1 && NST >= 2, "tile shape");
+  __device__ __forceinline__ static int swz(int r) { return KB == 32 ? ((r >> 2) & 3) : ((r >> 1) & 7); }
 };
 
-// The four ring stages are separate LDS objects and the K loop is unrolled by
-// four, so the compiler can see that a stage being read is not the one the
-// in-flight loads are filling (one shared object would make it drain every
-// outstanding load before each LDS read).
-template <int TM, int TN, int S>
+// The ring stages are separate LDS objects and the K loop is unrolled by NST,
+// so every stage address is a compile-time constant.
+template <class TL, int S>
 struct StageLds {
   __device__ static uint8_t* ptr() {
-    __shared__ __align__(16) uint8_t buf[Tile<TM, TN>::ARR];
+    __shared__ __align__(16) uint8_t buf[TL::ARR];
     return buf;
   }
 };
 
-template <int MODE, bool DUAL, int TM, int TN>
-__global__ void __launch_bounds__(GEMM_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
-gemm_bf16_kernel(GemmArgs<bf16_t> p) {
-  using TL = Tile<TM, TN>;
-  constexpr int BM = TL::BM, BN = TL::BN, A_I = TL::A_I, B_I = TL::B_I, PER = TL::PER;
-  constexpr int OUT_N = DUAL ? BN / 2 : BN;  // output columns per block
-  uint8_t* const stg[NSTAGE] = {StageLds<TM, TN, 0>::ptr(), StageLds<TM, TN, 1>::ptr(), StageLds<TM, TN, 2>::ptr(),
-                                StageLds<TM, TN, 3>::ptr()};
+// 16 bytes per lane from base + off (scalar base, 32-bit lane byte offset),
+// landing at LDS address lds_base + 16 * lane
+__device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds_base) : "memory");
+}
 
-  const int M = row_count(p.n_rows, p.M_max);
-  // Tile rasterisation.  Workgroups go to the 8 XCDs round-robin (id % 8), each
-  // XCD with its own L2: give every XCD a contiguous run of a grouped tile
-  // order (GM m-tiles sweeping all n-tiles), so the tiles an XCD runs at the
-  // same time share A and B panels in its L2.
-  int tm, tn;
-  {
-    const int num_m = cdiv_dev(p.M_max, BM), num_n = cdiv_dev(p.N, OUT_N);
-    const int total = num_m * num_n;
-    const int per = (total + 7) >> 3;
-    const int tid = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
-    if (tid >= total) return;
-    const int GM = num_m <= 16 ? num_m : 8;
-    const int gsize = GM * num_n;
-    const int grp = tid / gsize, first = grp * GM;
-    const int gm = min(GM, num_m - first);
-    const int in = tid - grp * gsize;
-    tm = first + in % gm;
-    tn = in / gm;
-  }
-  const int m0 = tm * BM, n0 = tn * OUT_N;
-  if (m0 >= M) return;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wm = (wave >> 1) * (32 * TM), wn = (wave & 1) * (32 * TN);
-
-  // ---- direct-to-LDS loaders: instruction i of this wave covers tile rows
-  //      (wave * X_I + i) * 16 + lane / 4, lane position lane % 4
-  const int lrow = lane >> 2, lpos = lane & 3;
-  const bf16_t* a_src[A_I];
-  const bf16_t* b_src[B_I];
-#pragma unroll
-  for (int i = 0; i < A_I; i++) {
-    const int r = (wave * A_I + i) * 16 + lrow;
-    int m = m0 + r;
-    m = m < M ? m : M - 1;
-    const int ar = p.a_rows ? p.a_rows[m] : m;
-    a_src[i] = p.A + (size_t)ar * p.K + ((lpos ^ ((r >> 2) & 3)) * 8);
-  }
-#pragma unroll
-  for (int i = 0; i < B_I; i++) {
-    const int r = (wave * B_I + i) * 16 + lrow;  // B-tile row; 32-row subtile r / 32
-    const bf16_t* base = p.B;
-    int n;
-    if (DUAL) {
-      base = ((r >> 5) & 1) ? p.B2 : p.B;
-      n = n0 + (r >> 6) * 32 + (r & 31);
-    } else {
-      n = n0 + r;
-    }
-    n = n < p.N ? n : p.N - 1;
-    b_src[i] = base + (size_t)n * p.K + ((lpos ^ ((r >> 2) & 3)) * 8);
-  }
-  const int KT = p.K / KB;
-#define KVB_ISSUE(KT_, ST_)                                                                       \
-  do {                                                                                            \
-    uint8_t* st_ = (ST_);                                                                         \
-    const int ko_ = (KT_) * KB;                                                                   \
-    _Pragma("unroll") for (int i = 0; i < A_I; i++)                                               \
-      dma16(a_src[i] + ko_, __builtin_amdgcn_readfirstlane(lds_addr(st_ + (wave * A_I + i) * 1024))); \
-    _Pragma("unroll") for (int i = 0; i < B_I; i++)                                               \
-      dma16(b_src[i] + ko_, __builtin_amdgcn_readfirstlane(lds_addr(st_ + BM * 64 + (wave * B_I + i) * 1024))); \
-  } while (0)
-
-  f32x16_t acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; i++)
-#pragma unroll
-    for (int j = 0; j < TN; j++) acc[i][j] = (f32x16_t){};
-
-  // fragment addressing: lane reads row (l % 32) of a 32-row subtile, chunk 2 s + l / 32
-  const int fr = lane & 31, fh = lane >> 5, fswz = (fr >> 2) & 3;
-  const int foff0 = fr * 64 + (((0 + fh) ^ fswz) * 16);  // k16 step 0
-  const int foff1 = fr * 64 + (((2 + fh) ^ fswz) * 16);  // k16 step 1
-
-  // Fragments are double-buffered in registers: while the MFMAs of one k16
-  // step run, the reads of the next step (in the same stage, or step 0 of the
-  // next stage) are in flight.  Stage kt+1 is therefore published (vmcnt wait
-  // + barrier) at the start of step kt, and the ring is refilled three stages
-  // ahead into the stage consumed in the previous step.
-  uint4 fa[2][TM], fb[2][TN];
-#define KVB_FRAGS(BUF, STG, FO)                                                                   \
-  do {                                                                                            \
-    const uint8_t* sa_ = (STG) + wm * 64 + (FO);                                                  \
-    const uint8_t* sb_ = (STG) + BM * 64 + wn * 64 + (FO);                                        \
-    _Pragma("unroll") for (int i = 0; i < TM; i++) fa[BUF][i] = *reinterpret_cast<const uint4*>(sa_ + i * 2048); \
-    _Pragma("unroll") for (int j = 0; j < TN; j++) fb[BUF][j] = *reinterpret_cast<const uint4*>(sb_ + j * 2048); \
-  } while (0)
-#define KVB_MMA(BUF)                                                                              \
-  do {                                                                                            \
-    _Pragma("unroll") for (int i = 0; i < TM; i++)                                                \
-      _Pragma("unroll") for (int j = 0; j < TN; j++)                                              \
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[BUF][i]), as_bf16x8(fb[BUF][j]), acc[i][j], 0, 0, 0); \
-  } while (0)
-  // one K step on ring stage S (compile-time), with stage S+1 published on entry
-#define KVB_STEP(S, KT_)                                                                          \
-  do {                                                                                            \
-    const int kt_ = (KT_);                                                                        \
-    if (kt_ + 2 < KT) wait_vmcnt<PER>();                                                          \
-    else wait_vmcnt<0>();                                                                         \
-    lds_barrier();                                                                                \
-    if (kt_ + 3 < KT) KVB_ISSUE(kt_ + 3, stg[((S) + 3) & 3]);                                     \
-    KVB_FRAGS(1, stg[S], foff1);                                                                  \
-    KVB_MMA(0);                                                                                   \
-    if (kt_ + 1 < KT) KVB_FRAGS(0, stg[((S) + 1) & 3], foff0);                                    \
-    KVB_MMA(1);                                                                                   \
-  } while (0)
-
-  if (KT > 0) KVB_ISSUE(0, stg[0]);
-  if (KT > 1) KVB_ISSUE(1, stg[1]);
-  if (KT > 2) KVB_ISSUE(2, stg[2]);
-  // publish stage 0, read its step-0 fragments
-  if (KT > 2) wait_vmcnt<2 * PER>();
-  else if (KT > 1) wait_vmcnt<PER>();
-  else wait_vmcnt<0>();
-  lds_barrier();
-  if (KT > 0) KVB_FRAGS(0, stg[0], foff0);
-  int kt = 0;
-  for (; kt + 4 <= KT; kt += 4) {
-    KVB_STEP(0, kt);
-    KVB_STEP(1, kt + 1);
-    KVB_STEP(2, kt + 2);
-    KVB_STEP(3, kt + 3);
-  }
-  if (kt < KT) KVB_STEP(0, kt);
-  if (kt + 1 < KT) KVB_STEP(1, kt + 1);
-  if (kt + 2 < KT) KVB_STEP(2, kt + 2);
-#undef KVB_STEP
-#undef KVB_MMA
-#undef KVB_FRAGS
-#undef KVB_ISSUE
-  wait_vmcnt<0>();
-  lds_barrier();  // every wave is done with the ring before the epilogue reuses LDS
-
-  // Epilogue, staged through LDS in 2 TM phases of 32 rows: the two waves
-  // owning a phase's rows (subtile i of their half) write their float
-  // accumulators (SwiGLU already combined) to a [32][OUT_N] tile, then all
-  // threads read 8 consecutive outputs of a row, apply the mode (scale,
-  // residual, scatter) and store 16 bytes at a time.
-  // acc[i][j][r] sits at tile row wm + 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4,
-  // tile col wn + 32 j + lane % 32 (DUAL: output col (wn / 32 + j) / 2 * 32 + lane % 32).
-  constexpr int LDC = OUT_N + 8;  // floats; rows 4 apart land 32 banks apart
-  float* sC = reinterpret_cast<float*>(stg[0]);
-  const int lc = lane & 31;
-#pragma unroll
-  for (int ph = 0; ph < 2 * TM; ph++) {
-    const int i = ph % TM;
-    if ((wave >> 1) == ph / TM) {
-#pragma unroll
-      for (int j = 0; j < TN; j += (DUAL ? 2 : 1)) {
-        const int cl = DUAL ? ((wn / 32 + j) >> 1) * 32 + lc : wn + j * 32 + lc;
-#pragma unroll
-        for (int r = 0; r < 16; r++) {
-          const int rl = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);  // row inside the phase
-          float v = acc[i][j][r];
-          if (DUAL) v = silu(v) * acc[i][j + 1][r];
-          sC[rl * LDC + cl] = v;
-        }
-      }
-    }
-    __syncthreads();
-    constexpr int CPR = OUT_N / 8;  // 8-output chunks per row
-    for (int c = t; c < 32 * CPR; c += GEMM_THREADS) {
-      const int rl = c / CPR, cc = (c % CPR) * 8;
-      const int ml = ph * 32 + rl, m = m0 + ml, n = n0 + cc;
-      if (m >= M || n >= p.N) continue;
-      const float4 lo = *reinterpret_cast<const float4*>(sC + rl * LDC + cc);
-      const float4 hi = *reinterpret_cast<const float4*>(sC + rl * LDC + cc + 4);
-      float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      bf16_t* dst;
-      if (MODE == EPI_QKV) {
-        if (n < p.n0) dst = p.out0 + (size_t)m * p.n0 + n;
-        else if (n < p.n1) dst = p.out1 + (size_t)m * (p.n1 - p.n0) + (n - p.n0);
-        else dst = p.out2 + (size_t)m * (p.N - p.n1) + (n - p.n1);
-      } else if (MODE == EPI_SWIGLU) {
-        dst = p.out0 + (size_t)m * p.ldo + n;
-      } else {
-        const int rr = (MODE == EPI_RESID && p.resid_rows) ? p.resid_rows[m] : m;
-        const uint4 h = *reinterpret_cast<const uint4*>(p.resid + (size_t)rr * p.ldr + n);
-        const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          v[2 * e] += __uint_as_float(hw[e] << 16);
-          v[2 * e + 1] += __uint_as_float(hw[e] & 0xffff0000u);
-        }
-        const int orow = (MODE == EPI_SCATTER && p.out_rows) ? p.out_rows[m] : m;
-        dst = p.out0 + (size_t)orow * p.ldo + n;
-      }
-      *reinterpret_cast<uint4*>(dst) = make_uint4(pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3]), pack2_bf16(v[4], v[5]),
-                                                  pack2_bf16(v[6], v[7]));
-    }
-    __syncthreads();
+// wait until at most `allowed` (a multiple of the per-stage load count, <= N)
+// direct-to-LDS loads are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm_upto(int allowed) {
+  if constexpr (N <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (allowed >= N) wait_vmcnt<N>();
+    else wait_vm_upto<N - 1>(allowed);
   }
 }
 
-template <int MODE, bool DUAL, int TM, int TN>
-static kvb_status launch_bf16(hipStream_t st, const GemmArgs<bf16_t>& p, const char* name) {
-  using TL = Tile<TM, TN>;
+// split-K schedule of one launch
+struct SkArgs {
+  int S;           // K slices per tile (1: no split)
+  int rows;        // row stride of a slice: M_max rounded up to the tile height
+  int cols;        // N (DUAL: 2 N, gate columns then up columns)
+  float* part;     // [S][rows][cols]
+};
+
+// grouped tile order: GM m-tiles sweep all n-tiles, so concurrent tiles share panels
+__device__ __forceinline__ void tile_coords(int t, int num_m, int num_n, int& tm, int& tn) {
+  const int GM = num_m <= 16 ? num_m : 8;
+  const int gsize = GM * num_n;
+  const int grp = t / gsize, first = grp * GM;
+  const int gm = min(GM, num_m - first);
+  const int in = t - grp * gsize;
+  tm = first + in % gm;
+  tn = in / gm;
+}
+
+template <int MODE, bool DUAL, class TL, bool SK>
+__global__ void __launch_bounds__(GEMM_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+gemm_bf16_kernel(GemmArgs<bf16_t> p, SkArgs sk) {
+  constexpr int BM = TL::BM, BN = TL::BN, WN = TL::WN, TM = TL::TM, TN = TL::TN, KB = TL::KB, NST = TL::NST;
+  constexpr int A_I = TL::A_I, B_I = TL::B_I, PER = TL::PER, ROWB = TL::ROWB, CPR = TL::CPR, RPI = TL::RPI;
+  constexpr int KS = TL::KS;
+  constexpr int OUT_N = DUAL ? BN / 2 : BN;  // output columns per block
+  constexpr bool PA = NST >= 3;              // publish the next stage one step ahead
+  static_assert(!DUAL || TN % 2 == 0, "SwiGLU pairs gate and up subtiles inside a wave");
+  uint8_t* const stg[4] = {StageLds<TL, 0>::ptr(), StageLds<TL, 1>::ptr(),
+                           NST > 2 ? StageLds<TL, 2>::ptr() : nullptr, NST > 3 ? StageLds<TL, 3>::ptr() : nullptr};
+
+  const int M = row_count(p.n_rows, p.M_max);
+  const int num_m = cdiv_dev(p.M_max, BM), num_n = cdiv_dev(p.N, OUT_N);
+  const int tiles = num_m * num_n;
+  const int KT = p.K / KB;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = (wave / WN) * (32 * TM), wn = (wave % WN) * (32 * TN);
+  const int lrow = lane / CPR, lpos = lane % CPR;
+  const int fr = lane & 31, fh = lane >> 5, fs = TL::swz(fr);
+  const bf16_t* const Bup = DUAL ? p.B2 : p.B;
+
+  // this block's work: K slice `split` of one tile.  Workgroups go to the 8
+  // XCDs round-robin (id % 8), each XCD with its own L2: give every XCD a
+  // contiguous run of the (tile, slice) order.
+  const int S = SK ? sk.S : 1;
+  const int total = tiles * S;
+  const int per = (total + 7) >> 3;
+  const int tid = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+  if (tid >= total) return;
+  const int tile = tid / S, split = tid - tile * S;
+  const int kbeg = split * KT / S, kend = (split + 1) * KT / S;
+  {
+    f32x16_t acc[TM][TN];
+    uint4 fa[2][TM], fb[2][TN];
+    int tm, tn;
+    tile_coords(tile, num_m, num_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * OUT_N;
+    // rows past the device row count: nothing to compute or store (every slice
+    // of such a tile leaves here, so its counter is never touched)
+    if (m0 >= M) return;
+    const int KTL = kend - kbeg;
+
+    // ---- direct-to-LDS loaders: instruction i of this wave covers tile rows
+    //      (wave * X_I + i) * RPI + lane / CPR, lane position lane % CPR
+    uint32_t a_off[A_I], b_off[B_I];
+#pragma unroll
+    for (int i = 0; i < A_I; i++) {
+      const int r = (wave * A_I + i) * RPI + lrow;
+      int m = m0 + r;
+      m = m < M ? m : M - 1;
+      m = m < 0 ? 0 : m;
+      const int ar = p.a_rows ? p.a_rows[m] : m;
+      a_off[i] = (uint32_t)(((size_t)ar * p.K + (size_t)((lpos ^ TL::swz(r)) * 8)) * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < B_I; i++) {
+      const int r = (wave * B_I + i) * RPI + lrow;  // B-tile row; 32-row subtile r / 32
+      int n;
+      size_t base = 0;
+      if (DUAL) {
+        n = n0 + (r >> 6) * 32 + (r & 31);
+        if ((r >> 5) & 1) base = (size_t)(Bup - p.B);
+      } else {
+        n = n0 + r;
+      }
+      n = n < p.N ? n : p.N - 1;
+      b_off[i] = (uint32_t)((base + (size_t)n * p.K + (size_t)((lpos ^ TL::swz(r)) * 8)) * 2);
+    }
+    auto issue = [&](int j, uint8_t* st) {
+      const size_t ko = (size_t)(kbeg + j) * KB;
+      const bf16_t* ab = p.A + ko;
+      const bf16_t* bb = p.B + ko;
+#pragma unroll
+      for (int i = 0; i < A_I; i++)
+        dma16s(ab, a_off[i], __builtin_amdgcn_readfirstlane(lds_addr(st + (wave * A_I + i) * 1024)));
+#pragma unroll
+      for (int i = 0; i < B_I; i++)
+        dma16s(bb, b_off[i], __builtin_amdgcn_readfirstlane(lds_addr(st + BM * ROWB + (wave * B_I + i) * 1024)));
+    };
+    auto frags = [&](int buf, const uint8_t* st, int s) {
+      const int off = fr * ROWB + (((2 * s + fh) ^ fs) * 16);
+#pragma unroll
+      for (int i = 0; i < TM; i++) fa[buf][i] = *reinterpret_cast<const uint4*>(st + (wm + 32 * i) * ROWB + off);
+#pragma unroll
+      for (int j = 0; j < TN; j++)
+        fb[buf][j] = *reinterpret_cast<const uint4*>(st + BM * ROWB + (wn + 32 * j) * ROWB + off);
+    };
+    auto mma = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[buf][i]), as_bf16x8(fb[buf][j]), acc[i][j],
+                                                              0, 0, 0);
+    };
+
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+      for (int j = 0; j < TN; j++) acc[i][j] = (f32x16_t){};
+
+    // ---- K loop over [kbeg, kend)
+#pragma unroll
+    for (int j = 0; j < NST - 1; j++)
+      if (j < KTL) issue(j, stg[j]);
+    if constexpr (PA) {
+      if (KTL > 0) {
+        wait_vm_upto<(NST - 2) * PER>(min(KTL - 1, NST - 2) * PER);
+        lds_barrier();
+        frags(0, stg[0], 0);
+      }
+    }
+    for (int kt0 = 0; kt0 < KTL; kt0 += NST) {
+#pragma unroll
+      for (int S = 0; S < NST; S++) {
+        const int kt = kt0 + S;
+        if (kt < KTL) {
+          if constexpr (PA) wait_vm_upto<(NST - 3) * PER>(max(0, min(KTL - 2 - kt, NST - 3)) * PER);
+          else wait_vmcnt<0>();
+          lds_barrier();  // stage kt (PA: kt + 1) published; every wave is done with the stage refilled next
+          if (kt + NST - 1 < KTL) issue(kt + NST - 1, stg[(S + NST - 1) % NST]);
+          if constexpr (!PA) frags(0, stg[S], 0);
+#pragma unroll
+          for (int s = 0; s < KS; s++) {
+            if (s + 1 < KS) frags((s + 1) & 1, stg[S], s + 1);
+            else if (PA && kt + 1 < KTL) frags((s + 1) & 1, stg[(S + 1) % NST], 0);
+            mma(s & 1);
+          }
+        }
+      }
+    }
+    wait_vmcnt<0>();
+    lds_barrier();  // every wave is done with the ring before the epilogue reuses LDS
+
+    // ---- split-K: write this slice's partial (row-major, the reduction kernel
+    // applies the epilogue)
+    if constexpr (SK) {
+      float* dst = sk.part + (size_t)split * sk.rows * sk.cols;
+#pragma unroll
+      for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++) {
+          // DUAL: subtile j even holds gate, odd holds up, of output cols (wn / 32 + j) / 2 * 32
+          const int col = DUAL ? ((j & 1) ? p.N : 0) + n0 + ((wn / 32 + j) >> 1) * 32 + (lane & 31)
+                               : n0 + wn + 32 * j + (lane & 31);
+#pragma unroll
+          for (int r = 0; r < 16; r++) {
+            const int row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            if (row < M && (DUAL ? ((j & 1) ? col - p.N : col) : col) < p.N)
+              dst[(size_t)row * sk.cols + col] = acc[i][j][r];
+          }
+        }
+      return;
+    }
+
+    // ---- epilogue, staged through LDS in BM / 32 phases of 32 rows: the waves
+    // owning a phase's rows (subtile i of their wave row) write their float
+    // accumulators (SwiGLU already combined) to a [32][OUT_N] tile, then all
+    // threads read 8 consecutive outputs of a row, apply the mode (residual,
+    // scatter) and store 16 bytes at a time.
+    // acc[i][j][r] sits at tile row wm + 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4,
+    // tile col wn + 32 j + lane % 32 (DUAL: output col (wn / 32 + j) / 2 * 32 + lane % 32).
+    constexpr int LDC = OUT_N + 8;  // floats; rows 4 apart land 32 banks apart
+    float* sC = reinterpret_cast<float*>(stg[0]);
+    const int lc = lane & 31;
+#pragma unroll
+    for (int ph = 0; ph < BM / 32; ph++) {
+      const int i = ph % TM;
+      if (wave / WN == ph / TM) {
+#pragma unroll
+        for (int j = 0; j < TN; j += (DUAL ? 2 : 1)) {
+          const int cl = DUAL ? ((wn / 32 + j) >> 1) * 32 + lc : wn + j * 32 + lc;
+#pragma unroll
+          for (int r = 0; r < 16; r++) {
+            const int rl = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);  // row inside the phase
+            float v = acc[i][j][r];
+            if (DUAL) v = silu(v) * acc[i][j + 1][r];
+            sC[rl * LDC + cl] = v;
+          }
+        }
+      }
+      __syncthreads();
+      constexpr int CPRO = OUT_N / 8;  // 8-output chunks per row
+      for (int c = t; c < 32 * CPRO; c += GEMM_THREADS) {
+        const int rl = c / CPRO, cc = (c % CPRO) * 8;
+        const int ml = ph * 32 + rl, m = m0 + ml, n = n0 + cc;
+        if (m >= M || n >= p.N) continue;
+        const float4 lo = *reinterpret_cast<const float4*>(sC + rl * LDC + cc);
+        const float4 hi = *reinterpret_cast<const float4*>(sC + rl * LDC + cc + 4);
+        float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        bf16_t* dst;
+        if (MODE == EPI_QKV) {
+          if (n < p.n0) dst = p.out0 + (size_t)m * p.n0 + n;
+          else if (n < p.n1) dst = p.out1 + (size_t)m * (p.n1 - p.n0) + (n - p.n0);
+          else dst = p.out2 + (size_t)m * (p.N - p.n1) + (n - p.n1);
+        } else if (MODE == EPI_SWIGLU) {
+          dst = p.out0 + (size_t)m * p.ldo + n;
+        } else {
+          const int rr = (MODE == EPI_RESID && p.resid_rows) ? p.resid_rows[m] : m;
+          const uint4 h = *reinterpret_cast<const uint4*>(p.resid + (size_t)rr * p.ldr + n);
+          const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            v[2 * e] += __uint_as_float(hw[e] << 16);
+            v[2 * e + 1] += __uint_as_float(hw[e] & 0xffff0000u);
+          }
+          const int orow = (MODE == EPI_SCATTER && p.out_rows) ? p.out_rows[m] : m;
+          dst = p.out0 + (size_t)orow * p.ldo + n;
+        }
+        *reinterpret_cast<uint4*>(dst) = make_uint4(pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3]),
+                                                    pack2_bf16(v[4], v[5]), pack2_bf16(v[6], v[7]));
+      }
+      __syncthreads();
+    }
+  }
+}
+
+template <int MODE, bool DUAL, class TL, bool SK>
+static kvb_status launch_bf16(hipStream_t st, const GemmArgs<bf16_t>& p, const SkArgs& sk, const char* name) {
   constexpr int OUT_N = DUAL ? TL::BN / 2 : TL::BN;
-  const int total = cdiv(p.M_max, TL::BM) * cdiv(p.N, OUT_N);
+  const int total = cdiv(p.M_max, TL::BM) * cdiv(p.N, OUT_N) * (SK ? sk.S : 1);
   dim3 grid(((total + 7) / 8) * 8);
   {
     LaunchTimer lt(st, name);
-    gemm_bf16_kernel<MODE, DUAL, TM, TN><<<grid, GEMM_THREADS, 0, st>>>(p);
+    gemm_bf16_kernel<MODE, DUAL, TL, SK><<<grid, GEMM_THREADS, 0, st>>>(p, sk);
   }
   return check_launch("gemm_bf16_kernel");
 }
 
-// Tile choice: the per-element reduction order (32-wide K stages, 16-wide MFMA
-// slices in order) is the same for every tile shape, so picking the shape from
-// the launch bound keeps every row's result independent of the batch.
+// Sum of the S split-K partials in slice order, then the epilogue of MODE;
+// one thread per 8 consecutive output columns of a row.
 template <int MODE, bool DUAL>
-static kvb_status run_bf16(hipStream_t st, const GemmArgs<bf16_t>& p, const char* name) {
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmArgs<bf16_t> p, SkArgs sk) {
+  const int M = row_count(p.n_rows, p.M_max);
+  const int cpr = p.N / 8;
+  const long c = (long)blockIdx.x * 256 + threadIdx.x;
+  const int m = (int)(c / cpr), n = (int)(c % cpr) * 8;
+  if (m >= M) return;
+  float v[8] = {}, u[8] = {};
+  for (int s = 0; s < sk.S; s++) {
+    const float* src = sk.part + ((size_t)s * sk.rows + m) * sk.cols + n;
+    const float4 a = *reinterpret_cast<const float4*>(src), b = *reinterpret_cast<const float4*>(src + 4);
+    v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w; v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
+    if (DUAL) {
+      const float4 g = *reinterpret_cast<const float4*>(src + p.N), h = *reinterpret_cast<const float4*>(src + p.N + 4);
+      u[0] += g.x; u[1] += g.y; u[2] += g.z; u[3] += g.w; u[4] += h.x; u[5] += h.y; u[6] += h.z; u[7] += h.w;
+    }
+  }
+  bf16_t* dst;
+  if (MODE == EPI_SWIGLU) {
+#pragma unroll
+    for (int e = 0; e < 8; e++) v[e] = DUAL ? silu(v[e]) * u[e] : v[e];
+    dst = p.out0 + (size_t)m * p.ldo + n;
+  } else if (MODE == EPI_QKV) {
+    if (n < p.n0) dst = p.out0 + (size_t)m * p.n0 + n;
+    else if (n < p.n1) dst = p.out1 + (size_t)m * (p.n1 - p.n0) + (n - p.n0);
+    else dst = p.out2 + (size_t)m * (p.N - p.n1) + (n - p.n1);
+  } else {
+    const int rr = (MODE == EPI_RESID && p.resid_rows) ? p.resid_rows[m] : m;
+    const uint4 h = *reinterpret_cast<const uint4*>(p.resid + (size_t)rr * p.ldr + n);
+    const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      v[2 * e] += __uint_as_float(hw[e] << 16);
+      v[2 * e + 1] += __uint_as_float(hw[e] & 0xffff0000u);
+    }
+    const int orow = (MODE == EPI_SCATTER && p.out_rows) ? p.out_rows[m] : m;
+    dst = p.out0 + (size_t)orow * p.ldo + n;
+  }
+  *reinterpret_cast<uint4*>(dst) =
+      make_uint4(pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3]), pack2_bf16(v[4], v[5]), pack2_bf16(v[6], v[7]));
+}
+
+template <int MODE, bool DUAL>
+static kvb_status launch_splitk_reduce(hipStream_t st, const GemmArgs<bf16_t>& p, const SkArgs& sk,
+                                       const char* name) {
+  const long n = (long)p.M_max * (p.N / 8);
+  {
+    LaunchTimer lt(st, name);
+    splitk_reduce_kernel<MODE, DUAL><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(p, sk);
+  }
+  return check_launch("splitk_reduce_kernel");
+}
+
+using TileL = Tile<256, 256, 2, 64, 2>;     // waves 128 x 64, 2 stages of K 64
+using TileL192 = Tile<192, 256, 2, 64, 2>;  // waves 96 x 64
+using TileM = Tile<256, 128, 4, 32, 4>;  // waves 64 x 64, 4 stages of K 32
+using TileS = Tile<128, 128, 4, 32, 4>;  // waves 32 x 64, 4 stages of K 32
+
+// split-K partials: float [S][rows][cols], at most this many bytes
+constexpr size_t SK_BUDGET = (size_t)256 << 20;
+size_t ws_gemm_sk_bytes(int) { return SK_BUDGET; }
+
+// Launch choice.  Without split-K the per-element reduction order (K stages in
+// order, 16-wide MFMA slices in order) is the same for every tile shape and
+// stage depth, so picking the shape from the launch bound keeps every row's
+// result independent of the batch.  `sk_ws` (SK_BUDGET bytes) allows split-K.
+//
+// Cost model (microseconds): a tile of BM x BN takes 2 BM BN K / (4.5 TFLOP/s
+// x shape efficiency) on one CU; whole waves of tiles (or slices) run on the
+// CUs; split-K adds the partials' round trip at ~5 TB/s and the reduction
+// launch.
+template <int MODE, bool DUAL>
+static kvb_status run_bf16(hipStream_t st, const GemmArgs<bf16_t>& p, const char* name, void* sk_ws = nullptr) {
   if (p.M_max == 0 || p.N == 0) return KVB_OK;
-  const Ctx* c = current_ctx();
+  // the loads address A and B with 32-bit byte offsets from their bases
+  const size_t b_span = (DUAL ? (size_t)(p.B2 - p.B) + (size_t)p.N * p.K : (size_t)p.N * p.K) * 2;
+  if (p.a_rows || (size_t)p.M_max * p.K * 2 > 0xffffffffu || b_span > 0xffffffffu)
+    return fail(KVB_ERR_UNSUPPORTED, std::string(name) + ": operands beyond 4 GiB of one base");
+  Ctx* c = current_ctx();
   const long cus = c ? c->n_cu : 256;
-  const long big_blocks = (long)cdiv(p.M_max, 256) * cdiv(p.N, DUAL ? 128 : 256);
-  if (big_blocks >= cus) return launch_bf16<MODE, DUAL, 4, 4>(st, p, name);
-  const long mid_blocks = (long)cdiv(p.M_max, 256) * cdiv(p.N, DUAL ? 64 : 128);
-  if (mid_blocks >= cus) return launch_bf16<MODE, DUAL, 4, 2>(st, p, name);
-  return launch_bf16<MODE, DUAL, 2, 2>(st, p, name);
+  struct Shape { int bm, bn, kb; double eff; };
+  const Shape shapes[4] = {{256, 256, 64, 1.0}, {192, 256, 64, 0.95}, {256, 128, 32, 0.85}, {128, 128, 32, 0.65}};
+  int best_shape = -1, best_s = 1;
+  double best_t = 1e30;
+  for (int si = 0; si < 4; si++) {
+    const Shape& sh = shapes[si];
+    if (p.K % sh.kb) continue;
+    const long tiles = (long)cdiv(p.M_max, sh.bm) * cdiv(p.N, DUAL ? sh.bn / 2 : sh.bn);
+    const double tile_us = 2.0 * sh.bm * sh.bn * p.K / (4.5e6 * sh.eff);
+    const int max_split = (si == 0 && sk_ws && p.N % 8 == 0) ? 16 : 1;
+    const long rows = (long)cdiv(p.M_max, sh.bm) * sh.bm, cols = DUAL ? 2L * p.N : p.N;
+    for (int S = 1; S <= max_split && S <= p.K / sh.kb; S++) {
+      if (S > 1 && (size_t)S * rows * cols * 4 > SK_BUDGET) break;
+      double tt = (double)((tiles * S + cus - 1) / cus) * tile_us / S;
+      if (S > 1) tt += 2.0 * S * rows * cols * 4 / 5e6 + 4.0;
+      if (tt < best_t * (S > 1 ? 0.92 : 1.0)) {
+        best_t = tt;
+        best_shape = si;
+        best_s = S;
+      }
+    }
+  }
+  SkArgs sk{};
+  sk.S = 1;
+  if (best_s > 1) {
+    sk.S = best_s;
+    sk.rows = cdiv(p.M_max, TileL::BM) * TileL::BM;
+    sk.cols = DUAL ? 2 * p.N : p.N;
+    sk.part = (float*)sk_ws;
+    KVB_TRY((launch_bf16<MODE, DUAL, TileL, true>(st, p, sk, name)));
+    return launch_splitk_reduce<MODE, DUAL>(st, p, sk, "splitk_reduce");
+  }
+  switch (best_shape) {
+    case 0: return launch_bf16<MODE, DUAL, TileL, false>(st, p, sk, name);
+    case 1: return launch_bf16<MODE, DUAL, TileL192, false>(st, p, sk, name);
+    case 2: return launch_bf16<MODE, DUAL, TileM, false>(st, p, sk, name);
+    case 3: return launch_bf16<MODE, DUAL, TileS, false>(st, p, sk, name);
+    default: return fail(KVB_ERR_UNSUPPORTED, std::string(name) + ": K must be a multiple of 32");
+  }
 }
 
 // ====================================================================== fp32 FMA
@@ -545,6 +718,7 @@ static kvb_status mlp_impl(hipStream_t st, const kvb_model_desc* d, int T_max, c
   T* h1 = (T*)ws;
   T* u = (T*)((char*)ws + h1_bytes);
   T* hn = (T*)((char*)ws + h1_bytes + align_up((size_t)T_max * F * sizeof(T), 256));
+  void* sk_ws = (char*)hn + ws_qkv_bytes(d, T_max);  // stream-K partials (bf16)
   // h1 = hidden[row] + o W_o^T
   GemmArgs<T> a{};
   a.A = (const T*)attn_o;
@@ -585,12 +759,12 @@ static kvb_status mlp_impl(hipStream_t st, const kvb_model_desc* d, int T_max, c
   c.ldr = D;
   c.out_rows = row_tok;
   if constexpr (sizeof(T) == 2) {
-    KVB_TRY((run_bf16<EPI_RESID, false>(st, a, "gemm_oproj")));
+    KVB_TRY((run_bf16<EPI_RESID, false>(st, a, "gemm_oproj", sk_ws)));
     KVB_TRY(rmsnorm_rows(st, h1, nullptr, n_rows, T_max, D, (const bf16_t*)norm2_w, d->rms_eps, hn));
     b.A = hn;
     b.norm_w = nullptr;
-    KVB_TRY((run_bf16<EPI_SWIGLU, true>(st, b, "gemm_swiglu")));
-    return run_bf16<EPI_SCATTER, false>(st, c, "gemm_down");
+    KVB_TRY((run_bf16<EPI_SWIGLU, true>(st, b, "gemm_swiglu", sk_ws)));
+    return run_bf16<EPI_SCATTER, false>(st, c, "gemm_down", sk_ws);
   } else {
     KVB_TRY((run_f32<EPI_RESID, false, false>(st, a, "gemm_oproj")));
     KVB_TRY((run_f32<EPI_SWIGLU, true, true>(st, b, "gemm_swiglu")));
@@ -637,7 +811,8 @@ extern "C" kvb_status kvb_mlp(kvb_ctx* ctx, void* stream, const kvb_model_desc* 
   KVB_CHECK_PTR(hidden, "hidden");
   KVB_CHECK_PTR(w_gate_up, "w_gate_up");
   KVB_CHECK_PTR(w_down, "w_down");
-  if (!ws || ws_bytes < ws_mlp_bytes(desc, T_max)) return fail(KVB_ERR_WORKSPACE, "kvb_mlp workspace too small");
+  if (!ws || ws_bytes < ws_mlp_bytes(desc, T_max, reinterpret_cast<Ctx*>(ctx)->n_cu))
+    return fail(KVB_ERR_WORKSPACE, "kvb_mlp workspace too small");
   CtxScope scope(ctx);
   hipStream_t st = (hipStream_t)stream;
   if (desc->dtype == KVB_BF16)

@@ -95,10 +95,12 @@ kvb_status check_desc(const kvb_model_desc* d) {
 
 static size_t esize(const kvb_model_desc* d) { return d->dtype == KVB_BF16 ? 2 : 4; }
 
-size_t ws_mlp_bytes(const kvb_model_desc* d, int32_t max_rows) {
+size_t ws_mlp_bytes(const kvb_model_desc* d, int32_t max_rows, int n_cu) {
   // h1 [T, d] and u [T, F] in storage type; bf16 adds the normalised h1 [T, d]
+  // and the stream-K partials of its products
   return align_up((size_t)max_rows * d->d_model * esize(d), 256) +
-         align_up((size_t)max_rows * d->ffn * esize(d), 256) + ws_qkv_bytes(d, max_rows);
+         align_up((size_t)max_rows * d->ffn * esize(d), 256) + ws_qkv_bytes(d, max_rows) +
+         (d->dtype == KVB_BF16 ? ws_gemm_sk_bytes(n_cu) : 0);
 }
 
 size_t ws_qkv_bytes(const kvb_model_desc* d, int32_t max_rows) {
@@ -219,7 +221,7 @@ kvb_status kvb_workspace_size(kvb_ctx* ctx, const kvb_model_desc* desc, int32_t 
   KVB_TRY(check_desc(desc));
   KVB_CHECK_PTR(bytes, "bytes");
   if (max_rows < 0 || max_tokens < 0 || max_requests < 0) return fail(KVB_ERR_INVALID_ARG, "negative size");
-  size_t b = ws_mlp_bytes(desc, max_rows);
+  size_t b = ws_mlp_bytes(desc, max_rows, reinterpret_cast<Ctx*>(ctx)->n_cu);
   b = std::max(b, ws_qkv_bytes(desc, max_rows));
   b = std::max(b, ws_topk_bytes(max_tokens, max_requests));
   b = std::max(b, ws_refresh_bytes(max_tokens, max_requests));
