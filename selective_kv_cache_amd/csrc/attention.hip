@@ -189,6 +189,9 @@ attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DT; dt++) oacc[dt] = (f32x16_t){};
   float moff = -INFINITY, lrow = 0.f;
+  // the query loads complete here, so the compiler has no load of its own to
+  // wait for inside the loop (such a wait would also drain the K/V ring)
+  wait_vmcnt<0>();
 
   // The per-lane parts of the load addresses are recomputed at every issue from
   // `ln`, which the empty asm makes opaque: hoisted out of the loop they would
@@ -214,17 +217,21 @@ attn_bf16_kernel(AttnArgs a) {
       const int rl = i * RPI + ln / CPR;  // row among the wave's 8
       const int row = wave * 8 + rl;
       int slot = s_slot[st][wave][rl];
-      const bool ok = slot >= 0 && slot < a.n_slots;
+      const bool ok = (unsigned)slot < (unsigned)a.n_slots;
       const uint64_t bb = __ballot(!ok);
+      if (bb) {  // rare: a key without a valid slot
 #pragma unroll
-      for (int q = 0; q < RPI; q++) bad |= (uint32_t)((bb >> (q * CPR)) & 1u) << (i * RPI + q);
+        for (int q = 0; q < RPI; q++) bad |= (uint32_t)((bb >> (q * CPR)) & 1u) << (i * RPI + q);
+      }
       slot = ok ? slot : 0;
-      const size_t base = kv_off(slot, h, a.Hkv, HD);
+      // pool row of (slot, head h): page, head, position in page
+      const uint32_t prow = (uint32_t)(slot >> 4) * (uint32_t)(a.Hkv * 16) + (uint32_t)(h * 16 + (slot & 15));
       const int pos = ln % CPR;
       const uint32_t dst = (uint32_t)(wave * IPW + i) * 1024u;
-      dma16(a.k_pool + base + ((pos ^ Gm::swz_k(row)) * 8), __builtin_amdgcn_readfirstlane(lds_addr(kb + dst)));
-      dma16(a.v_pool + base + ((pos ^ Gm::swz_v(row)) * 8),
-            __builtin_amdgcn_readfirstlane(lds_addr(kb + TILE + dst)));
+      const bf16_t* kp = a.k_pool + (size_t)prow * HD;
+      const bf16_t* vp = a.v_pool + (size_t)prow * HD;
+      dma16(kp + ((pos ^ Gm::swz_k(row)) * 8), __builtin_amdgcn_readfirstlane(lds_addr(kb + dst)));
+      dma16(vp + ((pos ^ Gm::swz_v(row)) * 8), __builtin_amdgcn_readfirstlane(lds_addr(kb + TILE + dst)));
     }
     if (lane == 0) s_inval[st][wave] = bad;
   };
@@ -502,6 +509,8 @@ extern "C" kvb_status kvb_sparse_query_attn(kvb_ctx* ctx, void* stream, const kv
   KVB_CHECK_PTR(slot_map, "slot_map");
   KVB_CHECK_PTR(o, "o");
   if ((long)n_pages * 16 > 0x7fffffffL) return fail(KVB_ERR_INVALID_ARG, "too many pages for int32 slots");
+  if ((long)n_pages * desc->n_kv_heads * 16 > 0xffffffffL)
+    return fail(KVB_ERR_UNSUPPORTED, "pool rows (pages x KV heads x 16) must fit 32 bits");
   CtxScope scope(ctx);
   const Ctx* c = current_ctx();
   const int Hq = desc->n_q_heads, Hkv = desc->n_kv_heads, hd = desc->head_dim;
