@@ -546,7 +546,7 @@ static kvb_status run_bf16(hipStream_t st, const GemmArgs<bf16_t>& p, const char
     const long tiles = (long)cdiv(p.M_max, sh.bm) * cdiv(p.N, DUAL ? sh.bn / 2 : sh.bn);
     const double tile_us = 2.0 * sh.bm * sh.bn * p.K / (4.5e6 * sh.eff);
     const int max_split = (si == 0 && sk_ws && p.N % 8 == 0) ? 16 : 1;
-    const long rows = (long)cdiv(p.M_max, sh.bm) * sh.bm, cols = DUAL ? 2L * p.N : p.N;
+    const long rows = p.M_max, cols = DUAL ? 2L * p.N : p.N;
     for (int S = 1; S <= max_split && S <= p.K / sh.kb; S++) {
       if (S > 1 && (size_t)S * rows * cols * 4 > SK_BUDGET) break;
       double tt = (double)((tiles * S + cus - 1) / cus) * tile_us / S;
@@ -562,7 +562,7 @@ static kvb_status run_bf16(hipStream_t st, const GemmArgs<bf16_t>& p, const char
   sk.S = 1;
   if (best_s > 1) {
     sk.S = best_s;
-    sk.rows = cdiv(p.M_max, TileL::BM) * TileL::BM;
+    sk.rows = p.M_max;  // partial row stride; only rows below the row count are written
     sk.cols = DUAL ? 2 * p.N : p.N;
     sk.part = (float*)sk_ws;
     KVB_TRY((launch_bf16<MODE, DUAL, TileL, true>(st, p, sk, name)));

@@ -57,6 +57,11 @@ class LinkConfig:
     lego_k: int = 32
     alpha_mode: int = K.KVB_ALPHA_LAG
     refresh_rule: int = K.KVB_REFRESH_LITERAL
+    # After each refresh, read the surviving row count back to the host (a
+    # 4-byte copy and one wait) so later layers launch at their true size and
+    # layers left with no rows are skipped; False keeps every launch sized for
+    # the layer-1 selection, the count read on the device only.
+    exact_rows: bool = True
 
 
 class LinkEngine:
@@ -202,6 +207,8 @@ class LinkEngine:
         self.ws_bytes = K.kvb_workspace_size(self.ctx, self.desc, rows_max, max(self.N, self.Nc), self.B)
         self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
         self.cur = 0
+        self._count_h = torch.zeros(1, dtype=torch.int32, pin_memory=True)
+        self._count_ev = torch.cuda.Event()
 
     # ------------------------------------------------------------------ helpers
     def close(self):
@@ -220,6 +227,15 @@ class LinkEngine:
 
     def _n_rows_ptr(self, which: int) -> int:
         return self.cu_rows[which].data_ptr() + 4 * self.B
+
+    def _read_rows(self, which: int) -> int:
+        """Total rows of selection buffer `which`, copied to the host once the
+        engine stream reaches this point."""
+        with torch.cuda.stream(self.stream):
+            self._count_h.copy_(self.cu_rows[which][self.B:self.B + 1], non_blocking=True)
+            self._count_ev.record(self.stream)
+        self._count_ev.synchronize()
+        return int(self._count_h[0])
 
     # ------------------------------------------------------------------ compile step
     def run_compile(self):
@@ -277,11 +293,18 @@ class LinkEngine:
         if hook:
             hook(1, self)
         T = self.T_sel
+        exact = cfg.exact_rows
         for l in range(2, self.L + 1):
             cur = self.cur
+            if T == 0:
+                # no row left to recompute: this layer's new pages stay unused
+                if hook:
+                    hook(l, self)
+                continue
             refresh = (l % cfg.period == 0) and l < self.L
-            self._layer_rows(l, T, self._n_rows_ptr(cur), self.sel[cur], self.cu_rows[cur], self.reuse_slot[l - 1],
-                             cfg.alpha_mode, self.alpha, self.dev_l, self.cksim if refresh else None)
+            self._layer_rows(l, T, None if exact else self._n_rows_ptr(cur), self.sel[cur], self.cu_rows[cur],
+                             self.reuse_slot[l - 1], cfg.alpha_mode, self.alpha, self.dev_l,
+                             self.cksim if refresh else None)
             if hook:
                 hook(l, self)
             if refresh:
@@ -289,6 +312,8 @@ class LinkEngine:
                                      cfg.tau, cfg.refresh_rule, self.ranking, self.s_count, self.cursor,
                                      self.sel[1 - cur], self.cu_rows[1 - cur], self.ws, self.ws_bytes)
                 self.cur = 1 - cur
+                if exact:
+                    T = self._read_rows(self.cur)
                 if hook:
                     hook(("refresh", l), self)
 

@@ -147,6 +147,8 @@ def run_fullsize(w, check_layers, seed=0):
             rows = [(gg, gg, b) for b in range(eng.B) for gg in range(cu[b], cu[b + 1])]
         else:
             rows = rows_in_order(eng, st)
+        if cacheslide and l > 1 and not rows:
+            continue  # no row left: the engine skips the layer, nothing is written
         # slot map of the layer, bit-exact, request by request
         for b, req in enumerate(w.requests):
             S_b = np.array([gg for _, gg, bb in rows if bb == b], dtype=np.int64) - cu[b]
