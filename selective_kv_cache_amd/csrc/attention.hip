@@ -21,6 +21,8 @@
 // fp32 path: one wave per (row, query head), plain online softmax.
 #include "common.h"
 
+#include <type_traits>
+
 namespace kvb {
 
 __device__ __forceinline__ size_t kv_off(int slot, int h, int Hkv, int hd) {
@@ -61,7 +63,7 @@ struct AttnGeom {
   static constexpr int RPI = 64 / CPR;               // rows per 1 KiB instruction
   static constexpr int TILE = AKT * ROWB;            // bytes of one K (or V) tile
   static constexpr int IPW = TILE / 1024 / AWAVES;   // instructions per wave per tile
-  static constexpr int STAGE = 2 * TILE;             // K tile, then V tile
+  static constexpr int STAGE = 2 * TILE;             // one K and one V tile
   // K: the fragment read of 16 consecutive rows at one chunk hits 16 distinct
   // bank groups.  V: the transposing read of 4 consecutive rows x 4 chunks
   // hits 16 distinct bank groups.  Both depend on the low row bits only.
@@ -107,7 +109,10 @@ attn_bf16_kernel(AttnArgs a) {
   static_assert(IPW * RPI == 8, "a wave loads 8 key rows");
   __shared__ __align__(16) uint8_t s_kv[ANST * Gm::STAGE];
   __shared__ __align__(16) int32_t s_slot[ANST][AWAVES][64];  // per stage, wave: keys 8 w + (lane % 8)
-  __shared__ uint32_t s_inval[ANST][AWAVES];                   // invalid-slot bits of the wave's 8 keys
+  // invalid-slot bits of each wave's 8 keys, one byte per wave: a stage's 64
+  // bits read back as one word
+  __shared__ __align__(8) uint8_t s_inval[ANST][AWAVES];
+  static_assert(AWAVES == 8, "one byte per wave makes the 64-key word");
   __shared__ int s_kmin, s_kmax, s_pmin, s_lomax;
 
   const int G = a.Hq / a.Hkv;
@@ -175,13 +180,21 @@ attn_bf16_kernel(AttnArgs a) {
   // the swizzles depend on the low row bits only, so kt, c and u are immediates.
   int koff[KS], voff[DT];
 #pragma unroll
-  for (int ks = 0; ks < KS; ks++) koff[ks] = l32 * ROWB + (((2 * ks + g2) ^ Gm::swz_k(l32)) * 16);
+  for (int ks = 0; ks < KS; ks++) {
+    koff[ks] = l32 * ROWB + (((2 * ks + g2) ^ Gm::swz_k(l32)) * 16);
+    // opaque, so stage + half offsets stay immediates of the reads rather
+    // than being merged into the lane offset with a per-read OR
+    asm volatile("" : "+v"(koff[ks]));
+  }
   {
     const int vr = 4 * g2 + (l16 >> 2);
 #pragma unroll
     for (int dt = 0; dt < DT; dt++) {
       const int chunk = 4 * dt + 2 * ((lane >> 4) & 1) + ((l16 >> 1) & 1);
-      voff[dt] = TILE + vr * ROWB + ((chunk ^ Gm::swz_v(vr)) * 16) + 8 * (l16 & 1);
+      // V tiles start after the ANST K tiles; the base is folded in here and
+      // hidden from the compiler so the stage offset stays an immediate
+      voff[dt] = ANST * TILE + vr * ROWB + ((chunk ^ Gm::swz_v(vr)) * 16) + 8 * (l16 & 1);
+      asm volatile("" : "+v"(voff[dt]));
     }
   }
 
@@ -208,7 +221,8 @@ attn_bf16_kernel(AttnArgs a) {
   // s_slot[X % 3][wave] complete
   auto issue_kv = [&](int X) {
     const int st = X % ANST;
-    uint8_t* kb = s_kv + st * Gm::STAGE;
+    uint8_t* kb = s_kv + st * TILE;
+    uint8_t* vb = s_kv + (ANST + st) * TILE;
     uint32_t bad = 0;
     int ln = lane;
     asm volatile("" : "+v"(ln));
@@ -231,9 +245,9 @@ attn_bf16_kernel(AttnArgs a) {
       const bf16_t* kp = a.k_pool + (size_t)prow * HD;
       const bf16_t* vp = a.v_pool + (size_t)prow * HD;
       dma16(kp + ((pos ^ Gm::swz_k(row)) * 8), __builtin_amdgcn_readfirstlane(lds_addr(kb + dst)));
-      dma16(vp + ((pos ^ Gm::swz_v(row)) * 8), __builtin_amdgcn_readfirstlane(lds_addr(kb + TILE + dst)));
+      dma16(vp + ((pos ^ Gm::swz_v(row)) * 8), __builtin_amdgcn_readfirstlane(lds_addr(vb + dst)));
     }
-    if (lane == 0) s_inval[st][wave] = bad;
+    if (lane == 0) s_inval[st][wave] = (uint8_t)bad;
   };
 
   // Issue order keeps vmcnt accounting fixed: ... D(X), S(X+2), D(X+1) are the
@@ -258,19 +272,18 @@ attn_bf16_kernel(AttnArgs a) {
     }
   }
 
-  for (int X = 0; X < nt; X++) {
+  // tile X in ring stage ST (a constant, so every LDS read is a lane base
+  // plus an immediate offset)
+  auto tile = [&](int X, auto stc) {
+    constexpr int st = decltype(stc)::value;
     if (X + 1 < nt) wait_vmcnt<2 * IPW>();
     else wait_vmcnt<0>();
     lds_barrier();  // stage X published; every wave is done with stage X - 1
-    if (X + 3 < nt) issue_slots(X + 3);
-    if (X + 2 < nt) issue_kv(X + 2);
 
-    const int st = X % ANST;
-    const uint8_t* sb = s_kv + st * Gm::STAGE;
+    const uint8_t* kbs = s_kv + st * TILE;
+    const uint8_t* vbs = s_kv + st * TILE;  // plus voff, which holds the V region base
     const int j0 = kbase + X * AKT;
-    uint64_t inval = 0;
-#pragma unroll
-    for (int w = 0; w < AWAVES; w++) inval |= (uint64_t)s_inval[st][w] << (8 * w);
+    const uint64_t inval = *reinterpret_cast<const uint64_t*>(&s_inval[st][0]);
     const bool need_mask = (j0 + AKT - 1 > pmin) || (j0 < lomax) || inval != 0;
 
 #pragma unroll
@@ -280,19 +293,25 @@ attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int ks = 0; ks < KS; ks++) {
         const bf16x8_t kf =
-            __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(sb + kt * 32 * ROWB + koff[ks]));
+            __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(kbs + kt * 32 * ROWB + koff[ks]));
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc, 0, 0, 0);
+      }
+      if (kt == 0) {
+        if (X + 3 < nt) issue_slots(X + 3);
+        if (X + 2 < nt) issue_kv(X + 2);
       }
       // softmax over the query's 32 keys of this half: 16 here, 16 in lane ^ 32
       float sv[16];
 #pragma unroll
       for (int r = 0; r < 16; r++) sv[r] = sacc[r];
       if (need_mask) {
+        // invalid bits of this lane's 16 keys: bit 8 (r / 4) + r % 4 of iv
+        const uint32_t iv = (uint32_t)(inval >> (kt * 32 + 4 * g2));
 #pragma unroll
         for (int r = 0; r < 16; r++) {
           const int kk = kt * 32 + 8 * (r >> 2) + 4 * g2 + (r & 3);
           const int key = j0 + kk;
-          if (key > qpos || key < qlo || ((inval >> kk) & 1u)) sv[r] = -INFINITY;
+          if (key > qpos || key < qlo || ((iv >> (8 * (r >> 2) + (r & 3))) & 1u)) sv[r] = -INFINITY;
         }
       }
       float mx = sv[0];
@@ -331,14 +350,19 @@ attn_bf16_kernel(AttnArgs a) {
         const int c = 2 * kt + cc;
 #pragma unroll
         for (int dt = 0; dt < DT; dt++) {
-          const uint2 v0 = lds_read_tr16(sb + (16 * c) * ROWB + voff[dt]);
-          const uint2 v1 = lds_read_tr16(sb + (16 * c + 8) * ROWB + voff[dt]);
+          const uint2 v0 = lds_read_tr16(vbs + (16 * c) * ROWB + voff[dt]);
+          const uint2 v1 = lds_read_tr16(vbs + (16 * c + 8) * ROWB + voff[dt]);
           const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
           oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, __builtin_bit_cast(bf16x8_t, pf[cc]), oacc[dt],
                                                              0, 0, 0);
         }
       }
     }
+  };
+  for (int X0 = 0; X0 < nt; X0 += ANST) {
+    tile(X0, std::integral_constant<int, 0>{});
+    if (X0 + 1 < nt) tile(X0 + 1, std::integral_constant<int, 1>{});
+    if (X0 + 2 < nt) tile(X0 + 2, std::integral_constant<int, 2>{});
   }
   wait_vmcnt<0>();
 
