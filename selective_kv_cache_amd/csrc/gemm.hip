@@ -21,6 +21,9 @@
 // deterministic for a given batch.
 #include "common.h"
 
+#include <algorithm>
+#include <type_traits>
+
 namespace kvb {
 
 enum EpiMode { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_SCATTER = 3 };
@@ -513,6 +516,10 @@ using TileL = Tile<256, 256, 2, 64, 2>;     // waves 128 x 64, 2 stages of K 64
 using TileL192 = Tile<192, 256, 2, 64, 2>;  // waves 96 x 64
 using TileM = Tile<256, 128, 4, 32, 4>;  // waves 64 x 64, 4 stages of K 32
 using TileS = Tile<128, 128, 4, 32, 4>;  // waves 32 x 64, 4 stages of K 32
+// few rows: 64-row tiles (waves 32 x 64, gate and up subtile pairs for
+// SwiGLU) with a 4-stage ring, so each block keeps three 40 KiB stages of
+// the weight stream in flight
+using TileN = Tile<64, 256, 2, 64, 4>;
 
 // split-K partials: float [S][rows][cols], at most this many bytes
 constexpr size_t SK_BUDGET = (size_t)256 << 20;
@@ -523,10 +530,13 @@ size_t ws_gemm_sk_bytes(int) { return SK_BUDGET; }
 // stage depth, so picking the shape from the launch bound keeps every row's
 // result independent of the batch.  `sk_ws` (SK_BUDGET bytes) allows split-K.
 //
-// Cost model (microseconds): a tile of BM x BN takes 2 BM BN K / (4.5 TFLOP/s
-// x shape efficiency) on one CU; whole waves of tiles (or slices) run on the
-// CUs; split-K adds the partials' round trip at ~5 TB/s and the reduction
-// launch.
+// Cost model (microseconds).  A block of BM x BN over K / S takes the longer
+// of its MFMA work at 4.5 TFLOP/s x shape efficiency and its operand bytes at
+// the rate one block streams them (150 GB/s for the large tiles, whose
+// operands mostly hit L2; 60 GB/s for the 64-row tile, which streams the
+// weights); whole waves of blocks run on the CUs; the launch takes at least
+// its unique operand bytes at 5 TB/s; split-K adds the partials' round trip
+// at 5 TB/s and the reduction launch.
 template <int MODE, bool DUAL>
 static kvb_status run_bf16(hipStream_t st, const GemmArgs<bf16_t>& p, const char* name, void* sk_ws = nullptr) {
   if (p.M_max == 0 || p.N == 0) return KVB_OK;
@@ -536,21 +546,27 @@ static kvb_status run_bf16(hipStream_t st, const GemmArgs<bf16_t>& p, const char
     return fail(KVB_ERR_UNSUPPORTED, std::string(name) + ": operands beyond 4 GiB of one base");
   Ctx* c = current_ctx();
   const long cus = c ? c->n_cu : 256;
-  struct Shape { int bm, bn, kb; double eff; };
-  const Shape shapes[4] = {{256, 256, 64, 1.0}, {192, 256, 64, 0.95}, {256, 128, 32, 0.85}, {128, 128, 32, 0.65}};
+  struct Shape { int bm, bn, kb; double eff, rate; bool split; };
+  const Shape shapes[5] = {{256, 256, 64, 1.0, 150e3, true},
+                           {192, 256, 64, 0.95, 150e3, false},
+                           {256, 128, 32, 0.85, 150e3, false},
+                           {128, 128, 32, 0.65, 150e3, false},
+                           {64, 256, 64, 0.5, 60e3, true}};
+  const double cols = DUAL ? 2.0 * p.N : (double)p.N;
+  const double hbm_us = (cols * p.K + (double)p.M_max * p.K) * 2.0 / 5e6;
   int best_shape = -1, best_s = 1;
   double best_t = 1e30;
-  for (int si = 0; si < 4; si++) {
+  for (int si = 0; si < 5; si++) {
     const Shape& sh = shapes[si];
     if (p.K % sh.kb) continue;
     const long tiles = (long)cdiv(p.M_max, sh.bm) * cdiv(p.N, DUAL ? sh.bn / 2 : sh.bn);
-    const double tile_us = 2.0 * sh.bm * sh.bn * p.K / (4.5e6 * sh.eff);
-    const int max_split = (si == 0 && sk_ws && p.N % 8 == 0) ? 16 : 1;
-    const long rows = p.M_max, cols = DUAL ? 2L * p.N : p.N;
+    const int max_split = (sh.split && sk_ws && p.N % 8 == 0) ? 16 : 1;
     for (int S = 1; S <= max_split && S <= p.K / sh.kb; S++) {
-      if (S > 1 && (size_t)S * rows * cols * 4 > SK_BUDGET) break;
-      double tt = (double)((tiles * S + cus - 1) / cus) * tile_us / S;
-      if (S > 1) tt += 2.0 * S * rows * cols * 4 / 5e6 + 4.0;
+      if (S > 1 && (size_t)S * p.M_max * (size_t)cols * 4 > SK_BUDGET) break;
+      const double kk = (double)p.K / S;
+      const double blk_us = std::max(2.0 * sh.bm * sh.bn * kk / (4.5e6 * sh.eff), (sh.bm + sh.bn) * kk * 2.0 / sh.rate);
+      double tt = std::max((double)((tiles * S + cus - 1) / cus) * blk_us, hbm_us);
+      if (S > 1) tt += 2.0 * S * p.M_max * cols * 4 / 5e6 + 4.0;
       if (tt < best_t * (S > 1 ? 0.92 : 1.0)) {
         best_t = tt;
         best_shape = si;
@@ -565,7 +581,8 @@ static kvb_status run_bf16(hipStream_t st, const GemmArgs<bf16_t>& p, const char
     sk.rows = p.M_max;  // partial row stride; only rows below the row count are written
     sk.cols = DUAL ? 2 * p.N : p.N;
     sk.part = (float*)sk_ws;
-    KVB_TRY((launch_bf16<MODE, DUAL, TileL, true>(st, p, sk, name)));
+    if (best_shape == 0) KVB_TRY((launch_bf16<MODE, DUAL, TileL, true>(st, p, sk, name)));
+    else KVB_TRY((launch_bf16<MODE, DUAL, TileN, true>(st, p, sk, name)));
     return launch_splitk_reduce<MODE, DUAL>(st, p, sk, "splitk_reduce");
   }
   switch (best_shape) {
@@ -573,6 +590,7 @@ static kvb_status run_bf16(hipStream_t st, const GemmArgs<bf16_t>& p, const char
     case 1: return launch_bf16<MODE, DUAL, TileL192, false>(st, p, sk, name);
     case 2: return launch_bf16<MODE, DUAL, TileM, false>(st, p, sk, name);
     case 3: return launch_bf16<MODE, DUAL, TileS, false>(st, p, sk, name);
+    case 4: return launch_bf16<MODE, DUAL, TileN, false>(st, p, sk, name);
     default: return fail(KVB_ERR_UNSUPPORTED, std::string(name) + ": K must be a multiple of 32");
   }
 }

@@ -268,12 +268,14 @@ def test_sparse_query_attention(ctx, name, req_lens, n_sel):
 # ------------------------------------------------------------------ O-proj + MLP
 
 @pytest.mark.parametrize("name", ["bf16", "fp32"])
-def test_mlp(ctx, name):
+@pytest.mark.parametrize("T_max,n_valid", [(230, 201), (64, 64), (7, 5), (1, 1)])
+def test_mlp(ctx, name, T_max, n_valid):
+    """O-proj + MLP on gathered rows; the small batches take the 64-row tiles with split-K."""
     s = SHAPES[name]
-    g = np.random.default_rng(8)
+    g = np.random.default_rng(8 + T_max)
     desc = K.model_desc(s)
     dt = tdt(s)
-    n_tok, T_max, n_valid = 400, 230, 201
+    n_tok = 400
     hidden0 = rand((n_tok, s.d_model), g, dtype=dt)
     hidden = hidden0.to(DEV)
     W = weights(s, g)
