@@ -60,7 +60,7 @@ class LinkConfig:
     # After each refresh, read the surviving row count back to the host (a
     # 4-byte copy and one wait) so later layers launch at their true size and
     # layers left with no rows are skipped; False keeps every launch sized for
-    # the layer-1 selection, the count read on the device only.
+    # the layer-1 selection.  The device-side count bounds the rows either way.
     exact_rows: bool = True
 
 
@@ -302,9 +302,10 @@ class LinkEngine:
                     hook(l, self)
                 continue
             refresh = (l % cfg.period == 0) and l < self.L
-            self._layer_rows(l, T, None if exact else self._n_rows_ptr(cur), self.sel[cur], self.cu_rows[cur],
-                             self.reuse_slot[l - 1], cfg.alpha_mode, self.alpha, self.dev_l,
-                             self.cksim if refresh else None)
+            # the device count always bounds the rows: until the first refresh T is
+            # the capacity, which the top-k does not fill when few tokens deviate
+            self._layer_rows(l, T, self._n_rows_ptr(cur), self.sel[cur], self.cu_rows[cur], self.reuse_slot[l - 1],
+                             cfg.alpha_mode, self.alpha, self.dev_l, self.cksim if refresh else None)
             if hook:
                 hook(l, self)
             if refresh:

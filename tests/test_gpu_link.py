@@ -298,12 +298,44 @@ def test_link_is_deterministic_and_repeatable():
     eng.close()
 
 
-def test_single_chunk_selects_nothing():
-    """A one-chunk prompt: d == 0 everywhere, S empty, later layers recompute nothing."""
-    w = wl.tiny(n_layers=3, lens=(200,))
+@pytest.mark.parametrize("exact", [True, False])
+def test_single_chunk_selects_nothing(exact):
+    """A one-chunk prompt: d == 0 everywhere, S empty, later layers recompute and write nothing."""
+    w = wl.tiny(n_layers=5, lens=(200,))
     eng, E, W = build_engine(w)
+    eng.cfg.exact_rows = exact
     eng.run_compile()
-    eng.run_link()
+    after1 = {}
+
+    def hook(key, e):
+        if key == 1:
+            torch.cuda.synchronize()
+            after1.update(hidden=e.hidden.clone(), k=e.k_pool.clone(), v=e.v_pool.clone())
+
+    eng.run_link(hook=hook)
     torch.cuda.synchronize()
     assert torch.all(eng.d == 0) and int(eng.s_count[0]) == 0 and len(eng.selected()[0]) == 0
+    assert torch.equal(eng.hidden, after1["hidden"])
+    assert torch.equal(eng.k_pool, after1["k"]) and torch.equal(eng.v_pool, after1["v"])
+    eng.close()
+
+
+@pytest.mark.parametrize("exact", [True, False])
+def test_few_deviating_tokens_fill_less_than_capacity(exact):
+    """A long first chunk (d == 0) and a short second one: |S| < k, so only |S| rows run in layer 2."""
+    w = wl.tiny(n_layers=3, lens=(400, 40))
+    eng, E, W = build_engine(w)
+    eng.cfg.exact_rows = exact
+    eng.run_compile()
+    rec = Recorder()
+    eng.run_link(hook=rec)
+    torch.cuda.synchronize()
+    n_dev = int((eng.d[:440] > 0).sum())
+    S = rows_of(rec.after[1])
+    assert len(S) == n_dev < eng.k_cap[0]
+    st2 = rec.after[2]
+    assert np.array_equal(rows_of(st2), S)
+    # the slot map of layer 2 moves exactly the selected tokens to new slots
+    moved = np.nonzero(st2["slot_map"].cpu().numpy()[:440] != eng.reuse_slot_h[1][:440])[0]
+    assert np.array_equal(moved, S)
     eng.close()
