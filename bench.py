@@ -37,6 +37,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mistral7b-cacheslide-8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-tier", action="store_true", help="skip the host-tier (reused KV in pinned host memory) leg")
     ap.add_argument("--profile-only", action="store_true", help="warmup + timed steps only (for rocprofv3)")
     return ap.parse_args()
 
@@ -103,6 +104,57 @@ def cpu_baseline(w, eng, rec_state, step_flops):
                        f"{threads} BLAS threads): {t2:.2f} s; link time scaled as T2 * FLOPs(link step) / "
                        f"FLOPs(layer 2) = {t_link:.1f} s"),
             "measured_s": t2, "extrapolated_link_s": t_link}
+
+
+def tier_host(eng, args, st, n_selected):
+    """The same link step with the reused KV (compile pages) in pinned host
+    memory, each layer's pages copied into the pool during the step: overlapped
+    with the recompute (copy stream ahead of it) and serially (copy, then the
+    layer), plus the copies alone.  Timed with HIP events on the engine stream."""
+    import numpy as np
+    import torch
+
+    from selective_kv_cache_amd import _lib as K
+
+    cfg = eng.cfg
+    saved = (cfg.reuse_tier, cfg.tier_overlap)
+    cfg.reuse_tier = "host"
+    eng.stage_reuse_to_host()
+
+    def timed(fn, n):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        torch.cuda.synchronize()
+        for a, b in ev:
+            a.record(st)
+            fn()
+            b.record(st)
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+    res = {}
+    for overlap in (True, False):
+        cfg.tier_overlap = overlap
+        for _ in range(max(args.warmup, 1)):
+            eng.run_link()
+        res["overlapped" if overlap else "serial"] = timed(eng.run_link, args.steps)
+    # bytes one step loads: every layer's reused pages (layer 1 of CacheSlide: keys only)
+    page_b = eng.k_pool[0].numel() * eng.k_pool.element_size()
+    layers = list(range(1, eng.L + 1))
+    nbytes = sum(len(eng.layer_reuse_pages[l]) * page_b * (1 if (l == 1 and cfg.mode == "cacheslide") else 2)
+                 for l in layers)
+
+    def copies_only():
+        for l in layers:
+            eng._tier_copy(l, eng.sh)
+
+    copy_ms = timed(copies_only, 3)
+    cfg.reuse_tier, cfg.tier_overlap = saved
+    return {"ms_per_step_overlapped": res["overlapped"], "ms_per_step_serial": res["serial"],
+            "selected_tokens_per_s_overlapped": n_selected / (res["overlapped"] * 1e-3),
+            "copies_alone_ms": copy_ms, "bytes_if_every_layer_loads": nbytes,
+            "h2d_GBps": nbytes / (copy_ms * 1e-3) / 1e9,
+            "note": "reused KV in pinned host memory, each layer's pages copied host-to-device during the step "
+                    "(layers left with no rows load nothing); median of the timed steps"}
 
 
 def main():
@@ -261,7 +313,11 @@ def main():
                      "work_per_launch": dom_work_per_launch},
         "kernels": per_kernel,
         "step_ms_min_max": [float(np.min(step_ms)), float(np.max(step_ms))],
+        "step_ms_p10_median_p90": [float(np.percentile(step_ms, 10)), float(np.median(step_ms)),
+                                   float(np.percentile(step_ms, 90))],
     }
+    if not args.no_tier:
+        out["tier_host"] = tier_host(eng, args, st, n_selected)
     if not args.no_cpu_baseline and cfg.mode == "cacheslide":
         try:
             step_flops = sum(work[k] for k, b in BOUND.items() if b == "mfma")

@@ -132,6 +132,25 @@ kvb_status kvb_pool_alloc(kvb_pool* pool, int32_t n, int32_t* out_ids /* host [n
 kvb_status kvb_pool_release(kvb_pool* pool, int32_t n, const int32_t* ids /* host [n] */);
 kvb_status kvb_pool_free_count(const kvb_pool* pool, int32_t* out);
 
+/* --------------------------------------------------- page tiers
+ * Copy whole pages between a host tier and the device pool (CacheSlide page,
+ * SLIDE: reused KV that lives in a lower tier is loaded layer by layer while
+ * the selected rows are recomputed into new pages).  Both sides use the pool
+ * layout [page][Hkv][16][hd] with page p at byte offset p * page_bytes, so a
+ * host mirror of the first P pages serves pages 0..P-1.  page_ids: host int32
+ * [n_ids], non-negative; runs of consecutive ids become one hipMemcpyAsync
+ * each (K, then V) on `stream`, so the call returns once they are enqueued.
+ * dst_k or dst_v may be NULL to copy one half only (layer 1 of CacheSlide
+ * reads reused keys only).  direction: KVB_COPY_H2D (src host, dst device) or
+ * KVB_COPY_D2H.  Host buffers must be pinned for the copies to overlap
+ * kernels.  The caller keeps ids within both buffers; the library cannot
+ * check host extents. */
+#define KVB_COPY_H2D 0
+#define KVB_COPY_D2H 1
+kvb_status kvb_pages_copy(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t direction,
+                          const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                          const int32_t* page_ids /* host [n_ids] */, int32_t n_ids);
+
 /* ------------------------------------------------------------ the path */
 
 /* hidden[row_tok[r]] = table[tokens[row_tok[r]]] for r < *n_rows.

@@ -23,6 +23,7 @@ KVB_ERR_WORKSPACE = -5
 KVB_F32, KVB_BF16 = 0, 1
 KVB_ALPHA_LAG, KVB_ALPHA_CURRENT, KVB_ALPHA_ONE = 0, 1, 2
 KVB_REFRESH_LITERAL, KVB_REFRESH_DISSIM = 0, 1
+KVB_COPY_H2D, KVB_COPY_D2H = 0, 1
 
 
 class KvbError(RuntimeError):
@@ -52,6 +53,7 @@ _SIGS = {
     "kvb_pool_alloc": ([P, I, P], I),
     "kvb_pool_release": ([P, I, P], I),
     "kvb_pool_free_count": ([P, POINTER(c_int32)], I),
+    "kvb_pages_copy": ([P, P, P, I, P, P, P, P, P, I], I),
     "kvb_embed": ([P, P, P, I, P, P, P, I, P, P], I),
     "kvb_qkv_proj": ([P, P, P, I, P, P, P, P, P, P, P, P, P, P, c_size_t], I),
     "kvb_rope": ([P, P, P, I, P, P, P, P, P], I),
@@ -194,6 +196,14 @@ def kvb_pool_free_count(pool) -> int:
     out = c_int32()
     _check("kvb_pool_free_count", load().kvb_pool_free_count(pool, ctypes.byref(out)))
     return out.value
+
+
+def kvb_pages_copy(ctx, stream, desc, direction, src_k, src_v, dst_k, dst_v, page_ids) -> None:
+    """page_ids: host sequence of page ids (marshalled to a host int32 array)."""
+    ids = [int(x) for x in page_ids]
+    buf = (c_int32 * max(len(ids), 1))(*ids)
+    _call("kvb_pages_copy", ctx, stream, desc, direction, src_k, src_v, dst_k, dst_v,
+          ctypes.cast(buf, c_void_p).value, len(ids))
 
 
 # ------------------------------------------------------------------ the path

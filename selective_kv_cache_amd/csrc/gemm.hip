@@ -52,6 +52,9 @@ struct GemmArgs {
 };
 
 __device__ __forceinline__ float silu(float x) { return x / (1.f + __expf(-x)); }
+// bf16 epilogues: the hardware reciprocal (about 1 ulp) instead of an IEEE
+// division; the result is rounded to bf16 right after
+__device__ __forceinline__ float silu_bf16(float x) { return x * __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 
 template <int MODE, class T>
 __device__ __forceinline__ void epilogue(const GemmArgs<T>& p, int m, int n, float acc, float acc2, float rinv) {
@@ -404,7 +407,7 @@ gemm_bf16_kernel(GemmArgs<bf16_t> p, SkArgs sk) {
           for (int r = 0; r < 16; r++) {
             const int rl = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);  // row inside the phase
             float v = acc[i][j][r];
-            if (DUAL) v = silu(v) * acc[i][j + 1][r];
+            if (DUAL) v = silu_bf16(v) * acc[i][j + 1][r];
             sC[rl * LDC + cl] = v;
           }
         }
@@ -479,7 +482,7 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmArgs<bf16_t> p, 
   bf16_t* dst;
   if (MODE == EPI_SWIGLU) {
 #pragma unroll
-    for (int e = 0; e < 8; e++) v[e] = DUAL ? silu(v[e]) * u[e] : v[e];
+    for (int e = 0; e < 8; e++) v[e] = DUAL ? silu_bf16(v[e]) * u[e] : v[e];
     dst = p.out0 + (size_t)m * p.ldo + n;
   } else if (MODE == EPI_QKV) {
     if (n < p.n0) dst = p.out0 + (size_t)m * p.n0 + n;

@@ -292,4 +292,44 @@ kvb_status kvb_pool_free_count(const kvb_pool* pool, int32_t* out) {
   return KVB_OK;
 }
 
+// ------------------------------------------------------------ page tiers
+
+kvb_status kvb_pages_copy(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t direction,
+                          const void* src_k, const void* src_v, void* dst_k, void* dst_v, const int32_t* page_ids,
+                          int32_t n_ids) {
+  KVB_TRY(check_ctx(ctx));
+  KVB_TRY(check_desc(desc));
+  if (direction != KVB_COPY_H2D && direction != KVB_COPY_D2H)
+    return fail(KVB_ERR_INVALID_ARG, "direction must be KVB_COPY_H2D or KVB_COPY_D2H");
+  if (n_ids < 0) return fail(KVB_ERR_INVALID_ARG, "n_ids < 0");
+  if (n_ids == 0) return KVB_OK;
+  if (!page_ids) return fail(KVB_ERR_INVALID_ARG, "page_ids is NULL");
+  if (!src_k && dst_k) return fail(KVB_ERR_INVALID_ARG, "src_k is NULL");
+  if (!src_v && dst_v) return fail(KVB_ERR_INVALID_ARG, "src_v is NULL");
+  for (int32_t i = 0; i < n_ids; i++)
+    if (page_ids[i] < 0) return fail(KVB_ERR_INVALID_ARG, "negative page id");
+  CtxScope scope(ctx);
+  const size_t esz = desc->dtype == KVB_BF16 ? 2 : 4;
+  const size_t page_bytes = (size_t)desc->n_kv_heads * 16 * desc->head_dim * esz;
+  const hipMemcpyKind kind = direction == KVB_COPY_H2D ? hipMemcpyHostToDevice : hipMemcpyDeviceToHost;
+  hipStream_t st = (hipStream_t)stream;
+  // one copy per run of consecutive ids, for K then V
+  int32_t i = 0;
+  while (i < n_ids) {
+    int32_t j = i + 1;
+    while (j < n_ids && page_ids[j] == page_ids[j - 1] + 1) j++;
+    const size_t off = (size_t)page_ids[i] * page_bytes, len = (size_t)(j - i) * page_bytes;
+    if (dst_k) {
+      const hipError_t e = hipMemcpyAsync((char*)dst_k + off, (const char*)src_k + off, len, kind, st);
+      if (e != hipSuccess) return fail(KVB_ERR_HIP, std::string("hipMemcpyAsync: ") + hipGetErrorString(e));
+    }
+    if (dst_v) {
+      const hipError_t e = hipMemcpyAsync((char*)dst_v + off, (const char*)src_v + off, len, kind, st);
+      if (e != hipSuccess) return fail(KVB_ERR_HIP, std::string("hipMemcpyAsync: ") + hipGetErrorString(e));
+    }
+    i = j;
+  }
+  return KVB_OK;
+}
+
 }  // extern "C"

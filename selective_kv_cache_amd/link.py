@@ -62,6 +62,15 @@ class LinkConfig:
     # layers left with no rows are skipped; False keeps every launch sized for
     # the layer-1 selection.  The device-side count bounds the rows either way.
     exact_rows: bool = True
+    # Where the compile step's KV (the reused cache) lives during the link
+    # step.  "hbm": resident in the device pool.  "host": in pinned host memory
+    # (SLIDE's lower tier); each layer's reused pages are copied into the pool
+    # during the step, on a copy stream that runs `tier_lookahead` layers ahead
+    # of the recompute (tier_overlap=True) or on the compute stream right before
+    # the layer (False: the serial baseline).
+    reuse_tier: str = "hbm"
+    tier_overlap: bool = True
+    tier_lookahead: int = 2
 
 
 class LinkEngine:
@@ -139,6 +148,11 @@ class LinkEngine:
             for l in range(1, self.L + 1):
                 link_pages[b][l] = K.kvb_pool_alloc(self.pool, _npages(per_layer(l, b)))
         self.comp_pages, self.link_pages = comp_pages, link_pages
+        # compile pages are the first n_compile_pages ids; per layer, those every
+        # request may read (reused K/V of that layer)
+        self.n_compile_pages = n_compile_pages
+        self.layer_reuse_pages = [None] + [
+            sorted(p for c in chunks for p in comp_pages[c.uid][l - 1]) for l in range(1, self.L + 1)]
 
         def slots(pages, n):
             j = np.arange(n)
@@ -258,12 +272,82 @@ class LinkEngine:
                 K.kvb_mlp(c, sh, ds, Nc, None, None, self.o, W["w_o"], self.hidden_c, W["norm2"], W["w_gate_up"],
                           W["w_down"], self.ws, self.ws_bytes)
 
+    def stage_reuse_to_host(self, evict: bool = False):
+        """Copy the compile pages to pinned host memory (the lower tier the link
+        step then loads from).  evict=True also zeroes their device copies, so a
+        link step can only see what it loads."""
+        if self.cfg.reuse_tier != "host":
+            raise ValueError("stage_reuse_to_host needs reuse_tier='host'")
+        n = self.n_compile_pages
+        if getattr(self, "host_k", None) is None:
+            shp = (max(n, 1),) + tuple(self.k_pool.shape[1:])
+            self.host_k = torch.empty(shp, dtype=self.k_pool.dtype, pin_memory=True)
+            self.host_v = torch.empty(shp, dtype=self.v_pool.dtype, pin_memory=True)
+        K.kvb_pages_copy(self.ctx, self.sh, self.desc, K.KVB_COPY_D2H, self.k_pool, self.v_pool, self.host_k,
+                         self.host_v, range(n))
+        self.stream.synchronize()
+        if evict and n:
+            with torch.cuda.stream(self.stream):
+                self.k_pool[:n].zero_()
+                self.v_pool[:n].zero_()
+            self.stream.synchronize()
+
+    # ------------------------------------------------------------------ tiers
+    def _tier_begin(self):
+        """Start of a link step that loads its reused pages from the host tier."""
+        self._tier = self.cfg.reuse_tier == "host"
+        if not self._tier:
+            return
+        if getattr(self, "host_k", None) is None:
+            raise RuntimeError("reuse_tier='host': call stage_reuse_to_host() after run_compile()")
+        self._tier_enq = 0
+        self._tier_ev = [None] * (self.L + 1)
+        if self.cfg.tier_overlap:
+            if getattr(self, "copy_stream", None) is None:
+                self.copy_stream = torch.cuda.Stream(self.device)  # default priority
+            start = torch.cuda.Event()
+            start.record(self.stream)
+            self.copy_stream.wait_event(start)  # the previous step is done with the pool
+
+    def _tier_copy(self, l: int, stream_handle: int):
+        # layer 1 of CacheSlide reads reused keys only (the deviation)
+        keys_only = l == 1 and self.cfg.mode == "cacheslide"
+        K.kvb_pages_copy(self.ctx, stream_handle, self.desc, K.KVB_COPY_H2D, self.host_k,
+                         None if keys_only else self.host_v, self.k_pool, None if keys_only else self.v_pool,
+                         self.layer_reuse_pages[l])
+
+    def _tier_need(self, l: int, runs_until: int):
+        """Before layer l: its reused pages are in the pool.  Layers up to
+        runs_until are known to run, so copies for them may be queued ahead."""
+        if not self._tier:
+            return
+        if not self.cfg.tier_overlap:
+            self._tier_copy(l, self.sh)
+            return
+        last = min(self.L, runs_until, l + self.cfg.tier_lookahead)
+        ch = K.stream_handle(self.copy_stream)
+        while self._tier_enq < max(last, l):
+            j = self._tier_enq + 1
+            self._tier_copy(j, ch)
+            ev = torch.cuda.Event()
+            ev.record(self.copy_stream)
+            self._tier_ev[j] = ev
+            self._tier_enq = j
+        self.stream.wait_event(self._tier_ev[l])
+
+    def _tier_end(self):
+        # copies queued ahead for layers that were then skipped belong to this step
+        if self._tier and self.cfg.tier_overlap and self._tier_enq:
+            self.stream.wait_event(self._tier_ev[self._tier_enq])
+
     # ------------------------------------------------------------------ link step
     def run_link(self, hook: Optional[Callable] = None):
+        self._tier_begin()
         if self.cfg.mode == "cacheslide":
             self._link_cacheslide(hook)
         else:
             self._link_static(hook)
+        self._tier_end()
 
     def _layer_rows(self, l, T, n_rows, rows, cu_rows, src_slot, alpha_mode, alpha, d_out, cksim_out):
         """One recompute layer for the given rows: slot map, Q/K/V + RoPE, fusion and
@@ -286,6 +370,7 @@ class LinkEngine:
         K.kvb_embed(c, sh, ds, N, None, None, self.tok_l, self.shape.vocab, self.model.embedding, self.hidden)
         # layer 1: every token recomputed at its spliced position, written to layer-1 new pages
         self._layer_rows(1, N, None, None, self.cu_tok, None, K.KVB_ALPHA_ONE, None, None, None)
+        self._tier_need(1, min(self.L, cfg.period + 1))
         K.kvb_deviation_topk(c, sh, ds, B, N, self.cu_tok, self.k, self.k_pool, self.n_pages, self.reuse_slot[0],
                              self.k_cap_d, self.d, self.alpha, self.ranking, self.s_count, self.sel[0],
                              self.cu_rows[0], self.cursor, self.ws, self.ws_bytes)
@@ -302,6 +387,10 @@ class LinkEngine:
                     hook(l, self)
                 continue
             refresh = (l % cfg.period == 0) and l < self.L
+            # every layer up to the next refresh runs with the current set; the
+            # layer after it is loaded speculatively (it runs unless the refresh
+            # empties the set, and then its load is only wasted transfer)
+            self._tier_need(l, -(-l // cfg.period) * cfg.period + 1 if exact else self.L)
             # the device count always bounds the rows: until the first refresh T is
             # the capacity, which the top-k does not fill when few tokens deviate
             self._layer_rows(l, T, self._n_rows_ptr(cur), self.sel[cur], self.cu_rows[cur], self.reuse_slot[l - 1],
@@ -325,6 +414,7 @@ class LinkEngine:
         K.kvb_embed(c, sh, ds, T, None, self.lego_sel, self.tok_l, self.shape.vocab, self.model.embedding,
                     self.hidden)
         for l in range(1, self.L + 1):
+            self._tier_need(l, self.L)
             self._layer_rows(l, T, None, self.lego_sel, self.lego_cu, None, K.KVB_ALPHA_ONE, None, None, None)
             if hook:
                 hook(l, self)

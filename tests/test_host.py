@@ -147,3 +147,19 @@ def test_product_code_does_not_import_the_oracle():
                 src = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in src and "from oracle" not in src, f
                 assert "workloads" not in src or f.endswith(".py") is False or "import workloads" not in src, f
+
+
+def test_pages_copy_checks(lib):
+    """kvb_pages_copy: argument errors are reported before anything is enqueued."""
+    d = _desc()
+    for direction, ids, status in ((7, [0], K.KVB_ERR_INVALID_ARG), (K.KVB_COPY_H2D, [3, -1], K.KVB_ERR_INVALID_ARG)):
+        with pytest.raises(K.KvbError) as e:
+            K.kvb_pages_copy(FAKE_CTX, None, d, direction, 1, 1, 1, 1, ids)
+        assert e.value.status == status
+    with pytest.raises(K.KvbError) as e:
+        K.kvb_pages_copy(None, None, d, K.KVB_COPY_H2D, 1, 1, 1, 1, [0])
+    assert e.value.status == K.KVB_ERR_INVALID_ARG
+    with pytest.raises(K.KvbError) as e:  # a destination without its source
+        K.kvb_pages_copy(FAKE_CTX, None, d, K.KVB_COPY_H2D, None, 1, 1, 1, [0])
+    assert e.value.status == K.KVB_ERR_INVALID_ARG and "src_k" in K.kvb_last_error()
+    K.kvb_pages_copy(FAKE_CTX, None, d, K.KVB_COPY_D2H, None, None, None, None, [])  # nothing to copy
