@@ -38,6 +38,7 @@ def parse():
     ap.add_argument("--workload", default="mistral7b-cacheslide-8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-tier", action="store_true", help="skip the host-tier (reused KV in pinned host memory) leg")
+    ap.add_argument("--no-compile", action="store_true", help="skip timing the compile step")
     ap.add_argument("--profile-only", action="store_true", help="warmup + timed steps only (for rocprofv3)")
     return ap.parse_args()
 
@@ -104,6 +105,35 @@ def cpu_baseline(w, eng, rec_state, step_flops):
                        f"{threads} BLAS threads): {t2:.2f} s; link time scaled as T2 * FLOPs(link step) / "
                        f"FLOPs(layer 2) = {t_link:.1f} s"),
             "measured_s": t2, "extrapolated_link_s": t_link}
+
+
+def compile_step(eng, args, st, s):
+    """The compile step as a second workload: every chunk instance prefilled
+    alone from position 0 into its compile pages (QKV for every layer; attention,
+    O-projection and MLP for layers 1..L-1).  HIP events on the engine stream."""
+    import numpy as np
+    import torch
+
+    d, F, Hq, Hkv, hd, L = s.d_model, s.ffn, s.n_q_heads, s.n_kv_heads, s.head_dim, s.n_layers
+    lens = [len(c.tokens) for c in eng.chunks]
+    Nc = int(sum(lens))
+    pos_sum = float(sum(n * (n + 1) / 2 for n in lens))   # sum over tokens of (local position + 1)
+    flops = (L * 2.0 * Nc * d * (Hq + 2 * Hkv) * hd
+             + (L - 1) * (2.0 * Nc * (Hq * hd * d + 3 * d * F) + 4.0 * Hq * hd * pos_sum))
+    for _ in range(max(args.warmup, 1)):
+        eng.run_compile()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(st)
+        eng.run_compile()
+        b.record(st)
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"ms_per_step": ms, "tokens_per_s": Nc / (ms * 1e-3), "tokens": Nc, "algorithmic_tflop": flops / 1e12,
+            "achieved_tflops": tf, "mfma_frac": tf / PEAK_BF16_TFLOPS if s.dtype == "bf16" else None,
+            "note": "compile step (per-chunk prefill from position 0), median of the timed runs"}
 
 
 def tier_host(eng, args, st, n_selected):
@@ -316,6 +346,8 @@ def main():
         "step_ms_p10_median_p90": [float(np.percentile(step_ms, 10)), float(np.median(step_ms)),
                                    float(np.percentile(step_ms, 90))],
     }
+    if not args.no_compile:
+        out["compile_step"] = compile_step(eng, args, st, s)
     if not args.no_tier:
         out["tier_host"] = tier_host(eng, args, st, n_selected)
     if not args.no_cpu_baseline and cfg.mode == "cacheslide":
