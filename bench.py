@@ -28,6 +28,7 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 COPY_BYTES = 256 << 20         # copy probe of --profile-only (fp32 multiply by 1, out of place)
+DECODE_TOKENS = 8              # decode continuation leg: tokens per request
 
 
 def parse():
@@ -39,6 +40,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-tier", action="store_true", help="skip the host-tier (reused KV in pinned host memory) leg")
     ap.add_argument("--no-compile", action="store_true", help="skip timing the compile step")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode continuation leg")
     ap.add_argument("--profile-only", action="store_true", help="warmup + timed steps only (for rocprofv3)")
     return ap.parse_args()
 
@@ -105,6 +107,30 @@ def cpu_baseline(w, eng, rec_state, step_flops):
                        f"{threads} BLAS threads): {t2:.2f} s; link time scaled as T2 * FLOPs(link step) / "
                        f"FLOPs(layer 2) = {t_link:.1f} s"),
             "measured_s": t2, "extrapolated_link_s": t_link}
+
+
+def decode_leg(eng, st):
+    """Decode continuation after the last link step: DECODE_TOKENS tokens per
+    request, each a full pass over every layer at one row per request,
+    attending to the link step's page table.  New tokens go to new pages (the
+    HBM-resident cache is not overwritten).  HIP events on the engine stream."""
+    import numpy as np
+    import torch
+
+    eng.decode_init(overwrite_first=False)
+    toks = np.random.default_rng(11).integers(0, eng.shape.vocab, size=(DECODE_TOKENS, eng.B))
+    eng.decode_step(toks[0])  # first step: warm-up
+    n = DECODE_TOKENS - 1
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(st)
+    for t in range(1, DECODE_TOKENS):
+        eng.decode_step(toks[t])
+    b.record(st)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / n
+    return {"ms_per_decode_step": ms, "tokens_per_s": eng.B / (ms * 1e-3), "requests": eng.B, "steps_timed": n,
+            "note": "one token per request per step after the link step, placed on new pages"}
 
 
 def compile_step(eng, args, st, s):
@@ -211,7 +237,7 @@ def main():
     E = wl.embedding_table(w, dev)
     layers = [wl.layer_weights(w, l, dev) for l in range(1, s.n_layers + 1)]
     cfg = LinkConfig(mode=w.mode, ratio=w.ratio, tau=w.tau, period=w.period, lego_k=w.lego_k)
-    eng = LinkEngine(Model(s, E, layers), w.requests, cfg, device=dev)
+    eng = LinkEngine(Model(s, E, layers), w.requests, cfg, device=dev, max_decode=DECODE_TOKENS)
     eng.run_compile()
     torch.cuda.synchronize()
     print(f"# setup {time.perf_counter() - t_setup:.1f}s: {w.name}, N={eng.N}, pages={eng.n_pages}", file=sys.stderr,
@@ -346,6 +372,8 @@ def main():
         "step_ms_p10_median_p90": [float(np.percentile(step_ms, 10)), float(np.median(step_ms)),
                                    float(np.percentile(step_ms, 90))],
     }
+    if not args.no_decode:
+        out["decode"] = decode_leg(eng, st)
     if not args.no_compile:
         out["compile_step"] = compile_step(eng, args, st, s)
     if not args.no_tier:

@@ -81,8 +81,9 @@ class LinkEngine:
     shared read-only by every request that splices them.
     """
 
-    def __init__(self, model: Model, requests, cfg: LinkConfig, device="cuda:0", stream=None):
+    def __init__(self, model: Model, requests, cfg: LinkConfig, device="cuda:0", stream=None, max_decode: int = 0):
         self.model, self.cfg, self.device = model, cfg, torch.device(device)
+        self.requests = list(requests)
         s = model.shape
         self.shape = s
         self.L = s.n_layers
@@ -138,7 +139,11 @@ class LinkEngine:
             raise ValueError(cfg.mode)
         n_compile_pages = sum(_npages(n) for n in lens_c) * self.L
         n_link_pages = sum(_npages(per_layer(l, b)) for l in range(1, self.L + 1) for b in range(self.B))
-        self.n_pages = n_compile_pages + n_link_pages
+        # decode continuation: room for max_decode tokens per request and layer
+        # when no overwritable slot is left (allocated after every other page)
+        self.max_decode = int(max_decode)
+        n_decode_pages = _npages(self.max_decode) * self.L * self.B if self.max_decode > 0 else 0
+        self.n_pages = n_compile_pages + n_link_pages + n_decode_pages
         self.pool = K.kvb_pool_create(self.n_pages)
         comp_pages = {}
         for c in chunks:
@@ -216,7 +221,11 @@ class LinkEngine:
         self.cu_rows = [torch.zeros(self.B + 1, dtype=torch.int32, device=dev) for _ in range(2)]
         self.dev_l = torch.zeros(max(self.T_sel, 1), dtype=torch.float32, device=dev)
         self.cksim = torch.zeros(max(self.T_sel, 1), dtype=torch.float32, device=dev)
-        self.slot_map = torch.zeros(nt, dtype=torch.int32, device=dev)
+        # per-layer page table of the link step: the slot of every token's K/V in
+        # that layer (reused slot, or the new slot of a recomputed row)
+        self.page_table = torch.zeros((self.L, nt), dtype=torch.int32, device=dev)
+        self.slot_map = self.page_table[0]  # the layer being run
+        self._pt_reuse_rows = set()         # layers skipped by the last step: their rows still to fill
         self.dst_slot = torch.zeros(rows_max, dtype=torch.int32, device=dev)
         self.ws_bytes = K.kvb_workspace_size(self.ctx, self.desc, rows_max, max(self.N, self.Nc), self.B)
         self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
@@ -342,6 +351,7 @@ class LinkEngine:
 
     # ------------------------------------------------------------------ link step
     def run_link(self, hook: Optional[Callable] = None):
+        self._pt_reuse_rows = set()
         self._tier_begin()
         if self.cfg.mode == "cacheslide":
             self._link_cacheslide(hook)
@@ -353,6 +363,7 @@ class LinkEngine:
         """One recompute layer for the given rows: slot map, Q/K/V + RoPE, fusion and
         scatter into new pages, attention over the spliced KV, O-proj + MLP."""
         c, sh, ds, W = self.ctx, self.sh, self.desc, self.model.layers[l - 1]
+        self.slot_map = self.page_table[l - 1]
         K.kvb_slot_map(c, sh, ds, self.B, self.N, T, cu_rows, rows, self.reuse_slot[l - 1], self.new_pages[l],
                        self.cu_pages[l], self.slot_map, self.dst_slot)
         K.kvb_qkv_proj(c, sh, ds, T, n_rows, rows, self.hidden, W["norm1"], W["w_qkv"], self.pos_l, self.q, self.k,
@@ -382,7 +393,9 @@ class LinkEngine:
         for l in range(2, self.L + 1):
             cur = self.cur
             if T == 0:
-                # no row left to recompute: this layer's new pages stay unused
+                # no row left to recompute: this layer's new pages stay unused and
+                # its page table is the reused slots (filled on demand)
+                self._pt_reuse_rows.add(l)
                 if hook:
                     hook(l, self)
                 continue
@@ -418,6 +431,118 @@ class LinkEngine:
             self._layer_rows(l, T, None, self.lego_sel, self.lego_cu, None, K.KVB_ALPHA_ONE, None, None, None)
             if hook:
                 hook(l, self)
+
+    # ------------------------------------------------------------------ page tables
+    def final_page_table(self) -> torch.Tensor:
+        """[L, N] slot of every token's K/V in each layer after the last link step."""
+        for l in sorted(self._pt_reuse_rows):
+            K.kvb_slot_map(self.ctx, self.sh, self.desc, self.B, self.N, 0, None, None, self.reuse_slot[l - 1], None,
+                           None, self.page_table[l - 1], None)
+        self._pt_reuse_rows = set()
+        return self.page_table
+
+    # ------------------------------------------------------------------ decode continuation
+    def decode_init(self, overwrite_first: bool = True, consume_cache: bool = False):
+        """Prepare decode steps after a link step (CacheSlide page, SLIDE: decode
+        writes its K/V first into the original slots of the tokens recomputed in
+        that layer, whose reused K/V the new pages superseded, and only then into
+        newly allocated pages).
+
+        Overwriting those slots changes the compile pages, so it needs either the
+        host tier (every link step reloads them) or consume_cache=True.  Slots of
+        chunk instances shared with other requests are never overwritten.
+        overwrite_first=False appends every decode token to new pages."""
+        if self.max_decode <= 0:
+            raise ValueError("the engine was built with max_decode=0")
+        if overwrite_first and self.cfg.reuse_tier != "host" and not consume_cache:
+            raise ValueError("overwrite-first decode rewrites the compile pages: use reuse_tier='host' or "
+                             "consume_cache=True")
+        B, L, md, dev = self.B, self.L, self.max_decode, self.device
+        for per_layer in getattr(self, "dec_pages", []):  # pages of an earlier decode run
+            for ids in per_layer:
+                if ids:
+                    K.kvb_pool_release(self.pool, ids)
+        pt = self.final_page_table().cpu().numpy()
+        cu = self.cu_tok_h
+        # decode token space: request b's prompt at dcu[b] .. dcu[b] + N_b, then its max_decode tokens
+        self.dec_cu = np.array([cu[b] + b * md for b in range(B)], dtype=np.int64)
+        Nd = self.N + B * md
+        g_of = np.concatenate([np.arange(cu[b], cu[b + 1]) + b * md for b in range(B)]) if self.N else np.zeros(0)
+        pt_dec = np.full((L, Nd), -1, dtype=np.int32)
+        pt_dec[:, g_of.astype(np.int64)] = pt
+        lo_dec = np.zeros(Nd, dtype=np.int32)
+        for b in range(B):
+            lo_dec[self.dec_cu[b]:self.dec_cu[b] + self.req_lens[b] + md] = self.dec_cu[b]
+        # overwritable slots per (layer, request): reused slots of the tokens the layer recomputed,
+        # in token order, on chunk instances this request alone uses
+        owners = {}
+        for b, r in enumerate(self.requests):
+            for c in r.chunks:
+                owners.setdefault(c.uid, set()).add(b)
+        own = np.zeros(self.N, dtype=bool)
+        for b, r in enumerate(self.requests):
+            g = cu[b]
+            for c in r.chunks:
+                own[g:g + len(c.tokens)] = len(owners[c.uid]) == 1
+                g += len(c.tokens)
+        self.dec_holes = [[None] * B for _ in range(L + 1)]
+        for l in range(1, L + 1):
+            moved = (pt[l - 1] != self.reuse_slot_h[l - 1]) & own
+            for b in range(B):
+                seg = slice(cu[b], cu[b + 1])
+                self.dec_holes[l][b] = (self.reuse_slot_h[l - 1][seg][moved[seg]].astype(np.int64).tolist()
+                                        if overwrite_first else [])
+        self.dec_pages = [[[] for _ in range(B)] for _ in range(L + 1)]
+        self.dec_t = 0
+        self.dec_overwrite_first = overwrite_first
+        self.pt_dec = _i32(pt_dec, dev)
+        self.lo_dec = _i32(lo_dec, dev)
+        self.dec_slots_h = np.full((L, B, md), -1, dtype=np.int64)  # slot of decode token t per layer, request
+        self.hidden_dec = torch.zeros((B, self.shape.d_model), dtype=self.tdtype, device=dev)
+
+    def _dec_slot(self, l: int, b: int, t: int) -> int:
+        holes = self.dec_holes[l][b]
+        if t < len(holes):
+            return holes[t]
+        j = t - len(holes)  # j-th appended token of this layer and request
+        pages = self.dec_pages[l][b]
+        while len(pages) <= j // PAGE:
+            pages.extend(K.kvb_pool_alloc(self.pool, 1))
+        return pages[j // PAGE] * PAGE + j % PAGE
+
+    def decode_step(self, tokens) -> torch.Tensor:
+        """One decode token per request (vocabulary ids `tokens`, one per request)
+        at position N_b + t: embed, then per layer QKV + RoPE, K/V into the slot
+        the placement gives, attention over the request's prompt (the link
+        step's page table) and earlier decode tokens, O-projection + MLP.
+        Returns the new tokens' hidden rows [B, d] after the last layer."""
+        B, L, t = self.B, self.L, self.dec_t
+        if t >= self.max_decode:
+            raise ValueError("max_decode tokens already decoded")
+        c, sh, ds, dev, m = self.ctx, self.sh, self.desc, self.device, self.model
+        rows = self.dec_cu + np.array(self.req_lens) + t            # decode-space ids of the new tokens
+        slots = np.array([[self._dec_slot(l, b, t) for b in range(B)] for l in range(1, L + 1)], dtype=np.int64)
+        self.dec_slots_h[:, :, t] = slots
+        pt = self.pt_dec
+        with torch.cuda.stream(self.stream):
+            pt[:, torch.as_tensor(rows, device=dev)] = _i32(slots, dev)
+        rows_d = _i32(rows, dev)
+        pos_d = _i32(np.array(self.req_lens) + t, dev)
+        tok_d = _i32(np.asarray(tokens, dtype=np.int64), dev)
+        slots_d = _i32(slots, dev)
+        K.kvb_embed(c, sh, ds, B, None, None, tok_d, self.shape.vocab, m.embedding, self.hidden_dec)
+        for l in range(1, L + 1):
+            W = m.layers[l - 1]
+            K.kvb_qkv_proj(c, sh, ds, B, None, None, self.hidden_dec, W["norm1"], W["w_qkv"], pos_d, self.q, self.k,
+                           self.v, self.ws, self.ws_bytes)
+            K.kvb_blend_scatter(c, sh, ds, B, None, None, self.k, self.v, self.k_pool, self.v_pool, self.n_pages,
+                                None, slots_d[l - 1], K.KVB_ALPHA_ONE, None, None, None)
+            K.kvb_sparse_query_attn(c, sh, ds, B, None, rows_d, self.lo_dec, self.q, self.k_pool, self.v_pool,
+                                    self.n_pages, pt[l - 1], self.scale, self.o, self.ws, self.ws_bytes)
+            K.kvb_mlp(c, sh, ds, B, None, None, self.o, W["w_o"], self.hidden_dec, W["norm2"], W["w_gate_up"],
+                      W["w_down"], self.ws, self.ws_bytes)
+        self.dec_t = t + 1
+        return self.hidden_dec
 
     # ------------------------------------------------------------------ results
     def selected(self, which: Optional[int] = None) -> List[np.ndarray]:
