@@ -300,6 +300,16 @@ attn_bf16_kernel(AttnArgs a) {
         if (X + 3 < nt) issue_slots(X + 3);
         if (X + 2 < nt) issue_kv(X + 2);
       }
+      // this half's V^T fragments, read now so the LDS latency hides under the softmax
+      uint2 vr[2][DT][2];
+#pragma unroll
+      for (int cc = 0; cc < 2; cc++)
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++) {
+          vr[cc][dt][0] = lds_read_tr16(vbs + (16 * (2 * kt + cc)) * ROWB + voff[dt]);
+          vr[cc][dt][1] = lds_read_tr16(vbs + (16 * (2 * kt + cc) + 8) * ROWB + voff[dt]);
+        }
+      __builtin_amdgcn_sched_barrier(0);
       // softmax over the query's 32 keys of this half: 16 here, 16 in lane ^ 32
       float sv[16];
 #pragma unroll
@@ -347,11 +357,9 @@ attn_bf16_kernel(AttnArgs a) {
       // dim 32 dt + l % 32, keys 16 c + 4 g2 + 0..3 (u = 0) and 16 c + 8 + 4 g2 + 0..3 (u = 1)
 #pragma unroll
       for (int cc = 0; cc < 2; cc++) {
-        const int c = 2 * kt + cc;
 #pragma unroll
         for (int dt = 0; dt < DT; dt++) {
-          const uint2 v0 = lds_read_tr16(vbs + (16 * c) * ROWB + voff[dt]);
-          const uint2 v1 = lds_read_tr16(vbs + (16 * c + 8) * ROWB + voff[dt]);
+          const uint2 v0 = vr[cc][dt][0], v1 = vr[cc][dt][1];
           const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
           oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, __builtin_bit_cast(bf16x8_t, pf[cc]), oacc[dt],
                                                              0, 0, 0);
