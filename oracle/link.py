@@ -7,15 +7,18 @@ prefilled on its own with positions starting from zero and its per-layer K/V
 are kept.  Link: the cached K/V of a request's chunks are spliced (token i of
 the request at global position i) and a subset of tokens is recomputed.
 
-Two ways of choosing that subset are implemented:
+Three ways of choosing that subset are implemented:
   * CacheSlide Weighted Correction Attention (CacheSlide page, "Method
     details" and Algorithm 2): layer 1 recomputes every token, then the k
     tokens with the largest key deviation are recomputed in layers 2..L and
     fused with the cached K/V; every four layers a cosine check retires and
     refills tokens;
   * EPIC LegoLink (EPIC page, section 4 "LegoLink"): a static set, the first k
-    tokens of every chunk except the first, recomputed in every layer, whose
-    K/V replace the cached ones.
+    tokens of every chunk except the first plus the uncached query tokens,
+    recomputed in every layer, whose K/V replace the cached ones;
+  * the CacheBlend baseline as the EPIC page describes it (section 3.2): layer 1
+    recomputes every token, the 15 % whose attention maps deviate most from the
+    cached ones are recomputed in layers 2..L and replace the cached K/V.
 "Fully recompute" and "Naive" (EPIC page, section 3.2) are the static-set
 cases S = everything and S = nothing.
 
@@ -79,18 +82,33 @@ def full_prefill(tokens: np.ndarray, shape, E: np.ndarray, W: Callable[[int], di
 
 
 def compile_chunks(chunks, shape, E, W) -> Dict[int, tuple]:
-    """uid -> (K list, V list) for every chunk instance, each prefilled alone."""
+    """uid -> (K list, V list) for every cached chunk instance, each prefilled alone.
+    A query chunk (the request's mutable tokens) has no compile step."""
     out = {}
     for c in chunks:
+        if not c.cached:
+            continue
         K, V, _ = full_prefill(c.tokens, shape, E, W, skip_last_mlp=True)
         out[c.uid] = (K, V)
     return out
 
 
-def splice(request, compiled: Dict[int, tuple], layer: int):
-    """Request's reuse K, V at 1-based `layer`: the chunks' cached rows concatenated."""
-    K = np.concatenate([compiled[c.uid][0][layer - 1] for c in request.chunks])
-    V = np.concatenate([compiled[c.uid][1][layer - 1] for c in request.chunks])
+def splice(request, compiled: Dict[int, tuple], layer: int, shape=None):
+    """Request's reuse K, V at 1-based `layer`: the chunks' cached rows concatenated.
+
+    Rows of an uncached query chunk are NaN: such tokens are recomputed in every
+    layer, so their cached rows must never be read (a NaN would show if they were)."""
+    def rows(c, i):
+        if c.cached:
+            return compiled[c.uid][i][layer - 1]
+        if shape is not None:
+            tail = (shape.n_kv_heads, shape.head_dim)
+        else:
+            tail = next(iter(compiled.values()))[i][layer - 1].shape[1:]
+        return np.full((len(c),) + tuple(tail), np.nan)
+
+    K = np.concatenate([rows(c, 0) for c in request.chunks])
+    V = np.concatenate([rows(c, 1) for c in request.chunks])
     return K, V
 
 
@@ -189,15 +207,53 @@ def wca_link(request, shape, E, W, compiled, k_cap: int, tau: float, period: int
     return state, outs
 
 
+# ---------------------------------------------------------------- CacheBlend-style selection
+
+def cacheblend_layer1(request, shape, E, W1: dict, reuse_K1: np.ndarray, k_cap: int):
+    """Layer 1 of the CacheBlend-style link (EPIC page, section 3.2): every token
+    recomputed at its spliced position (the KV written is the recomputed one),
+    then the attention-map deviation of every token against the cached keys
+    and the top-k of S = {dev > 0}.  Returns (state, outputs); alpha is 1 for
+    every token: the later layers' recomputed KV replace the cached KV."""
+    tokens = request.tokens
+    N = len(tokens)
+    pos = np.arange(N)
+    h = M.store(E[tokens], shape.dtype)
+    q, k, v = M.qkv(h, pos, W1, shape, blocks=chunk_blocks(request))
+    o = M.attention_rows_fast(q, pos, k, v, np.zeros(N, dtype=np.int64), shape)
+    h2 = M.post_attention(h, o, W1, shape)
+    dev = Sel.attention_map_deviation(q, k, reuse_K1, np.zeros(N, dtype=np.int64), shape)
+    ranking, S_k, cursor = Sel.top_k(dev, k_cap)
+    out = dict(q=q, k=k, v=v, o=o, h=h2.copy(), d=dev, ranking=ranking, S_k=S_k, cursor=cursor)
+    return WCAState(h=h2, alpha=np.ones(N), d=dev, ranking=ranking, cursor=cursor, S_k=S_k), out
+
+
+def cacheblend_link(request, shape, E, W, compiled, k_cap: int, keep: bool = True):
+    """CacheBlend-style link of one request: layer 1 as above, then layers 2..L
+    recompute the fixed set S_k (no refresh) and its KV replaces the cache."""
+    L = shape.n_layers
+    K1, _ = splice(request, compiled, 1)
+    state, out1 = cacheblend_layer1(request, shape, E, W(1), K1, k_cap)
+    outs = [out1]
+    for l in range(2, L + 1):
+        Kl, Vl = splice(request, compiled, l)
+        o = wca_layer(state, l, shape, W(l), Kl, Vl, tau=0.0, period=L + 1, n_layers=L, alpha_mode="one")
+        outs.append(o if keep else {k: o[k] for k in ("S", "h_rows", "S_next")})
+    return state, outs
+
+
 # ---------------------------------------------------------------- static sets
 
 def legolink_rows(request, k: int) -> np.ndarray:
-    """First min(k, len) tokens of every chunk except the first (EPIC page, section 4)."""
+    """LegoLink's static set (EPIC page, section 4): the first min(k, len) tokens
+    of every cached chunk except the first, plus every token of the request's
+    uncached query chunks (the user's mutable input, which has no cache)."""
     rows = []
-    for c, (s, e) in enumerate(chunk_blocks(request)):
-        if c == 0:
-            continue
-        rows.extend(range(s, s + min(k, e - s)))
+    for c, ((s, e), ch) in enumerate(zip(chunk_blocks(request), request.chunks)):
+        if not ch.cached:
+            rows.extend(range(s, e))
+        elif c > 0:
+            rows.extend(range(s, s + min(k, e - s)))
     return np.asarray(rows, dtype=np.int64)
 
 
@@ -211,7 +267,7 @@ def static_link(request, S: np.ndarray, shape, E, W, compiled, keep: bool = True
     outs = []
     for l in range(1, shape.n_layers + 1):
         Wl = W(l)
-        Kr, Vr = splice(request, compiled, l)
+        Kr, Vr = splice(request, compiled, l, shape)
         K_log = np.array(Kr, dtype=np.float64, copy=True)
         V_log = np.array(Vr, dtype=np.float64, copy=True)
         if S.size:

@@ -76,15 +76,20 @@ def compile_plan(chunks, n_layers: int, alloc: PageAllocator, page_size: int = 1
     """pages[uid][layer-1] for every compiled chunk instance, in compile order."""
     plan = {}
     for c in chunks:
-        plan[c.uid] = [alloc.alloc(n_pages_for(len(c), page_size)) for _ in range(n_layers)]
+        if c.cached:
+            plan[c.uid] = [alloc.alloc(n_pages_for(len(c), page_size)) for _ in range(n_layers)]
     return plan
 
 
 def reuse_slots(request, plan, layer: int, page_size: int = 16) -> np.ndarray:
-    """Slot of each spliced token's compile-step KV at 1-based `layer`: int64 [N]."""
+    """Slot of each spliced token's compile-step KV at 1-based `layer`: int64 [N];
+    -1 for the tokens of an uncached query chunk."""
     out = []
     for c in request.chunks:
-        out.append(slot_of(plan[c.uid][layer - 1], np.arange(len(c)), page_size))
+        if c.cached:
+            out.append(slot_of(plan[c.uid][layer - 1], np.arange(len(c)), page_size))
+        else:
+            out.append(np.full(len(c), -1, dtype=np.int64))
     return np.concatenate(out)
 
 

@@ -20,6 +20,18 @@ Readings (the pages leave these open):
     entries of the layer-1 ranking (d only exists at layer 1), so retired
     tokens never return; if the ranking runs out S_k shrinks;
   * a KV head whose two vectors are both zero has cosine 1, one zero vector 0.
+
+CacheBlend-style selection (EPIC page, section 3.2, the CacheBlend baseline:
+layer 1 recomputes every token, the attention maps computed with the old
+(cached) and the new (recomputed) KV are compared, and the tokens whose maps
+differ most, 15 %, are recomputed in the later layers):
+  * a token's deviation is the L1 distance between its two attention rows,
+    averaged over the query heads (reading: the page names no distance; L1 is
+    the plain distance between two probability rows and lies in [0, 2]);
+  * both rows use the layer-1 queries recomputed at the spliced positions
+    (the cache holds no queries), the causal key range of the token, and the
+    model's 1/sqrt(hd) scale; the selection then follows the same ranking,
+    S = {dev > 0} and top-k rule as above.
 """
 from __future__ import annotations
 
@@ -102,3 +114,35 @@ def refresh(S_k: List[int], c: np.ndarray, tau: float, ranking: List[int], curso
     n_new = min(len(retire), len(ranking) - cursor)
     refill = ranking[cursor: cursor + n_new]
     return sorted(keep + refill), cursor + n_new, retire
+
+
+def attention_map_deviation(q: np.ndarray, k_new: np.ndarray, k_old: np.ndarray, lo: np.ndarray,
+                            shape) -> np.ndarray:
+    """Per-token attention-map deviation of the CacheBlend-style selection.
+
+    q [N, Hq, hd] layer-1 queries at the spliced positions; k_new, k_old
+    [N, Hkv, hd] the recomputed and the cached (spliced) layer-1 keys; lo [N]
+    the first key a token may see.  For token i and query head h (KV head
+    h // (Hq / Hkv)) the two attention rows are softmax over keys j in
+    lo_i..i of q_i . k_j / sqrt(hd), once with k_new and once with k_old;
+    the result is the mean over h of the L1 distance of the two rows, float64 [N].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k_new = np.asarray(k_new, dtype=np.float64)
+    k_old = np.asarray(k_old, dtype=np.float64)
+    N, Hq, hd = q.shape
+    G = Hq // k_new.shape[1]
+    scale = 1.0 / np.sqrt(hd)
+    dev = np.zeros(N)
+    for i in range(N):
+        j0 = int(lo[i])
+        total = 0.0
+        for h in range(Hq):
+            rows = []
+            for K in (k_new, k_old):
+                s = K[j0:i + 1, h // G] @ q[i, h] * scale
+                e = np.exp(s - s.max())
+                rows.append(e / e.sum())
+            total += np.abs(rows[0] - rows[1]).sum()
+        dev[i] = total / Hq
+    return dev

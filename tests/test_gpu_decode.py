@@ -70,7 +70,7 @@ def expected_holes(eng, pt, l, b):
     out, g = [], int(eng.cu_tok_h[b])
     for c in eng.requests[b].chunks:
         for j in range(len(c.tokens)):
-            if len(owners[c.uid]) == 1 and pt[l - 1][g + j] != eng.reuse_slot_h[l - 1][g + j]:
+            if c.cached and len(owners[c.uid]) == 1 and pt[l - 1][g + j] != eng.reuse_slot_h[l - 1][g + j]:
                 out.append(int(eng.reuse_slot_h[l - 1][g + j]))
         g += len(c.tokens)
     return out
@@ -167,6 +167,19 @@ def test_decode_bf16_legolink_consumes_cache():
     w = wl.small_bf16(n_layers=4, mode="legolink")
     eng, E, layers, pt, toks, hs, first = run(w, "hbm", True, n_dec=3, consume=True)
     check_decode(eng, E, layers, pt, toks, hs, True)
+    eng.close()
+
+
+def test_decode_legolink_query_suffix_has_no_slot_to_overwrite():
+    """An uncached query has no reused slot: decode overwrites only the
+    superseded slots of recomputed cached tokens, then appends."""
+    w = wl.tiny(n_layers=2, mode="legolink", lens=(96, 40, 70), query_len=24)
+    n_dec = 80   # more than the cached tokens LegoLink recomputes (32 + 32): some are appended
+    eng, E, layers, pt, toks, hs, first = run(w, "host", True, n_dec=n_dec)
+    check_decode(eng, E, layers, pt, toks, hs, True)
+    assert np.all(eng.dec_slots_h >= 0)
+    for l in range(1, w.shape.n_layers + 1):
+        assert len(eng.dec_holes[l][0]) == 64
     eng.close()
 
 

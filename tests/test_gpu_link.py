@@ -238,7 +238,10 @@ def test_small_bf16_cacheslide_teacher_forced():
 
 
 @pytest.mark.parametrize("make", [lambda: wl.tiny(n_layers=3, mode="legolink", lens=(96, 40, 130, 20, 64)),
-                                  lambda: wl.small_bf16(n_layers=4, mode="legolink")])
+                                  lambda: wl.small_bf16(n_layers=4, mode="legolink"),
+                                  lambda: wl.tiny(n_layers=3, mode="legolink", lens=(96, 40, 130), query_len=45),
+                                  lambda: wl.small_bf16(n_layers=4, mode="legolink", query_len=77)],
+                         ids=["tiny", "small-bf16", "tiny-query", "small-bf16-query"])
 def test_legolink_layers(make):
     w = make()
     w.lego_k = 32
@@ -296,6 +299,13 @@ def test_link_is_deterministic_and_repeatable():
         else:
             assert torch.equal(x, y)
     eng.close()
+
+
+def test_query_chunk_needs_legolink():
+    """A selection that may leave a query token out is refused: it has no cache."""
+    w = wl.tiny(n_layers=2, query_len=8)
+    with pytest.raises(ValueError):
+        build_engine(w)
 
 
 @pytest.mark.parametrize("exact", [True, False])

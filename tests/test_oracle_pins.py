@@ -184,6 +184,133 @@ def test_compile_equals_prefill_of_each_chunk():
             assert np.allclose(compiled[c.uid][1][l], Vr[l], rtol=1e-10, atol=1e-10)
 
 
+# ------------------------------------------------------------ LegoLink with an uncached query suffix
+
+def test_legolink_rows_with_query_worked_example():
+    """EPIC section 4: k' = the first k tokens of each chunk (not the first) plus
+    the user's query tokens.  Chunks [5, 3, 40] then a 7-token query, k = 4."""
+    ch = lambda uid, kind, n: wl.Chunk(uid=uid, kind=kind, tokens=np.zeros(n, dtype=np.int32))
+    req = wl.Request([ch(0, "fixed", 5), ch(1, "dynamic", 3), ch(2, "fixed", 40), ch(3, "query", 7)])
+    assert OL.legolink_rows(req, 4).tolist() == [5, 6, 7, 8, 9, 10, 11] + list(range(48, 55))
+    assert OL.legolink_rows(req, 0).tolist() == list(range(48, 55))
+    only_query = wl.Request([ch(9, "query", 6)])
+    assert OL.legolink_rows(only_query, 32).tolist() == list(range(6))
+    plan = OP.compile_plan([c for c in req.chunks if c.cached], 1, OP.PageAllocator(16))
+    assert set(plan) == {0, 1, 2}
+    rs = OP.reuse_slots(req, plan, 1)
+    assert np.all(rs[48:] == -1) and np.all(rs[:48] >= 0)
+
+
+def test_legolink_query_after_first_chunk_is_prefill():
+    """The first chunk is compiled at positions 0.. already, so its cache is exact;
+    a query after it, recomputed in every layer, then matches plain prefill of the
+    whole prompt on the query rows (library decoder), and the query's cached rows
+    (NaN, there is none) are never read."""
+    w = tiny64(n_layers=2, lens=(48,), query_len=20, mode="legolink")
+    E, W = oracle_inputs(w)
+    req = w.requests[0]
+    assert [c.cached for c in req.chunks] == [True, False]
+    compiled = OL.compile_chunks(req.chunks, w.shape, E, W)
+    assert set(compiled) == {req.chunks[0].uid}
+    S = OL.legolink_rows(req, 32)
+    assert S.tolist() == list(range(48, 68))
+    hS, outs = OL.static_link(req, S, w.shape, E, W, compiled)
+    _, _, hr = torch_prefill(req.tokens, w.shape, E, W, 2)
+    assert np.all(np.isfinite(hS))
+    assert np.allclose(hS, hr[48:], rtol=1e-10, atol=1e-10)
+    Kr, _ = OL.splice(req, compiled, 1, w.shape)
+    assert np.all(np.isnan(Kr[48:])) and np.all(np.isfinite(outs[0]["K_log"]))
+
+
+# ------------------------------------------------------------ CacheBlend-style attention-map deviation
+
+def _amd_shape(Hq=4, Hkv=2, hd=16):
+    return wl.ModelShape(n_layers=1, d_model=Hq * hd, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=hd, ffn=32,
+                         dtype="fp64")
+
+
+def test_attention_map_deviation_two_keys_closed_form(rng):
+    """With two visible keys an attention row is (sigmoid(a), 1 - sigmoid(a)),
+    a = (s_0 - s_1); the L1 distance of two such rows is 2 |sigmoid(a) - sigmoid(b)|.
+    A token that sees one key has the row (1) under both: deviation 0."""
+    from scipy.special import expit
+    shape = _amd_shape()
+    q = rng.standard_normal((2, 4, 16))
+    kn = rng.standard_normal((2, 2, 16))
+    ko = rng.standard_normal((2, 2, 16))
+    dev = OS.attention_map_deviation(q, kn, ko, np.zeros(2, int), shape)
+    assert dev[0] == 0.0
+    ref = 0.0
+    for h in range(4):
+        a = (kn[0, h // 2] - kn[1, h // 2]) @ q[1, h] / 4.0
+        b = (ko[0, h // 2] - ko[1, h // 2]) @ q[1, h] / 4.0
+        ref += 2.0 * abs(expit(a) - expit(b))
+    assert np.isclose(dev[1], ref / 4.0, rtol=1e-12, atol=1e-15)
+
+
+def test_attention_map_deviation_matches_library_maps(rng):
+    """Brute force with library routines: full masked score matrices per head,
+    torch.softmax, L1 over each row, mean over heads (GQA 3, per-token key
+    lower bounds as in a batch of two requests)."""
+    Hq, Hkv, hd, N = 6, 2, 8, 37
+    shape = _amd_shape(Hq, Hkv, hd)
+    q = rng.standard_normal((N, Hq, hd))
+    kn = rng.standard_normal((N, Hkv, hd))
+    ko = kn + 0.3 * rng.standard_normal((N, Hkv, hd))
+    lo = np.where(np.arange(N) < 20, 0, 20)
+    dev = OS.attention_map_deviation(q, kn, ko, lo, shape)
+    idx = torch.arange(N)
+    allowed = (idx[None, :] <= idx[:, None]) & (idx[None, :] >= torch.as_tensor(lo)[:, None])
+    maps = []
+    for K in (kn, ko):
+        Kr = torch.tensor(K).repeat_interleave(Hq // Hkv, dim=1)                 # [N, Hq, hd]
+        S = torch.einsum("ihd,jhd->hij", torch.tensor(q), Kr) / np.sqrt(hd)
+        maps.append(torch.softmax(S.masked_fill(~allowed, float("-inf")), dim=-1))
+    ref = (maps[0] - maps[1]).abs().sum(-1).mean(0).numpy()
+    assert np.allclose(dev, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_attention_map_deviation_invariants(rng):
+    shape = _amd_shape()
+    N = 25
+    q = rng.standard_normal((N, 4, 16))
+    kn = rng.standard_normal((N, 2, 16))
+    ko = rng.standard_normal((N, 2, 16))
+    lo = np.zeros(N, int)
+    dev = OS.attention_map_deviation(q, kn, ko, lo, shape)
+    assert np.all(dev >= 0) and np.all(dev <= 2.0)
+    assert np.array_equal(OS.attention_map_deviation(q, kn, kn, lo, shape), np.zeros(N))
+    assert np.allclose(OS.attention_map_deviation(q, ko, kn, lo, shape), dev, rtol=1e-13)
+    # causal: keys after token i do not change its deviation
+    ko2 = ko.copy()
+    ko2[15:] += 5.0
+    dev2 = OS.attention_map_deviation(q, kn, ko2, lo, shape)
+    assert np.array_equal(dev2[:15], dev[:15]) and not np.allclose(dev2[15:], dev[15:])
+    # identical keys up to token i: zero up to i, whatever follows
+    ko3 = kn.copy()
+    ko3[10:] = ko[10:]
+    assert np.all(OS.attention_map_deviation(q, kn, ko3, lo, shape)[:10] == 0.0)
+
+
+def test_cacheblend_select_all_is_prefill():
+    """Chunk 0 is cached at its own positions, so its tokens' maps agree exactly
+    (deviation 0) and they are never selected; selecting every other token and
+    replacing its KV in every layer reproduces full prefill (library decoder)."""
+    w = tiny64(n_layers=3, lens=(40, 24, 36), mode="cacheblend")
+    E, W = oracle_inputs(w)
+    req = w.requests[0]
+    compiled = OL.compile_chunks(w.compile_chunks, w.shape, E, W)
+    st, outs = OL.cacheblend_link(req, w.shape, E, W, compiled, k_cap=req.n_tokens)
+    assert np.all(outs[0]["d"][:40] == 0.0) and np.all(outs[0]["d"][40:] > 0.0)
+    assert st.S_k == list(range(40, 100))
+    _, _, hr = torch_prefill(req.tokens, w.shape, E, W, 3)
+    assert np.allclose(st.h[40:], hr[40:], rtol=1e-10, atol=1e-10)
+    # a cap below |S| keeps the ranking's top entries, ascending
+    st2, outs2 = OL.cacheblend_link(req, w.shape, E, W, compiled, k_cap=9, keep=False)
+    d = outs2[0]["d"]
+    assert st2.S_k == sorted(sorted(range(100), key=lambda i: (-d[i], i))[:9])
+
+
 # ------------------------------------------------------------ naive / identical-reuse special cases
 
 def test_naive_link_keeps_cache_bitwise():

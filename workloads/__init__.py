@@ -67,11 +67,16 @@ class ModelShape:
 @dataclass
 class Chunk:
     uid: int                     # identity of the compiled instance (shared fixed chunks share it)
-    kind: str                    # "fixed" or "dynamic"
+    kind: str                    # "fixed", "dynamic", or "query" (mutable tokens that are never compiled)
     tokens: np.ndarray           # int32 [len]
 
     def __len__(self) -> int:
         return int(self.tokens.shape[0])
+
+    @property
+    def cached(self) -> bool:
+        """True when the chunk has compile-step KV to reuse."""
+        return self.kind != "query"
 
 
 @dataclass
@@ -99,9 +104,10 @@ class Request:
 class Workload:
     name: str
     shape: ModelShape
-    mode: str                    # "cacheslide" or "legolink"
+    mode: str                    # "cacheslide", "legolink" or "cacheblend"
     requests: List[Request]
-    ratio: float = 0.26          # CacheSlide top-k ratio
+    ratio: float = 0.26          # top-k ratio (CacheSlide; the CacheBlend-style selection uses cb_ratio)
+    cb_ratio: float = 0.15       # CacheBlend-style selection ratio
     tau: float = 0.12            # CKSim threshold
     period: int = 4              # refresh every `period` layers
     lego_k: int = 32             # LegoLink first-k per chunk
@@ -115,7 +121,7 @@ class Workload:
         seen, out = set(), []
         for req in self.requests:
             for c in req.chunks:
-                if c.uid not in seen:
+                if c.cached and c.uid not in seen:
                     seen.add(c.uid)
                     out.append(c)
         return out
@@ -155,9 +161,14 @@ def alternating_kinds(n: int) -> List[str]:
     return ["fixed" if i % 2 == 0 else "dynamic" for i in range(n)]
 
 
-def _single_request(seed: int, lens: List[int]) -> Request:
+def _single_request(seed: int, lens: List[int], query_len: int = 0) -> Request:
+    """Alternating fixed / dynamic chunks, then (query_len > 0) an uncached query suffix."""
     kinds = alternating_kinds(len(lens))
-    return Request([Chunk(uid=i, kind=kinds[i], tokens=chunk_tokens(seed, i, n)) for i, n in enumerate(lens)])
+    chunks = [Chunk(uid=i, kind=kinds[i], tokens=chunk_tokens(seed, i, n)) for i, n in enumerate(lens)]
+    if query_len > 0:
+        u = len(lens)
+        chunks.append(Chunk(uid=u, kind="query", tokens=chunk_tokens(seed, u, query_len)))
+    return Request(chunks)
 
 
 def gen_normal(shape, std: float, key: int, device: str = "cpu", dtype: str = "fp32"):
@@ -206,19 +217,21 @@ LLAMA70 = ModelShape(n_layers=80, d_model=8192, n_q_heads=64, n_kv_heads=8, head
 
 
 def tiny(seed: int = 0, n_layers: int = 2, lens=(128, 96, 160, 128), mode: str = "cacheslide",
-         dtype: str = "fp32", **kw) -> Workload:
+         dtype: str = "fp32", query_len: int = 0, **kw) -> Workload:
     """Tiny decoder: 4 chunks [fixed 128, dynamic 96, fixed 160, dynamic 128], fp32."""
     shape = ModelShape(**{**TINY.__dict__, "n_layers": n_layers, "dtype": dtype})
-    return Workload(f"tiny-{n_layers}L", shape, mode, [_single_request(seed, list(lens))], seed=seed, **kw)
+    return Workload(f"tiny-{n_layers}L", shape, mode, [_single_request(seed, list(lens), query_len)], seed=seed,
+                    **kw)
 
 
 def small_bf16(seed: int = 0, n_layers: int = 8, lens=(192, 320, 256, 288), mode: str = "cacheslide",
-               head_dim: int = 128, **kw) -> Workload:
+               head_dim: int = 128, query_len: int = 0, **kw) -> Workload:
     """A small bf16 stack with the large configs' head geometry (GQA 4, hd 128),
     sized so that the oracle finishes in seconds while kernels still span several tiles."""
     shape = ModelShape(n_layers=n_layers, d_model=512, n_q_heads=8, n_kv_heads=2, head_dim=head_dim,
                        ffn=1536, dtype="bf16")
-    return Workload(f"small-bf16-{n_layers}L", shape, mode, [_single_request(seed, list(lens))], seed=seed, **kw)
+    return Workload(f"small-bf16-{n_layers}L", shape, mode, [_single_request(seed, list(lens), query_len)],
+                    seed=seed, **kw)
 
 
 def mistral_cacheslide(seed: int = 0, n_layers: int = 32) -> Workload:
