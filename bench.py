@@ -41,6 +41,7 @@ def parse():
     ap.add_argument("--no-tier", action="store_true", help="skip the host-tier (reused KV in pinned host memory) leg")
     ap.add_argument("--no-compile", action="store_true", help="skip timing the compile step")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode continuation leg")
+    ap.add_argument("--no-cacheblend", action="store_true", help="skip the CacheBlend-style selection leg")
     ap.add_argument("--profile-only", action="store_true", help="warmup + timed steps only (for rocprofv3)")
     return ap.parse_args()
 
@@ -196,7 +197,7 @@ def tier_host(eng, args, st, n_selected):
     # bytes one step loads: every layer's reused pages (layer 1 of CacheSlide: keys only)
     page_b = eng.k_pool[0].numel() * eng.k_pool.element_size()
     layers = list(range(1, eng.L + 1))
-    nbytes = sum(len(eng.layer_reuse_pages[l]) * page_b * (1 if (l == 1 and cfg.mode == "cacheslide") else 2)
+    nbytes = sum(len(eng.layer_reuse_pages[l]) * page_b * (1 if (l == 1 and cfg.mode != "legolink") else 2)
                  for l in layers)
 
     def copies_only():
@@ -211,6 +212,51 @@ def tier_host(eng, args, st, n_selected):
             "h2d_GBps": nbytes / (copy_ms * 1e-3) / 1e9,
             "note": "reused KV in pinned host memory, each layer's pages copied host-to-device during the step "
                     "(layers left with no rows load nothing); median of the timed steps"}
+
+
+def cacheblend_leg(w, model, args, dev):
+    """The same request linked with the CacheBlend-style selection (layer 1 in
+    full, attention-map deviation, top 15 %, later layers replace the cached
+    K/V): its own engine and compile pages on the same weights, timed with HIP
+    events on its stream; the attention-map kernel's share with its algorithmic
+    FLOPs (both maps of every token over its visible keys)."""
+    import numpy as np
+    import torch
+
+    from selective_kv_cache_amd import _lib as K
+    from selective_kv_cache_amd.link import LinkConfig, LinkEngine
+
+    s = w.shape
+    cfg = LinkConfig(mode="cacheblend", cb_ratio=w.cb_ratio)
+    eng = LinkEngine(model, w.requests, cfg, device=dev)
+    eng.run_compile()
+    for _ in range(max(args.warmup, 1)):
+        eng.run_link()
+    st = eng.stream
+    K.kvb_timing_enable(eng.ctx, "attnmap")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(st)
+        eng.run_link()
+        b.record(st)
+    torch.cuda.synchronize()
+    t = K.kvb_timing_read(eng.ctx)
+    K.kvb_timing_enable(eng.ctx, None)
+    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    n_sel = len(eng.selected()[0]) if eng.B == 1 else int(eng.cu_rows[0][-1])
+    pos_sum = float(sum(n * (n + 1) / 2 for n in eng.req_lens))
+    flops = 2 * 2.0 * s.n_q_heads * s.head_dim * pos_sum
+    amap = t.get("attnmap", {"ms": float("nan"), "count": 1})
+    amap_ms = amap["ms"] / amap["count"]
+    tf = flops / (amap_ms * 1e-3) / 1e12
+    out = {"ms_per_step": ms, "selected_tokens_per_s": n_sel / (ms * 1e-3), "selected": n_sel,
+           "ratio": w.cb_ratio, "attnmap_ms": amap_ms, "attnmap_algorithmic_tflop": flops / 1e12,
+           "attnmap_tflops": tf, "attnmap_mfma_frac": tf / PEAK_BF16_TFLOPS if s.dtype == "bf16" else None,
+           "note": "CacheBlend-style selection on the same request; median of the timed steps; the attention-map "
+                   "kernel computes every score twice (two passes), its rate counts each score once"}
+    eng.close()
+    return out
 
 
 def main():
@@ -378,6 +424,8 @@ def main():
         out["compile_step"] = compile_step(eng, args, st, s)
     if not args.no_tier:
         out["tier_host"] = tier_host(eng, args, st, n_selected)
+    if not args.no_cacheblend and cfg.mode == "cacheslide":
+        out["cacheblend"] = cacheblend_leg(w, eng.model, args, dev)
     if not args.no_cpu_baseline and cfg.mode == "cacheslide":
         try:
             step_flops = sum(work[k] for k, b in BOUND.items() if b == "mfma")

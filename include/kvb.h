@@ -258,6 +258,39 @@ kvb_status kvb_deviation_topk(kvb_ctx* ctx, void* stream, const kvb_model_desc* 
                               int32_t* s_count, int32_t* sel, int32_t* cu_rows, int32_t* cursor,
                               void* ws, size_t ws_bytes);
 
+/* Top-k selection from a per-token score already computed (the ranking, S and
+ * S_k rules of kvb_deviation_topk, for a selection whose score is not the key
+ * deviation, e.g. kvb_attnmap_deviation).  d [n_tok] float (>= 0) is read
+ * only; every other argument and the results are as in kvb_deviation_topk.
+ * Needs workspace.  Results are bitwise deterministic. */
+kvb_status kvb_topk(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t B,
+                    int32_t n_tok, const int32_t* cu_tok, const float* d, const int32_t* k_cap,
+                    int32_t* ranking, int32_t* s_count, int32_t* sel, int32_t* cu_rows,
+                    int32_t* cursor, void* ws, size_t ws_bytes);
+
+/* Attention-map deviation of the CacheBlend-style selection (EPIC page,
+ * section 3.2, the CacheBlend baseline: after layer 1 is recomputed for every
+ * token, each token's attention map under the cached keys is compared with
+ * its map under the recomputed keys; the tokens that differ most are
+ * recomputed in the later layers).  For every token g:
+ *   dev[g] = (1 / Hq) sum_h sum_{j = tok_lo[g] .. g} |Pn[h,g,j] - Po[h,g,j]|
+ *   Pn[h,g,:] = softmax_j(scale * q[g,h] . k_rec[j, h / G])
+ *   Po[h,g,:] = softmax_j(scale * q[g,h] . key at slot reuse_slot[j] of k_pool, head h / G)
+ * with G = Hq / Hkv, i.e. the L1 distance of the two attention rows, mean over
+ * query heads, in [0, 2].  q [n_tok, Hq, hd] and k_rec [n_tok, Hkv, hd] are
+ * token-indexed (layer 1 recomputes every token); k_pool [n_pages, Hkv, 16,
+ * hd]; tok_lo, reuse_slot device int32 [n_tok]; dev float [n_tok].  A key
+ * whose reuse slot is outside the pool is left out of both maps; a token with
+ * no visible key gets 0.  bf16 needs n_q_heads / n_kv_heads to be a power of
+ * two up to 32 and workspace (kvb_workspace_size for max_tokens >= n_tok);
+ * fp32 needs n_q_heads <= 256 and no workspace.  Results are bitwise
+ * deterministic. */
+kvb_status kvb_attnmap_deviation(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc,
+                                 int32_t n_tok, const int32_t* tok_lo, const void* q,
+                                 const void* k_rec, const void* k_pool, int32_t n_pages,
+                                 const int32_t* reuse_slot, float scale, float* dev, void* ws,
+                                 size_t ws_bytes);
+
 /* Similarity-gated refresh (CacheSlide page, Algorithm 2, every four layers:
  * a token of S_k whose CKSim is below tau leaves S_k and S, and the token of
  * S \ S_k with the largest deviation joins).  Works on a snapshot: for

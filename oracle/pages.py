@@ -17,6 +17,7 @@ Readings taken where the pages are silent:
       CacheSlide: N_r pages' worth at layer 1 (full recompute), and
                   floor(ratio * N_r) tokens' worth at every later layer
                   (the selection capacity, known before any kernel runs);
+                  the CacheBlend-style selection the same with its ratio;
       LegoLink:   |S_r| tokens' worth at every layer;
   * the j-th selected token (ascending token index) of a layer goes to slot
     page[j // 16] * 16 + j % 16 of that layer's new pages.
@@ -65,7 +66,7 @@ def slot_of(pages: List[int], j, page_size: int = 16):
 
 def capacity(workload_mode: str, n_tok: int, ratio: float, lego_rows: int, layer: int) -> int:
     """Tokens' worth of new pages a request gets at 1-based `layer` of the link step."""
-    if workload_mode == "cacheslide":
+    if workload_mode in ("cacheslide", "cacheblend"):
         return n_tok if layer == 1 else int(np.floor(ratio * n_tok))
     if workload_mode == "legolink":
         return lego_rows

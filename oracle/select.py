@@ -117,7 +117,7 @@ def refresh(S_k: List[int], c: np.ndarray, tau: float, ranking: List[int], curso
 
 
 def attention_map_deviation(q: np.ndarray, k_new: np.ndarray, k_old: np.ndarray, lo: np.ndarray,
-                            shape) -> np.ndarray:
+                            shape, rows=None) -> np.ndarray:
     """Per-token attention-map deviation of the CacheBlend-style selection.
 
     q [N, Hq, hd] layer-1 queries at the spliced positions; k_new, k_old
@@ -125,7 +125,8 @@ def attention_map_deviation(q: np.ndarray, k_new: np.ndarray, k_old: np.ndarray,
     the first key a token may see.  For token i and query head h (KV head
     h // (Hq / Hkv)) the two attention rows are softmax over keys j in
     lo_i..i of q_i . k_j / sqrt(hd), once with k_new and once with k_old;
-    the result is the mean over h of the L1 distance of the two rows, float64 [N].
+    the result is the mean over h of the L1 distance of the two rows, float64 [N]
+    (or, with `rows`, for those tokens only, in that order).
     """
     q = np.asarray(q, dtype=np.float64)
     k_new = np.asarray(k_new, dtype=np.float64)
@@ -133,8 +134,9 @@ def attention_map_deviation(q: np.ndarray, k_new: np.ndarray, k_old: np.ndarray,
     N, Hq, hd = q.shape
     G = Hq // k_new.shape[1]
     scale = 1.0 / np.sqrt(hd)
-    dev = np.zeros(N)
-    for i in range(N):
+    rows = range(N) if rows is None else [int(i) for i in rows]
+    dev = np.zeros(len(rows))
+    for t, i in enumerate(rows):
         j0 = int(lo[i])
         total = 0.0
         for h in range(Hq):
@@ -144,5 +146,5 @@ def attention_map_deviation(q: np.ndarray, k_new: np.ndarray, k_old: np.ndarray,
                 e = np.exp(s - s.max())
                 rows.append(e / e.sum())
             total += np.abs(rows[0] - rows[1]).sum()
-        dev[i] = total / Hq
+        dev[t] = total / Hq
     return dev

@@ -61,6 +61,8 @@ _SIGS = {
     "kvb_sparse_query_attn": ([P, P, P, I, P, P, P, P, P, P, I, P, c_float, P, P, c_size_t], I),
     "kvb_mlp": ([P, P, P, I, P, P, P, P, P, P, P, P, P, c_size_t], I),
     "kvb_deviation_topk": ([P, P, P, I, I, P, P, P, I, P, P, P, P, P, P, P, P, P, P, c_size_t], I),
+    "kvb_topk": ([P, P, P, I, I, P, P, P, P, P, P, P, P, P, c_size_t], I),
+    "kvb_attnmap_deviation": ([P, P, P, I, P, P, P, P, I, P, c_float, P, P, c_size_t], I),
     "kvb_cosine_refresh": ([P, P, P, I, I, P, I, P, P, P, c_float, I, P, P, P, P, P, P, c_size_t], I),
     "kvb_slot_map": ([P, P, P, I, I, I, P, P, P, P, P, P, P], I),
 }
@@ -244,6 +246,17 @@ def kvb_deviation_topk(ctx, stream, desc, B, n_tok, cu_tok, k_rec, k_pool, n_pag
                        ranking, s_count, sel, cu_rows, cursor, ws, ws_bytes):
     _call("kvb_deviation_topk", ctx, stream, desc, B, n_tok, cu_tok, k_rec, k_pool, n_pages,
           reuse_slot, k_cap, d, alpha, ranking, s_count, sel, cu_rows, cursor, ws, ws_bytes)
+
+
+def kvb_topk(ctx, stream, desc, B, n_tok, cu_tok, d, k_cap, ranking, s_count, sel, cu_rows, cursor, ws, ws_bytes):
+    _call("kvb_topk", ctx, stream, desc, B, n_tok, cu_tok, d, k_cap, ranking, s_count, sel, cu_rows, cursor, ws,
+          ws_bytes)
+
+
+def kvb_attnmap_deviation(ctx, stream, desc, n_tok, tok_lo, q, k_rec, k_pool, n_pages, reuse_slot, scale, dev, ws,
+                          ws_bytes):
+    _call("kvb_attnmap_deviation", ctx, stream, desc, n_tok, tok_lo, q, k_rec, k_pool, n_pages, reuse_slot,
+          float(scale), dev, ws, ws_bytes)
 
 
 def kvb_cosine_refresh(ctx, stream, desc, B, n_tok, cu_tok, T_max, cu_rows_in, sel_in, cksim, tau, rule, ranking,

@@ -68,6 +68,7 @@ size_t ws_qkv_bytes(const kvb_model_desc* d, int32_t max_rows);
 size_t ws_topk_bytes(int32_t max_tokens, int32_t max_requests);
 size_t ws_refresh_bytes(int32_t max_tokens, int32_t max_requests);
 size_t ws_attn_bytes(const kvb_model_desc* d, int32_t max_rows, int n_cu);
+size_t ws_attnmap_bytes(const kvb_model_desc* d, int32_t max_tokens);
 
 }  // namespace kvb
 

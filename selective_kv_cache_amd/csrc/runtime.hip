@@ -226,6 +226,7 @@ kvb_status kvb_workspace_size(kvb_ctx* ctx, const kvb_model_desc* desc, int32_t 
   b = std::max(b, ws_topk_bytes(max_tokens, max_requests));
   b = std::max(b, ws_refresh_bytes(max_tokens, max_requests));
   b = std::max(b, ws_attn_bytes(desc, max_rows, reinterpret_cast<Ctx*>(ctx)->n_cu));
+  b = std::max(b, ws_attnmap_bytes(desc, max_tokens));
   *bytes = b;
   return KVB_OK;
 }

@@ -222,9 +222,56 @@ static TopkWs topk_ws(void* ws, int n_tok) {
   return w;
 }
 
+// sort, rank and compact of the per-request top-k by d (d already written)
+static kvb_status launch_topk(hipStream_t st, int B, int n_tok, const int32_t* cu_tok, const float* d,
+                              const int32_t* k_cap, int32_t* ranking, int32_t* s_count, int32_t* sel,
+                              int32_t* cu_rows, int32_t* cursor, void* ws) {
+  TopkWs w = topk_ws(ws, n_tok);
+  if (n_tok > 0) {
+    const int n_chunks = n_tok / CHUNK + B;  // >= sum over requests of cdiv(N_b, CHUNK)
+    {
+      LaunchTimer lt(st, "topk_sort");
+      chunk_sort_kernel<<<n_chunks, SORT_THREADS, 0, st>>>(B, cu_tok, d, w.sorted);
+    }
+    KVB_TRY(check_launch("chunk_sort_kernel"));
+    {
+      LaunchTimer lt(st, "topk_rank");
+      rank_kernel<<<cdiv(n_tok, 256), 256, 0, st>>>(B, n_tok, cu_tok, d, w.sorted, k_cap, ranking, w.flag);
+    }
+    KVB_TRY(check_launch("rank_kernel"));
+  }
+  {
+    LaunchTimer lt(st, "topk_compact");
+    compact_kernel<<<B, CT, 0, st>>>(B, cu_tok, w.flag, sel, cu_rows, cursor, d, s_count);
+  }
+  return check_launch("compact_kernel");
+}
+
 }  // namespace kvb
 
 using namespace kvb;
+
+extern "C" kvb_status kvb_topk(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t B, int32_t n_tok,
+                               const int32_t* cu_tok, const float* d, const int32_t* k_cap, int32_t* ranking,
+                               int32_t* s_count, int32_t* sel, int32_t* cu_rows, int32_t* cursor, void* ws,
+                               size_t ws_bytes) {
+  KVB_TRY(check_ctx(ctx));
+  KVB_TRY(check_desc(desc));
+  if (B <= 0 || n_tok < 0) return fail(KVB_ERR_INVALID_ARG, "B <= 0 or negative size");
+  KVB_CHECK_PTR(cu_tok, "cu_tok");
+  KVB_CHECK_PTR(k_cap, "k_cap");
+  KVB_CHECK_PTR(s_count, "s_count");
+  KVB_CHECK_PTR(cu_rows, "cu_rows");
+  KVB_CHECK_PTR(cursor, "cursor");
+  if (n_tok > 0) {
+    KVB_CHECK_PTR(d, "d");
+    KVB_CHECK_PTR(ranking, "ranking");
+    KVB_CHECK_PTR(sel, "sel");
+  }
+  if (!ws || ws_bytes < ws_topk_bytes(n_tok, B)) return fail(KVB_ERR_WORKSPACE, "kvb_topk workspace too small");
+  CtxScope scope(ctx);
+  return launch_topk((hipStream_t)stream, B, n_tok, cu_tok, d, k_cap, ranking, s_count, sel, cu_rows, cursor, ws);
+}
 
 extern "C" kvb_status kvb_deviation_topk(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t B,
                                          int32_t n_tok, const int32_t* cu_tok, const void* k_rec, const void* k_pool,
@@ -252,31 +299,13 @@ extern "C" kvb_status kvb_deviation_topk(kvb_ctx* ctx, void* stream, const kvb_m
   if (desc->n_kv_heads * desc->head_dim / 8 > 1024) return fail(KVB_ERR_UNSUPPORTED, "n_kv_heads * head_dim > 8192");
   CtxScope scope(ctx);
   hipStream_t st = (hipStream_t)stream;
-  TopkWs w = topk_ws(ws, n_tok);
   if (desc->dtype == KVB_BF16)
     KVB_TRY(launch_deviation<bf16_t>(st, n_tok, k_rec, k_pool, n_pages, reuse_slot, d, alpha, desc->n_kv_heads,
                                      desc->head_dim));
   else
     KVB_TRY(launch_deviation<float>(st, n_tok, k_rec, k_pool, n_pages, reuse_slot, d, alpha, desc->n_kv_heads,
                                     desc->head_dim));
-  if (n_tok > 0) {
-    const int n_chunks = n_tok / CHUNK + B;  // >= sum over requests of cdiv(N_b, CHUNK)
-    {
-      LaunchTimer lt(st, "topk_sort");
-      chunk_sort_kernel<<<n_chunks, SORT_THREADS, 0, st>>>(B, cu_tok, d, w.sorted);
-    }
-    KVB_TRY(check_launch("chunk_sort_kernel"));
-    {
-      LaunchTimer lt(st, "topk_rank");
-      rank_kernel<<<cdiv(n_tok, 256), 256, 0, st>>>(B, n_tok, cu_tok, d, w.sorted, k_cap, ranking, w.flag);
-    }
-    KVB_TRY(check_launch("rank_kernel"));
-  }
-  {
-    LaunchTimer lt(st, "topk_compact");
-    compact_kernel<<<B, CT, 0, st>>>(B, cu_tok, w.flag, sel, cu_rows, cursor, d, s_count);
-  }
-  return check_launch("compact_kernel");
+  return launch_topk(st, B, n_tok, cu_tok, d, k_cap, ranking, s_count, sel, cu_rows, cursor, ws);
 }
 
 extern "C" kvb_status kvb_cosine_refresh(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t B,

@@ -2,10 +2,11 @@
 
 This module only plans memory (page allocation through the library's C++
 allocator, index arrays) and issues the C-ABI calls in order on one HIP
-stream; every step of the method runs in the library's kernels.  There is no
-host synchronisation inside a link step: selection sizes produced on the
-device (|S_k| after the top-k and after each refresh) reach the later kernels
-as device-side row counts.
+stream; every step of the method runs in the library's kernels.  Selection
+sizes produced on the device (|S_k| after the top-k and after each refresh)
+reach the later kernels as device-side row counts; with exact_rows (the
+default) the step also reads each new count back (4 bytes) so that later
+launches are sized to it.
 
 Token spaces.  Compile: the unique chunk instances concatenated, each its own
 segment (positions from 0, keys visible from the chunk start).  Link: the
@@ -15,7 +16,8 @@ visible from cu_tok[b]).
 Page plan (CacheSlide page, SLIDE implementation paragraph; 16-token pages):
 compile pages per chunk instance and layer, then per request and layer the
 link's new pages, N_r tokens' worth at layer 1 and floor(ratio * N_r) at later
-layers (CacheSlide), or |S_r| at every layer (LegoLink).
+layers (CacheSlide; cb_ratio for the CacheBlend-style selection), or |S_r| at
+every layer (LegoLink).  An uncached query chunk has no compile pages.
 """
 from __future__ import annotations
 
@@ -35,6 +37,11 @@ def _i32(x, device) -> torch.Tensor:
     return torch.as_tensor(np.asarray(x, dtype=np.int32), device=device)
 
 
+def _cached(chunk) -> bool:
+    """A chunk has compile-step KV unless it is the request's uncached query."""
+    return getattr(chunk, "kind", "fixed") != "query"
+
+
 def _npages(n: int) -> int:
     return (int(n) + PAGE - 1) // PAGE
 
@@ -50,8 +57,9 @@ class Model:
 
 @dataclass
 class LinkConfig:
-    mode: str = "cacheslide"          # "cacheslide" or "legolink"
-    ratio: float = 0.26
+    mode: str = "cacheslide"          # "cacheslide", "legolink" or "cacheblend"
+    ratio: float = 0.26               # CacheSlide top-k ratio
+    cb_ratio: float = 0.15            # CacheBlend-style top-k ratio
     tau: float = 0.12
     period: int = 4
     lego_k: int = 32
@@ -82,6 +90,8 @@ class LinkEngine:
     """
 
     def __init__(self, model: Model, requests, cfg: LinkConfig, device="cuda:0", stream=None, max_decode: int = 0):
+        if cfg.mode != "legolink" and any(not _cached(c) for r in requests for c in r.chunks):
+            raise ValueError("uncached query chunks must be recomputed in every layer: use mode='legolink'")
         self.model, self.cfg, self.device = model, cfg, torch.device(device)
         self.requests = list(requests)
         s = model.shape
@@ -99,7 +109,7 @@ class LinkEngine:
         chunks, seen = [], set()
         for r in requests:
             for c in r.chunks:
-                if c.uid not in seen:
+                if _cached(c) and c.uid not in seen:
                     seen.add(c.uid)
                     chunks.append(c)
         self.chunks = chunks
@@ -119,8 +129,9 @@ class LinkEngine:
         lo_l = np.concatenate([np.full(n, cu_t[b]) for b, n in enumerate(self.req_lens)])
 
         # ---------------- page plan (host allocator in the library)
-        if cfg.mode == "cacheslide":
-            self.k_cap = [int(math.floor(cfg.ratio * n)) for n in self.req_lens]
+        if cfg.mode in ("cacheslide", "cacheblend"):
+            ratio = cfg.ratio if cfg.mode == "cacheslide" else cfg.cb_ratio
+            self.k_cap = [int(math.floor(ratio * n)) for n in self.req_lens]
             per_layer = lambda l, b: self.req_lens[b] if l == 1 else self.k_cap[b]
         elif cfg.mode == "legolink":
             rows = []
@@ -128,7 +139,9 @@ class LinkEngine:
                 s0 = 0
                 rr = []
                 for ci, c in enumerate(r.chunks):
-                    if ci > 0:
+                    if not _cached(c):       # the query: all of it, in every layer
+                        rr.extend(range(s0, s0 + len(c.tokens)))
+                    elif ci > 0:
                         rr.extend(range(s0, s0 + min(cfg.lego_k, len(c.tokens))))
                     s0 += len(c.tokens)
                 rows.append(np.asarray(rr, dtype=np.int64) + start)
@@ -173,7 +186,7 @@ class LinkEngine:
             for c in r.chunks:
                 n = len(c.tokens)
                 for l in range(self.L):
-                    reuse_slot[l, g:g + n] = slots(comp_pages[c.uid][l], n)
+                    reuse_slot[l, g:g + n] = slots(comp_pages[c.uid][l], n) if _cached(c) else -1
                 g += n
         self.comp_slot_h, self.reuse_slot_h = comp_slot, reuse_slot
         new_pages, cu_pages = [None], [None]
@@ -319,8 +332,9 @@ class LinkEngine:
             self.copy_stream.wait_event(start)  # the previous step is done with the pool
 
     def _tier_copy(self, l: int, stream_handle: int):
-        # layer 1 of CacheSlide reads reused keys only (the deviation)
-        keys_only = l == 1 and self.cfg.mode == "cacheslide"
+        # layer 1 of CacheSlide and of the CacheBlend-style link reads reused keys
+        # only (the deviation compares keys)
+        keys_only = l == 1 and self.cfg.mode != "legolink"
         K.kvb_pages_copy(self.ctx, stream_handle, self.desc, K.KVB_COPY_H2D, self.host_k,
                          None if keys_only else self.host_v, self.k_pool, None if keys_only else self.v_pool,
                          self.layer_reuse_pages[l])
@@ -355,6 +369,8 @@ class LinkEngine:
         self._tier_begin()
         if self.cfg.mode == "cacheslide":
             self._link_cacheslide(hook)
+        elif self.cfg.mode == "cacheblend":
+            self._link_cacheblend(hook)
         else:
             self._link_static(hook)
         self._tier_end()
@@ -420,6 +436,37 @@ class LinkEngine:
                 if hook:
                     hook(("refresh", l), self)
 
+    def _link_cacheblend(self, hook):
+        """CacheBlend-style link (EPIC page, section 3.2): layer 1 recomputes every
+        token; each token's attention row under the cached layer-1 keys is
+        compared with its row under the recomputed ones, and the cb_ratio share
+        that deviates most is recomputed in layers 2..L, its K/V replacing the
+        cached ones (no fusion, no refresh)."""
+        c, sh, ds, N, B = self.ctx, self.sh, self.desc, self.N, self.B
+        K.kvb_embed(c, sh, ds, N, None, None, self.tok_l, self.shape.vocab, self.model.embedding, self.hidden)
+        self._layer_rows(1, N, None, None, self.cu_tok, None, K.KVB_ALPHA_ONE, None, None, None)
+        self._tier_need(1, self.L)
+        # self.q / self.k still hold layer 1's queries and recomputed keys of every token
+        K.kvb_attnmap_deviation(c, sh, ds, N, self.lo_l, self.q, self.k, self.k_pool, self.n_pages,
+                                self.reuse_slot[0], self.scale, self.d, self.ws, self.ws_bytes)
+        K.kvb_topk(c, sh, ds, B, N, self.cu_tok, self.d, self.k_cap_d, self.ranking, self.s_count, self.sel[0],
+                   self.cu_rows[0], self.cursor, self.ws, self.ws_bytes)
+        self.cur = 0
+        if hook:
+            hook(1, self)
+        T = self._read_rows(0) if self.cfg.exact_rows else self.T_sel
+        for l in range(2, self.L + 1):
+            if T == 0:
+                self._pt_reuse_rows.add(l)
+                if hook:
+                    hook(l, self)
+                continue
+            self._tier_need(l, self.L)
+            self._layer_rows(l, T, self._n_rows_ptr(0), self.sel[0], self.cu_rows[0], None, K.KVB_ALPHA_ONE, None,
+                             None, None)
+            if hook:
+                hook(l, self)
+
     def _link_static(self, hook):
         c, sh, ds, T = self.ctx, self.sh, self.desc, self.T_sel
         if T == 0:
@@ -483,7 +530,7 @@ class LinkEngine:
         for b, r in enumerate(self.requests):
             g = cu[b]
             for c in r.chunks:
-                own[g:g + len(c.tokens)] = len(owners[c.uid]) == 1
+                own[g:g + len(c.tokens)] = _cached(c) and len(owners[c.uid]) == 1
                 g += len(c.tokens)
         self.dec_holes = [[None] * B for _ in range(L + 1)]
         for l in range(1, L + 1):

@@ -13,9 +13,10 @@ so every check is teacher-forced and sampled:
     row, each against the oracle fed the GPU's inputs to that layer (hidden
     rows, alpha, the layer's paged K/V); CKSim of every selected row.
 
-Workloads: the Mistral-7B-shaped 8192-token CacheSlide request, the
-16384-token LegoLink prompt, the batch of 8 requests with shared fixed chunks,
-and the Llama-3-70B-shaped 32768-token request (layers 1, 2, 5 and 80).
+Workloads: the Mistral-7B-shaped 8192-token CacheSlide request (also run
+with the CacheBlend-style selection), the 16384-token LegoLink prompt, the
+batch of 8 requests with shared fixed chunks, and the Llama-3-70B-shaped
+32768-token request (layers 1, 2, 5 and 80).
 """
 import math
 
@@ -228,6 +229,50 @@ def test_mistral_legolink_16k_fullsize():
 @pytest.mark.timeout(300)
 def test_mistral_batch8_fullsize():
     run_fullsize(wl.mistral_batch8(), check_layers=[1, 2, 4, 5])
+
+
+@pytest.mark.timeout(300)
+def test_mistral_cacheblend_8k_fullsize():
+    """The CacheBlend-style selection on the 8192-token Mistral-shaped request:
+    layer-1 attention-map deviations (chunk 0 exactly zero, sampled tokens
+    against the oracle), ranking and S_k bit-exact from the GPU's own scores,
+    slot maps and sampled rows of layers 2 and 32 (replace, no fusion)."""
+    w = wl.mistral_cacheslide()
+    s = w.shape
+    eng, _, _ = build_engine(w, mode="cacheblend")
+    rec = LayerRecorder({1, 2, 31, 32})
+    eng.run_compile()
+    eng.run_link(hook=rec)
+    torch.cuda.synchronize()
+    print(f"[{w.name} cacheblend] link step done", flush=True)
+    plan = page_plan_check(eng, w)
+    req, N, tol = w.requests[0], eng.N, TOL[s.dtype]
+    g = np.random.default_rng(3)
+    st = rec.after[1]
+    d_gpu = np64(st["d"])
+    assert np.all(d_gpu[: len(req.chunks[0])] == 0.0)
+    ranking, S_k, cursor = OS.top_k(d_gpu, eng.k_cap[0])
+    assert len(S_k) == eng.k_cap[0] == int(math.floor(w.cb_ratio * N))
+    assert list(st["ranking"][: len(ranking)]) == ranking and int(st["s_count"][0]) == len(ranking)
+    assert list(st["sel"][st["cu_rows"][0]:st["cu_rows"][1]]) == S_k
+    assert np.array_equal(st["slot_map"][:N], OP.slot_map(OP.reuse_slots(req, plan, 1), np.arange(N),
+                                                          eng.link_pages[0][1]))
+    samp = sorted({N - 1, len(req.chunks[0]), len(req.chunks[0]) - 1} | set(g.choice(N, N_SAMPLE).tolist()))
+    K_old = pool_rows(eng, eng.k_pool, eng.reuse_slot_h[0][:N])
+    ref = OS.attention_map_deviation(np64(st["q"][:N]), np64(st["k"][:N]), K_old, np.zeros(N, int), s, rows=samp)
+    assert np.allclose(d_gpu[samp], ref, rtol=1e-3, atol=5e-5)
+    for l in (2, 32):
+        print(f"[{w.name} cacheblend] layer {l}", flush=True)
+        stl = rec.after[l]
+        rows = rows_in_order(eng, stl)
+        assert [gg for _, gg, _ in rows] == S_k
+        ref_sm = OP.slot_map(OP.reuse_slots(req, plan, l), np.asarray(S_k), eng.link_pages[0][l])
+        assert np.array_equal(stl["slot_map"][:N], ref_sm)
+        samp_r = sample_rows(rows, g)
+        gi = np.array([gg for _, gg, _ in samp_r])
+        h_in = np64(rec.after[l - 1]["hidden"][gi])
+        check_rows(eng, w, l, layer_weights_np(w, l), stl, samp_r, h_in, None, tol, fused=False)
+    eng.close()
 
 
 @pytest.mark.timeout(600)

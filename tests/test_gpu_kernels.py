@@ -265,6 +265,100 @@ def test_sparse_query_attention(ctx, name, req_lens, n_sel):
     assert torch.all(o[n_valid:] == 3.0)
 
 
+# ------------------------------------------------------------------ CacheBlend-style attention-map deviation
+
+AMAP_SHAPES = {
+    "bf16": SHAPES["bf16"],
+    "bf16_hd64": SHAPES["bf16_hd64"],
+    "bf16_g8": wl.ModelShape(n_layers=1, d_model=2048, n_q_heads=16, n_kv_heads=2, head_dim=128, ffn=512,
+                             dtype="bf16"),
+    "fp32": SHAPES["fp32"],
+}
+
+
+@pytest.mark.parametrize("name", list(AMAP_SHAPES))
+@pytest.mark.parametrize("req_lens,invalid", [([700], False), ([300, 517, 64], False), ([33], False),
+                                              ([300, 517, 64], True)])
+def test_attnmap_deviation(ctx, name, req_lens, invalid):
+    """dev vs the oracle; tokens whose visible cached keys equal the recomputed
+    ones get exactly 0; a key with an invalid reuse slot is left out of both maps."""
+    s = AMAP_SHAPES[name]
+    g = np.random.default_rng(7 * sum(req_lens) + invalid)
+    desc = K.model_desc(s)
+    dt = tdt(s)
+    B, n_tok = len(req_lens), sum(req_lens)
+    cu = np.concatenate([[0], np.cumsum(req_lens)]).astype(np.int64)
+    lo = np.concatenate([np.full(n, cu[b]) for b, n in enumerate(req_lens)])
+    n_pages = (n_tok + 15) // 16 + 3
+    reuse_slot = g.permutation(n_pages * 16)[:n_tok]
+    k_rec = rand((n_tok, s.n_kv_heads, s.head_dim), g, dtype=dt)
+    kp = rand((n_pages, s.n_kv_heads, 16, s.head_dim), g, dtype=dt)
+    # cached keys: the recomputed ones for each request's first 40 tokens, a
+    # perturbation of them (position-shift-like) elsewhere
+    cached = k_rec.float() + 0.3 * rand((n_tok, s.n_kv_heads, s.head_dim), g)
+    for b in range(B):
+        cached[cu[b]:cu[b] + min(40, req_lens[b])] = k_rec[cu[b]:cu[b] + min(40, req_lens[b])].float()
+    sl = torch.as_tensor(reuse_slot)
+    kp[sl // 16, :, sl % 16, :] = cached.to(dt)
+    if invalid:
+        reuse_slot[cu[:-1]] = -5          # first key of every request: no valid slot
+    q = rand((n_tok, s.n_q_heads, s.head_dim), g, 1.5, dtype=dt)
+    q, k_rec, kp = q.to(DEV), k_rec.to(DEV), kp.to(DEV)
+    dev = torch.full((n_tok,), -1.0, device=DEV)
+    ws, wsb = workspace(ctx, desc, 1, n_tok, B)
+    scale = 1.0 / np.sqrt(s.head_dim)
+    K.kvb_attnmap_deviation(ctx, sh(), desc, n_tok, i32(lo), q, k_rec, kp, n_pages, i32(reuse_slot), scale, dev, ws,
+                            wsb)
+    torch.cuda.synchronize()
+    got = np64(dev)
+    reuse = _rows_at(kp, reuse_slot, s)
+    idx = np.arange(n_tok)
+    lo_ref = np.minimum(lo + 1, idx) if invalid else lo
+    ref = OS.attention_map_deviation(np64(q), np64(k_rec), reuse, lo_ref, s)
+    if invalid:
+        ref[cu[:-1]] = 0.0
+    # fp32 scores: absolute error of a probability ~ 1e-6 of its value, summed over a row
+    assert np.allclose(got, ref, rtol=1e-3, atol=5e-5), np.max(np.abs(got - ref))
+    for b in range(B):
+        n0 = min(40, req_lens[b])
+        assert np.all(got[cu[b]:cu[b] + n0] == 0.0)
+    assert np.all(got[np.abs(ref) > 1e-3] > 0.0)
+
+
+@pytest.mark.parametrize("req_lens", [[517], [4100, 300, 2049, 64], [2048, 2048]])
+def test_topk_from_scores(ctx, req_lens):
+    """kvb_topk on given scores (zeros and exact ties included) equals the
+    oracle's ranking and top-k of the same scores, bit for bit."""
+    s = SHAPES["bf16"]
+    g = np.random.default_rng(len(req_lens))
+    desc = K.model_desc(s)
+    B, n_tok = len(req_lens), sum(req_lens)
+    cu = np.concatenate([[0], np.cumsum(req_lens)]).astype(np.int64)
+    d_np = g.random(n_tok).astype(np.float32) * 2.0
+    d_np[g.random(n_tok) < 0.2] = 0.0
+    d_np[g.choice(n_tok, n_tok // 10)] = np.float32(0.75)
+    d = torch.tensor(d_np, device=DEV)
+    k_cap = [int(np.floor(0.15 * n)) for n in req_lens]
+    ranking = torch.full((n_tok,), -1, dtype=torch.int32, device=DEV)
+    s_count = torch.zeros(B, dtype=torch.int32, device=DEV)
+    sel = torch.full((n_tok,), -1, dtype=torch.int32, device=DEV)
+    cu_rows = torch.zeros(B + 1, dtype=torch.int32, device=DEV)
+    cursor = torch.zeros(B, dtype=torch.int32, device=DEV)
+    ws, wsb = workspace(ctx, desc, 1, n_tok, B)
+    K.kvb_topk(ctx, sh(), desc, B, n_tok, i32(cu), d, i32(k_cap), ranking, s_count, sel, cu_rows, cursor, ws, wsb)
+    torch.cuda.synchronize()
+    assert torch.equal(d.cpu(), torch.tensor(d_np))
+    rk, ss, sl, cr, cs = (x.cpu().numpy() for x in (ranking, s_count, sel, cu_rows, cursor))
+    assert cr[0] == 0
+    for b in range(B):
+        seg = d_np[cu[b]:cu[b + 1]].astype(np.float64)
+        ranking_ref, S_k_ref, cur_ref = OS.top_k(seg, k_cap[b])
+        assert ss[b] == len(ranking_ref)
+        assert list(rk[cu[b]:cu[b] + len(ranking_ref)] - cu[b]) == ranking_ref
+        assert cs[b] == cur_ref == cr[b + 1] - cr[b]
+        assert list(sl[cr[b]:cr[b + 1]] - cu[b]) == S_k_ref
+
+
 # ------------------------------------------------------------------ O-proj + MLP
 
 @pytest.mark.parametrize("name", ["bf16", "fp32"])

@@ -35,8 +35,8 @@ def build_engine(w, tau=None, mode=None):
     s = w.shape
     E = wl.embedding_table(w, DEV)
     layers = [wl.layer_weights(w, l, DEV) for l in range(1, s.n_layers + 1)]
-    cfg = LinkConfig(mode=mode or w.mode, ratio=w.ratio, tau=w.tau if tau is None else tau, period=w.period,
-                     lego_k=w.lego_k)
+    cfg = LinkConfig(mode=mode or w.mode, ratio=w.ratio, cb_ratio=w.cb_ratio, tau=w.tau if tau is None else tau,
+                     period=w.period, lego_k=w.lego_k)
     eng = LinkEngine(Model(s, E, layers), w.requests, cfg, device=DEV)
     E_np = np64(E)
     W_cache = {}
@@ -100,7 +100,8 @@ def page_plan_check(eng, w):
     for b, r in enumerate(w.requests):
         lego_rows = OL.legolink_rows(r, w.lego_k).size
         for l in range(1, s.n_layers + 1):
-            n = OP.capacity(eng.cfg.mode, r.n_tokens, w.ratio, lego_rows, l)
+            ratio = w.cb_ratio if eng.cfg.mode == "cacheblend" else w.ratio
+            n = OP.capacity(eng.cfg.mode, r.n_tokens, ratio, lego_rows, l)
             assert eng.link_pages[b][l] == alloc.alloc(OP.n_pages_for(n))
     return plan
 
@@ -278,6 +279,66 @@ def test_legolink_layers(make):
         h_prev = np64(gl["hidden"])[S]
     if s.dtype == "fp32":   # free-running end to end as well
         assert max_rel_err(np64(rec.after[s.n_layers]["hidden"])[S], hS_ref) < TOL["fp32"]
+    eng.close()
+
+
+@pytest.mark.parametrize("make", [lambda: wl.tiny(n_layers=3, mode="cacheblend"),
+                                  lambda: wl.small_bf16(n_layers=4, mode="cacheblend")],
+                         ids=["tiny", "small-bf16"])
+def test_cacheblend_teacher_forced(make):
+    """CacheBlend-style link: layer 1 (full recompute, attention-map deviation,
+    top-k at 15 %) and every later layer against the oracle fed the GPU's
+    inputs; the float32 case is also checked free-running end to end."""
+    w = make()
+    eng, E, W = build_engine(w)
+    rec = Recorder()
+    eng.run_compile()
+    eng.run_link(hook=rec)
+    torch.cuda.synchronize()
+    s, req = w.shape, w.requests[0]
+    tol = TOL[s.dtype]
+    N = req.n_tokens
+    compiled = OL.compile_chunks(w.compile_chunks, s, E, W)
+    assert compile_check(eng, w, E, W, compiled) < tol
+    plan = page_plan_check(eng, w)
+    reuse = {l: (pool_rows(eng, eng.k_pool, OP.reuse_slots(req, plan, l)),
+                 pool_rows(eng, eng.v_pool, OP.reuse_slots(req, plan, l))) for l in range(1, s.n_layers + 1)}
+    g1 = rec.after[1]
+    pos = np.arange(N)
+    q, k, v = OM.qkv(OM.store(E[req.tokens], s.dtype), pos, W(1), s, blocks=OL.chunk_blocks(req))
+    assert max_rel_err(g1["q"][:N], q) < tol and max_rel_err(g1["k"][:N], k) < tol
+    d_gpu = np64(g1["d"])
+    d_ref = OS.attention_map_deviation(np64(g1["q"][:N]), np64(g1["k"][:N]), reuse[1][0], np.zeros(N, int), s)
+    assert np.allclose(d_gpu, d_ref, rtol=1e-3, atol=5e-5)
+    assert np.all(d_gpu[: len(req.chunks[0])] == 0.0)
+    k_cap = int(math.floor(w.cb_ratio * N))
+    ranking, S_k, _ = OS.top_k(d_gpu, k_cap)         # exact on the GPU's own scores
+    S = rows_of(g1)
+    assert list(S) == S_k and len(S) == k_cap
+    assert list(g1["ranking"].cpu().numpy()[:len(ranking)]) == ranking
+    T = S.size
+    h_prev = np64(g1["hidden"])
+    for l in range(2, s.n_layers + 1):
+        gl = rec.after[l]
+        assert np.array_equal(rows_of(gl), S)
+        sm_ref = OP.slot_map(OP.reuse_slots(req, plan, l), S, eng.link_pages[0][l])
+        assert np.array_equal(gl["slot_map"].cpu().numpy(), sm_ref)
+        q, k, v = OM.qkv(h_prev[S], S, W(l), s)
+        assert max_rel_err(gl["q"][:T], q) < tol and max_rel_err(gl["k"][:T], k) < tol
+        K_log = pool_rows(eng, eng.k_pool, sm_ref)
+        V_log = pool_rows(eng, eng.v_pool, sm_ref)
+        assert np.array_equal(K_log[S], np64(gl["k"][:T])) and np.array_equal(V_log[S], np64(gl["v"][:T]))
+        nonsel = np.setdiff1d(np.arange(N), S)
+        assert np.array_equal(K_log[nonsel], reuse[l][0][nonsel])
+        o = OM.attention_rows_fast(np64(gl["q"][:T]), S, K_log, V_log, np.zeros(T, int), s)
+        assert max_rel_err(gl["o"][:T], o) < tol
+        h_out = OM.post_attention(h_prev[S], np64(gl["o"][:T]), W(l), s)
+        assert max_rel_err(np64(gl["hidden"])[S], h_out) < tol
+        h_prev = np64(gl["hidden"])
+    if s.dtype == "fp32":
+        st, outs = OL.cacheblend_link(req, s, E, W, compiled, k_cap)
+        if st.S_k == list(S):
+            assert max_rel_err(np64(eng.hidden)[S], st.h[S]) < TOL["fp32"]
     eng.close()
 
 
