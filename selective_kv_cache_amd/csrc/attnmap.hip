@@ -30,8 +30,8 @@
 // two-pass softmax.
 #include "common.h"
 
-// No multiply-add contraction in this file: the two maps' probabilities are
-// each rounded before they are subtracted, so equal scores give exactly 0.
+// No implicit multiply-add contraction in this file: every fused operation is
+// written out and applied to both maps alike, so equal scores give exactly 0.
 #pragma clang fp contract(off)
 
 namespace kvb {
@@ -70,7 +70,7 @@ struct MapGeom {
 };
 
 template <int HD>
-__global__ void __launch_bounds__(MTHREADS) attnmap_bf16_kernel(MapArgs a) {
+__global__ void __launch_bounds__(MTHREADS) __attribute__((amdgpu_waves_per_eu(4, 4))) attnmap_bf16_kernel(MapArgs a) {
   using Gm = MapGeom<HD>;
   constexpr int KS = HD / 16;
   constexpr int ROWB = Gm::ROWB, CPR = Gm::CPR, RPI = Gm::RPI, IPW = Gm::IPW, TILE = Gm::TILE;
@@ -170,7 +170,7 @@ __global__ void __launch_bounds__(MTHREADS) attnmap_bf16_kernel(MapArgs a) {
   // running statistics of the query's two rows (base-2 units); in pass 2 the
   // final offsets and reciprocal sums
   float mn = -INFINITY, ln = 0.f, mo = -INFINITY, lo_ = 0.f;
-  float inv_n = 0.f, inv_o = 0.f, acc = 0.f;
+  float inv_n = 0.f, ratio = 0.f, acc = 0.f;
 
   for (int pass = 0; pass < 2; pass++) {
     // prologue: slots of tiles 0 and 1, keys of tile 0
@@ -204,12 +204,13 @@ __global__ void __launch_bounds__(MTHREADS) attnmap_bf16_kernel(MapArgs a) {
           sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kn, qf[ks], sn, 0, 0, 0);
           so = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ko, qf[ks], so, 0, 0, 0);
         }
-        // scores of keys j0 + 32 kt + 8 (r / 4) + 4 g2 + r % 4, base-2 units
+        // raw scores of keys j0 + 32 kt + 8 (r / 4) + 4 g2 + r % 4; a probability is
+        // exp2(fma(score, scale_log2, -offset)) with the row's base-2 offset
         float tn[16], to[16];
 #pragma unroll
         for (int e = 0; e < 16; e++) {
-          tn[e] = sn[e] * a.scale_log2;
-          to[e] = so[e] * a.scale_log2;
+          tn[e] = sn[e];
+          to[e] = so[e];
         }
         if (need_mask) {
           const uint32_t iv = (uint32_t)(inval >> (kt * 32 + 4 * g2));
@@ -222,6 +223,7 @@ __global__ void __launch_bounds__(MTHREADS) attnmap_bf16_kernel(MapArgs a) {
             }
           }
         }
+        const float c = a.scale_log2;
         if (pass == 0) {
           float xn = tn[0], xo = to[0];
 #pragma unroll
@@ -229,8 +231,8 @@ __global__ void __launch_bounds__(MTHREADS) attnmap_bf16_kernel(MapArgs a) {
             xn = fmaxf(xn, tn[e]);
             xo = fmaxf(xo, to[e]);
           }
-          xn = fmaxf(xn, __shfl_xor(xn, 32, 64));
-          xo = fmaxf(xo, __shfl_xor(xo, 32, 64));
+          xn = fmaxf(xn, __shfl_xor(xn, 32, 64)) * c;
+          xo = fmaxf(xo, __shfl_xor(xo, 32, 64)) * c;
           if (xn > mn) {
             ln *= __builtin_amdgcn_exp2f(mn - xn);
             mn = xn;
@@ -241,16 +243,20 @@ __global__ void __launch_bounds__(MTHREADS) attnmap_bf16_kernel(MapArgs a) {
           }
           if (mn != -INFINITY) {
 #pragma unroll
-            for (int e = 0; e < 16; e++) ln += __builtin_amdgcn_exp2f(tn[e] - mn);
+            for (int e = 0; e < 16; e++) ln += __builtin_amdgcn_exp2f(fmaf(tn[e], c, -mn));
           }
           if (mo != -INFINITY) {
 #pragma unroll
-            for (int e = 0; e < 16; e++) lo_ += __builtin_amdgcn_exp2f(to[e] - mo);
+            for (int e = 0; e < 16; e++) lo_ += __builtin_amdgcn_exp2f(fmaf(to[e], c, -mo));
           }
         } else {
+          // |pn - po| = inv_n |en - ratio eo|, ratio = ln / lo (exactly 1 for equal rows)
 #pragma unroll
-          for (int e = 0; e < 16; e++)
-            acc += fabsf(__builtin_amdgcn_exp2f(tn[e] - mn) * inv_n - __builtin_amdgcn_exp2f(to[e] - mo) * inv_o);
+          for (int e = 0; e < 16; e++) {
+            const float en = __builtin_amdgcn_exp2f(fmaf(tn[e], c, -mn));
+            const float eo = __builtin_amdgcn_exp2f(fmaf(to[e], c, -mo));
+            acc += fabsf(fmaf(-eo, ratio, en));
+          }
         }
       }
     }
@@ -259,12 +265,13 @@ __global__ void __launch_bounds__(MTHREADS) attnmap_bf16_kernel(MapArgs a) {
       ln += __shfl_xor(ln, 32, 64);
       lo_ += __shfl_xor(lo_, 32, 64);
       inv_n = ln > 0.f ? 1.f / ln : 0.f;
-      inv_o = lo_ > 0.f ? 1.f / lo_ : 0.f;
+      ratio = lo_ > 0.f ? ln / lo_ : 0.f;
       if (mn == -INFINITY) mn = 0.f;  // no visible key: every probability is 0
       if (mo == -INFINITY) mo = 0.f;
       lds_barrier();  // every wave is done with the last tile before pass 2 refills stage 0
     }
   }
+  acc *= inv_n;
   // the query's two halves, then the group's heads (adjacent lanes)
   acc += __shfl_xor(acc, 32, 64);
   for (int o = 1; o < G; o <<= 1) acc += __shfl_xor(acc, o, 64);

@@ -352,12 +352,22 @@ gemm_bf16_kernel(GemmArgs<bf16_t> p, SkArgs sk) {
           else wait_vmcnt<0>();
           lds_barrier();  // stage kt (PA: kt + 1) published; every wave is done with the stage refilled next
           if (kt + NST - 1 < KTL) issue(kt + NST - 1, stg[(S + NST - 1) % NST]);
-          if constexpr (!PA) frags(0, stg[S], 0);
+          if constexpr (!PA) {
+            frags(0, stg[S], 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);  // this slice's reads come first
+          }
 #pragma unroll
           for (int s = 0; s < KS; s++) {
             if (s + 1 < KS) frags((s + 1) & 1, stg[S], s + 1);
             else if (PA && kt + 1 < KTL) frags((s + 1) & 1, stg[(S + 1) % NST], 0);
             mma(s & 1);
+            if (s + 1 < KS) {
+              // keep the next slice's fragment reads ahead of this slice's
+              // MFMAs (left alone, the scheduler sinks each read to just
+              // before its use and the MFMAs wait on LDS latency)
+              __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);  // LDS reads
+              __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);  // MFMAs
+            }
           }
         }
       }
