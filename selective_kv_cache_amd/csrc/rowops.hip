@@ -28,34 +28,51 @@ __global__ void embed_kernel(int T_max, const int32_t* __restrict__ n_rows, cons
 
 // ------------------------------------------------------------------ RoPE
 // rotate-half: (x_j, x_{j+hd/2}) -> (x_j c - x_{j+hd/2} s, x_{j+hd/2} c + x_j s),
-// angle = pos * base^(-2j/hd) formed in double precision.
+// angle = pos * base^(-2j/hd).  The angle is formed and reduced to [-pi, pi] in
+// double precision; its cosine and sine are then taken in float.
+
+template <class T> __device__ __forceinline__ void load8(const T* p, float* o);
+template <class T> __device__ __forceinline__ void store8(T* p, const float* v);
 
 template <class T>
-__global__ void rope_kernel(int T_max, const int32_t* __restrict__ n_rows, const int32_t* __restrict__ row_tok,
-                            const int32_t* __restrict__ tok_pos, T* __restrict__ q, T* __restrict__ k, int Hq,
-                            int Hkv, int hd, float base) {
+__global__ void __launch_bounds__(256) rope_kernel(int T_max, const int32_t* __restrict__ n_rows,
+                                                   const int32_t* __restrict__ row_tok,
+                                                   const int32_t* __restrict__ tok_pos, T* __restrict__ q,
+                                                   T* __restrict__ k, int Hq, int Hkv, int hd, float base) {
   const int r = blockIdx.x;
   if (r >= row_count(n_rows, T_max)) return;
   const int g = row_tok ? row_tok[r] : r;
   const double pos = (double)tok_pos[g];
   const int half = hd / 2;
   __shared__ float cs[64], sn[64];
-  for (int j = threadIdx.x; j < half; j += blockDim.x) {
-    double inv = pow((double)base, -2.0 * (double)j / (double)hd);
-    double s, c;
-    sincos(pos * inv, &s, &c);
-    cs[j] = (float)c;
-    sn[j] = (float)s;
+  if (threadIdx.x < half) {
+    const int j = threadIdx.x;
+    const double a = pos * exp2(-2.0 * (double)j / (double)hd * log2((double)base));
+    const double twopi = 6.283185307179586;
+    const double red = fma(-rint(a / twopi), twopi, a);
+    float s, c;
+    sincosf((float)red, &s, &c);
+    cs[j] = c;
+    sn[j] = s;
   }
   __syncthreads();
-  const int npairs = (Hq + Hkv) * half;
-  for (int p = threadIdx.x; p < npairs; p += blockDim.x) {
-    const int h = p / half, j = p % half;
+  // one item = 8 consecutive pairs (j .. j+7, j+half .. j+half+7) of one head
+  const int gph = half / 8;
+  const int items = (Hq + Hkv) * gph;
+  for (int it = threadIdx.x; it < items; it += blockDim.x) {
+    const int h = it / gph, j = (it % gph) * 8;
     T* x = (h < Hq) ? (q + ((size_t)r * Hq + h) * hd) : (k + ((size_t)r * Hkv + (h - Hq)) * hd);
-    const float x1 = to_f<T>(x[j]), x2 = to_f<T>(x[j + half]);
-    const float c = cs[j], s = sn[j];
-    Store<T>::st(x + j, x1 * c - x2 * s);
-    Store<T>::st(x + j + half, x2 * c + x1 * s);
+    float x1[8], x2[8], y1[8], y2[8];
+    load8<T>(x + j, x1);
+    load8<T>(x + j + half, x2);
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      const float c = cs[j + e], sv = sn[j + e];
+      y1[e] = x1[e] * c - x2[e] * sv;
+      y2[e] = x2[e] * c + x1[e] * sv;
+    }
+    store8<T>(x + j, y1);
+    store8<T>(x + j + half, y2);
   }
 }
 
