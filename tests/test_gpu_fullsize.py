@@ -227,6 +227,13 @@ def test_mistral_legolink_16k_fullsize():
 
 
 @pytest.mark.timeout(300)
+def test_mistral_legolink_16k_query_fullsize():
+    """The 16K LegoLink prompt followed by a 300-token uncached query, which is
+    recomputed in every layer (its slots come only from the new pages)."""
+    run_fullsize(wl.mistral_legolink(query_len=300), check_layers=[1, 2, 32])
+
+
+@pytest.mark.timeout(300)
 def test_mistral_batch8_fullsize():
     run_fullsize(wl.mistral_batch8(), check_layers=[1, 2, 4, 5])
 

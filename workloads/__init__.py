@@ -242,10 +242,12 @@ def mistral_cacheslide(seed: int = 0, n_layers: int = 32) -> Workload:
                     seed=seed, gen_device="cuda")
 
 
-def mistral_legolink(seed: int = 0, n_layers: int = 32) -> Workload:
-    """Mistral-7B-shaped stack, 16384 tokens as 32 chunks of 512, LegoLink k=32."""
+def mistral_legolink(seed: int = 0, n_layers: int = 32, query_len: int = 0) -> Workload:
+    """Mistral-7B-shaped stack, 16384 tokens as 32 chunks of 512, LegoLink k=32
+    (query_len > 0: then an uncached query of that many tokens)."""
     shape = ModelShape(**{**MISTRAL.__dict__, "n_layers": n_layers})
-    return Workload("mistral7b-legolink-16k", shape, "legolink", [_single_request(seed, [512] * 32)],
+    name = "mistral7b-legolink-16k" + (f"-q{query_len}" if query_len else "")
+    return Workload(name, shape, "legolink", [_single_request(seed, [512] * 32, query_len)],
                     seed=seed, gen_device="cuda")
 
 
