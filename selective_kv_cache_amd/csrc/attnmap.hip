@@ -401,13 +401,17 @@ extern "C" kvb_status kvb_attnmap_deviation(kvb_ctx* ctx, void* stream, const kv
   const int G = Hq / Hkv;
   if (hd != 64 && hd != 128) return fail(KVB_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
   if ((long)n_pages * 16 > 0x7fffffffL) return fail(KVB_ERR_INVALID_ARG, "pool too large for int32 slots");
-  CtxScope scope(ctx);
-  hipStream_t st = (hipStream_t)stream;
   if (desc->dtype == KVB_BF16) {
     if (G > 32 || (G & (G - 1)) != 0)
       return fail(KVB_ERR_UNSUPPORTED, "n_q_heads / n_kv_heads must be a power of two up to 32");
     if (!ws || ws_bytes < ws_attnmap_bytes(desc, n_tok))
       return fail(KVB_ERR_WORKSPACE, "kvb_attnmap_deviation workspace too small");
+  } else if (Hq > FMAXH) {
+    return fail(KVB_ERR_UNSUPPORTED, "n_q_heads > 256 on the float32 path");
+  }
+  CtxScope scope(ctx);
+  hipStream_t st = (hipStream_t)stream;
+  if (desc->dtype == KVB_BF16) {
     MapArgs a;
     a.n_tok = n_tok;
     a.tok_lo = tok_lo;
@@ -434,7 +438,6 @@ extern "C" kvb_status kvb_attnmap_deviation(kvb_ctx* ctx, void* stream, const kv
     }
     return check_launch("attnmap_reduce_kernel");
   }
-  if (Hq > FMAXH) return fail(KVB_ERR_UNSUPPORTED, "n_q_heads > 256 on the float32 path");
   {
     LaunchTimer lt(st, "attnmap");
     if (hd == 128)

@@ -163,3 +163,29 @@ def test_pages_copy_checks(lib):
         K.kvb_pages_copy(FAKE_CTX, None, d, K.KVB_COPY_H2D, None, 1, 1, 1, [0])
     assert e.value.status == K.KVB_ERR_INVALID_ARG and "src_k" in K.kvb_last_error()
     K.kvb_pages_copy(FAKE_CTX, None, d, K.KVB_COPY_D2H, None, None, None, None, [])  # nothing to copy
+
+
+def test_attnmap_and_topk_checks(lib):
+    """kvb_attnmap_deviation / kvb_topk: argument errors before anything is enqueued."""
+    d = _desc()
+    bf = _desc(dtype=K.KVB_BF16, d_model=512, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=1536)
+    with pytest.raises(K.KvbError) as e:          # no queries
+        K.kvb_attnmap_deviation(FAKE_CTX, None, d, 8, 1, None, 1, 1, 4, 1, 0.125, 1, None, 0)
+    assert e.value.status == K.KVB_ERR_INVALID_ARG and "q" in K.kvb_last_error()
+    with pytest.raises(K.KvbError) as e:          # bf16 needs its partials workspace
+        K.kvb_attnmap_deviation(FAKE_CTX, None, bf, 8, 1, 1, 1, 1, 4, 1, 0.125, 1, 1, 16)
+    assert e.value.status == K.KVB_ERR_WORKSPACE
+    g3 = _desc(dtype=K.KVB_BF16, d_model=768, n_q_heads=6, n_kv_heads=2, head_dim=128, ffn=1536)
+    with pytest.raises(K.KvbError) as e:          # a GQA group of 3 does not tile the lanes
+        K.kvb_attnmap_deviation(FAKE_CTX, None, g3, 8, 1, 1, 1, 1, 4, 1, 0.125, 1, 1, 1 << 20)
+    assert e.value.status == K.KVB_ERR_UNSUPPORTED
+    K.kvb_attnmap_deviation(FAKE_CTX, None, d, 0, None, None, None, None, 0, None, 0.125, None, None, 0)
+    with pytest.raises(K.KvbError) as e:
+        K.kvb_topk(FAKE_CTX, None, d, 0, 8, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1 << 20)
+    assert e.value.status == K.KVB_ERR_INVALID_ARG
+    with pytest.raises(K.KvbError) as e:
+        K.kvb_topk(FAKE_CTX, None, d, 1, 8, 1, None, 1, 1, 1, 1, 1, 1, 1, 1 << 20)
+    assert e.value.status == K.KVB_ERR_INVALID_ARG and "d" in K.kvb_last_error()
+    with pytest.raises(K.KvbError) as e:
+        K.kvb_topk(FAKE_CTX, None, d, 1, 8, 1, 1, 1, 1, 1, 1, 1, 1, 1, 8)
+    assert e.value.status == K.KVB_ERR_WORKSPACE
