@@ -314,7 +314,7 @@ __global__ void __launch_bounds__(64 * FWAVES) attnmap_f32_kernel(int n_tok, con
   for (int base = 0; base < Hq; base += FWAVES) {
     const int hq = base + wave;
     const int h = hq / G;
-    __syncthreads();  // the previous round's reads of sq are done
+    __syncthreads();  // the previous iteration's reads of sq are done
     if (hq < Hq)
       for (int i = lane; i < HD; i += 64) sq[wave][i] = q[((size_t)g * Hq + hq) * HD + i];
     __syncthreads();
