@@ -64,7 +64,8 @@ def kernel_work(eng, layer_rows, layer_pos, shape):
         w["blend_scatter"] += T * (6.0 * Hkv * hd * esz + 16.0)
         w["rope"] += T * 2.0 * (Hq + Hkv) * hd * esz
     w["deviation"] += eng.N * (2.0 * Hkv * hd * esz + 16.0)
-    w["embed"] += eng.N * 2.0 * d * esz
+    # the embedding gathers every token's row, except in LegoLink (its static rows only)
+    w["embed"] += (eng.T_sel if eng.cfg.mode == "legolink" else eng.N) * 2.0 * d * esz
     return w, rows_per_layer
 
 
