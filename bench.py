@@ -34,7 +34,7 @@ DECODE_TOKENS = 8              # decode continuation leg: tokens per request
 def parse():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mistral7b-cacheslide-8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -213,6 +213,57 @@ def tier_host(eng, args, st, n_selected):
             "h2d_GBps": nbytes / (copy_ms * 1e-3) / 1e9,
             "note": "reused KV in pinned host memory, each layer's pages copied host-to-device during the step "
                     "(layers left with no rows load nothing); median of the timed steps"}
+
+
+def cold_hbm_leg(eng, s, dev):
+    """The two HBM-bound row kernels of the step timed cold: a 1 GiB buffer is
+    rewritten before each call so that no operand is left in the 256 MiB MALL
+    or the L2s.  Deviation over all N tokens (layer 1, as in the step) and the
+    fusion + scatter over the layer-2 rows (alpha, d and CKSim not written, the
+    new-page slots of the last step rewritten with the same kind of values)."""
+    import numpy as np
+    import torch
+
+    from selective_kv_cache_amd import _lib as K
+
+    esz = 2 if s.dtype == "bf16" else 4
+    Hkv, hd = s.n_kv_heads, s.head_dim
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    c, sh, ds = eng.ctx, eng.sh, eng.desc
+    T = int(eng.k_cap[0]) if eng.B == 1 else eng.T_sel
+    calls = {
+        "deviation": (lambda: K.kvb_deviation_topk(c, sh, ds, eng.B, eng.N, eng.cu_tok, eng.k, eng.k_pool, eng.n_pages,
+                                                   eng.reuse_slot[0], eng.k_cap_d, eng.d, eng.alpha, eng.ranking,
+                                                   eng.s_count, eng.sel[0], eng.cu_rows[0], eng.cursor, eng.ws,
+                                                   eng.ws_bytes),
+                      eng.N * (2.0 * Hkv * hd * esz + 16.0)),
+        "blend_scatter": (lambda: K.kvb_blend_scatter(c, sh, ds, T, eng._n_rows_ptr(0), eng.sel[0], eng.k, eng.v,
+                                                      eng.k_pool,
+                                                      eng.v_pool, eng.n_pages, eng.reuse_slot[1], eng.dst_slot,
+                                                      K.KVB_ALPHA_CURRENT, None, None, None),
+                          T * (6.0 * Hkv * hd * esz + 16.0)),
+    }
+    fn0, _ = calls["deviation"]
+    fn0()  # the layer-1 selection in sel[0]; then layer 2's slot map and new-page slots for it
+    K.kvb_slot_map(c, sh, ds, eng.B, eng.N, T, eng.cu_rows[0], eng.sel[0], eng.reuse_slot[1], eng.new_pages[2],
+                   eng.cu_pages[2], eng.page_table[1], eng.dst_slot)
+    out = {}
+    for name, (fn, nbytes) in calls.items():
+        ms = []
+        for _ in range(6):
+            flush.fill_(1.0)
+            K.kvb_timing_enable(c, name)
+            fn()
+            t = K.kvb_timing_read(c)[name]
+            K.kvb_timing_enable(c, None)
+            ms.append(t["ms"] / t["count"])
+        m = float(np.median(ms[1:]))
+        out[name] = {"ms": m, "bytes": nbytes, "GBps": nbytes / (m * 1e-3) / 1e9,
+                     "frac": nbytes / (m * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    del flush
+    torch.cuda.synchronize()
+    out["note"] = "cold: 1 GiB written before each call; median of 5 calls after one warm-up"
+    return out
 
 
 def cacheblend_leg(w, model, args, dev):
@@ -411,6 +462,7 @@ def main():
         "config": {"workload": w.name, "mode": cfg.mode, "requests": B, "n_tokens": eng.N, "n_layers": s.n_layers,
                    "selected": n_selected, "ratio": w.ratio, "tau": w.tau,
                    "recomputed_row_layers": int(sum(rows_per_layer)), "rows_per_layer": rows_per_layer},
+        "recomputed_row_layers_per_s": float(sum(rows_per_layer)) / (ms * 1e-3),
         "roofline": {"kernel": dominant, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": traffic, "avg_launch_ms": dom_avg_ms,
                      "work_per_launch": dom_work_per_launch},
@@ -421,6 +473,8 @@ def main():
     }
     if not args.no_decode:
         out["decode"] = decode_leg(eng, st)
+    if cfg.mode == "cacheslide":
+        out["hbm_cold"] = cold_hbm_leg(eng, s, dev)
     if not args.no_compile:
         out["compile_step"] = compile_step(eng, args, st, s)
     if not args.no_tier:
