@@ -73,10 +73,11 @@ BOUND = {"gemm_qkv": "mfma", "gemm_oproj": "mfma", "gemm_swiglu": "mfma", "gemm_
          "blend_scatter": "hbm", "deviation": "hbm", "rope": "hbm", "embed": "hbm"}
 
 
-def cpu_baseline(w, eng, rec_state, step_flops):
-    """Time the oracle as it stands on a bounded sample: one selective layer (l = 2)
-    over every selected row, fed the GPU's layer-1 state; scale to the link step by
-    the step's algorithmic FLOPs (realised rows of every layer) over layer 2's."""
+def cpu_baseline(w, eng, rec_state, step_flops, layers=(2, 3, 4)):
+    """Time the oracle as it stands on a bounded sample: the selective layers 2..4
+    (the refresh after layer 4 included) over every selected row, free-running
+    from the GPU's layer-1 state; scaled to the link step by the step's
+    algorithmic FLOPs over the sampled layers'."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_info
@@ -87,28 +88,32 @@ def cpu_baseline(w, eng, rec_state, step_flops):
     s = w.shape
     st = rec_state
     sel = st["sel"]
-    W2 = {k: OL.as_f64(v) for k, v in wl.layer_weights(w, 2, "cuda:0").items()}
-    sm = eng.reuse_slot_h[1]
-    idx = torch.as_tensor(sm, device=eng.k_pool.device, dtype=torch.int64)
-    Kr = OL.as_f64(eng.k_pool[idx // 16, :, idx % 16, :])
-    Vr = OL.as_f64(eng.v_pool[idx // 16, :, idx % 16, :])
     state = OL.WCAState(h=OL.as_f64(st["hidden"]), alpha=OL.as_f64(st["alpha"]), d=OL.as_f64(st["d"]),
-                        ranking=[], cursor=0, S_k=[int(x) for x in sel])
-    t0 = time.perf_counter()
-    OL.wca_layer(state, 2, s, W2, Kr, Vr, w.tau, w.period, s.n_layers)
-    t2 = time.perf_counter() - t0
+                        ranking=[int(x) for x in st["ranking"]], cursor=len(sel), S_k=[int(x) for x in sel])
+    d, F, Hq, Hkv, hd = s.d_model, s.ffn, s.n_q_heads, s.n_kv_heads, s.head_dim
+    per_row = 2.0 * (d * (Hq + 2 * Hkv) * hd + Hq * hd * d + 3 * d * F)
+    t_sum, f_sum = 0.0, 0.0
+    for l in layers:
+        Wl = {k: OL.as_f64(v) for k, v in wl.layer_weights(w, l, "cuda:0").items()}
+        idx = torch.as_tensor(eng.reuse_slot_h[l - 1], device=eng.k_pool.device, dtype=torch.int64)
+        Kr = OL.as_f64(eng.k_pool[idx // 16, :, idx % 16, :])
+        Vr = OL.as_f64(eng.v_pool[idx // 16, :, idx % 16, :])
+        S = np.asarray(state.S_k, dtype=np.int64)
+        f_sum += S.size * per_row + 4.0 * Hq * hd * float(np.sum(S + 1))
+        t0 = time.perf_counter()
+        OL.wca_layer(state, l, s, Wl, Kr, Vr, w.tau, w.period, s.n_layers)
+        t_sum += time.perf_counter() - t0
+        del Wl, Kr, Vr
     info = threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
-    d, F, Hq, Hkv, hd = s.d_model, s.ffn, s.n_q_heads, s.n_kv_heads, s.head_dim
-    N, k = eng.N, len(sel)
-    per_row = 2.0 * (d * (Hq + 2 * Hkv) * hd + Hq * hd * d + 3 * d * F)
-    f2 = k * per_row + 4.0 * Hq * hd * float(np.sum(np.asarray(sel) + 1))
-    t_link = t2 * step_flops / f2
+    k = len(sel)
+    t_link = t_sum * step_flops / f_sum
     return {"value": k / t_link, "unit": "selected-tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"oracle layer 2 over all {k} selected rows of the {N}-token request (float64 numpy, "
-                       f"{threads} BLAS threads): {t2:.2f} s; link time scaled as T2 * FLOPs(link step) / "
-                       f"FLOPs(layer 2) = {t_link:.1f} s"),
-            "measured_s": t2, "extrapolated_link_s": t_link}
+            "sample": (f"oracle layers {list(layers)} (the refresh after layer 4 included) over the {k} selected "
+                       f"rows of the {eng.N}-token request, free-running from the GPU's layer-1 state (float64 "
+                       f"numpy, {threads} BLAS threads): {t_sum:.2f} s; link time scaled as T * FLOPs(link step) / "
+                       f"FLOPs(sampled layers) = {t_link:.1f} s"),
+            "measured_s": t_sum, "extrapolated_link_s": t_link}
 
 
 def decode_leg(eng, st):
@@ -352,7 +357,9 @@ def main():
             layer_rows.append(e.N)
             layer_pos.append(float(sum(n * (n + 1) / 2 for n in e.req_lens)))
             cu = e.cu_rows[e.cur].cpu().numpy()
+            ns = int(e.s_count[0].item())
             state1.update(hidden=e.hidden.clone(), alpha=e.alpha.clone(), d=e.d.clone(),
+                          ranking=e.ranking[:ns].cpu().numpy().copy(),
                           sel=e.sel[e.cur][:cu[-1]].cpu().numpy().copy())
             return
         if cfg.mode == "cacheslide":
@@ -481,7 +488,7 @@ def main():
         out["tier_host"] = tier_host(eng, args, st, n_selected)
     if not args.no_cacheblend and cfg.mode == "cacheslide":
         out["cacheblend"] = cacheblend_leg(w, eng.model, args, dev)
-    if not args.no_cpu_baseline and cfg.mode == "cacheslide":
+    if not args.no_cpu_baseline and cfg.mode == "cacheslide" and eng.B == 1:
         try:
             step_flops = sum(work[k] for k, b in BOUND.items() if b == "mfma")
             out["cpu_baseline"] = cpu_baseline(w, eng, state1, step_flops)
