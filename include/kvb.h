@@ -5,7 +5,7 @@
  *
  * The method: the KV caches of several chunks, each compiled alone from
  * position 0 (EPIC page, section 3.1, compile step), are spliced into one
- * request and a subset of tokens is recomputed (link step).  Two ways of
+ * request and a subset of tokens is recomputed (link step).  Three ways of
  * choosing the subset are served by the same calls:
  *   - CacheSlide Weighted Correction Attention (CacheSlide page, "Method
  *     details", weighted-correction paragraphs and Algorithm 2): layer 1
@@ -15,7 +15,12 @@
  *     alpha_i = d_i / ||K_i^reuse||^2; every four layers a cosine check
  *     retires tokens and refills from the ranking;
  *   - EPIC LegoLink (EPIC page, section 4): the first k tokens of every chunk
- *     but the first, recomputed in every layer, replacing the cached K/V.
+ *     but the first, plus the user's uncached query tokens, recomputed in
+ *     every layer, replacing the cached K/V;
+ *   - the CacheBlend baseline as the EPIC page describes it (section 3.2):
+ *     layer 1 recomputes every token, the tokens whose attention maps under
+ *     the cached and the recomputed keys differ most are recomputed in layers
+ *     2..L, replacing the cached K/V (kvb_attnmap_deviation, kvb_topk).
  * Recomputed K/V go to freshly allocated pages (CacheSlide page, SLIDE
  * implementation paragraph) of a paged cache with 16-token pages.
  *
@@ -112,7 +117,7 @@ kvb_status kvb_workspace_size(kvb_ctx* ctx, const kvb_model_desc* desc, int32_t 
  * HIP events on its stream; filter == NULL turns timing off.  Kernel names:
  * embed, rmsnorm, gemm_qkv, rope, blend_scatter, attention, attention_merge, gemm_oproj, gemm_swiglu,
  * gemm_down, splitk_reduce, deviation, topk_sort, topk_rank, topk_compact, refresh_flag,
- * refresh_compact, slot_copy, slot_scatter. */
+ * refresh_compact, slot_copy, slot_scatter, attnmap, attnmap_reduce. */
 kvb_status kvb_timing_enable(kvb_ctx* ctx, const char* filter);
 /* Waits for the recorded events and folds them into per-kernel totals, then
  * sets *needed to the size of the JSON text {"name": {"count": n, "ms": t}, ...}
