@@ -173,16 +173,25 @@ kvb_status kvb_embed(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int
  * hidden [n_tok, d]; norm_w [d]; w_qkv [(Hq + 2 Hkv) * hd, d] (Q rows, then K,
  * then V); outputs q [T, Hq, hd], k [T, Hkv, hd], v [T, Hkv, hd].
  * If tok_pos != NULL, rotate-half RoPE at position tok_pos[row_tok[r]] is
- * applied to q and k (as kvb_rope).  The per-row result does not depend on
+ * applied to q and k (as kvb_rope).
+ * flags = KVB_QKV_BATCH_INVARIANT (0): the per-row result does not depend on
  * T, on the row's place in the batch or on the other rows (a chunk seen at
- * the same positions in compile and link gets bitwise-equal keys).
+ * the same positions in compile and link gets bitwise-equal keys); use it for
+ * the compile step and for layer 1 of a link step.  flags = KVB_QKV_SPLIT_K:
+ * for bf16 the K reduction may also be split across blocks (partials added in
+ * a fixed order, so results stay deterministic but depend on T); for rows
+ * whose keys are never compared bitwise with another call's (decode tokens,
+ * the selective layers), where a few rows would otherwise leave most of the
+ * GPU idle.
  * norm_w == NULL means unit gains.  With bf16 storage a_r is written to the
  * workspace rounded to bf16 once (ws_bytes >= kvb_workspace_size for T_max
  * rows); float32 storage needs no workspace (ws may be NULL). */
+#define KVB_QKV_BATCH_INVARIANT 0
+#define KVB_QKV_SPLIT_K 1
 kvb_status kvb_qkv_proj(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t T_max,
                         const int32_t* n_rows, const int32_t* row_tok, const void* hidden,
                         const void* norm_w, const void* w_qkv, const int32_t* tok_pos, void* q,
-                        void* k, void* v, void* ws, size_t ws_bytes);
+                        void* k, void* v, void* ws, size_t ws_bytes, int32_t flags);
 
 /* In-place rotate-half RoPE of q [T, Hq, hd] and k [T, Hkv, hd] at positions
  * tok_pos[row_tok[r]]: pair (j, j + hd/2) rotated by pos * base^(-2j/hd).

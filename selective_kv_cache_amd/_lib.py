@@ -24,6 +24,7 @@ KVB_F32, KVB_BF16 = 0, 1
 KVB_ALPHA_LAG, KVB_ALPHA_CURRENT, KVB_ALPHA_ONE = 0, 1, 2
 KVB_REFRESH_LITERAL, KVB_REFRESH_DISSIM = 0, 1
 KVB_COPY_H2D, KVB_COPY_D2H = 0, 1
+KVB_QKV_BATCH_INVARIANT, KVB_QKV_SPLIT_K = 0, 1
 
 
 class KvbError(RuntimeError):
@@ -55,7 +56,7 @@ _SIGS = {
     "kvb_pool_free_count": ([P, POINTER(c_int32)], I),
     "kvb_pages_copy": ([P, P, P, I, P, P, P, P, P, I], I),
     "kvb_embed": ([P, P, P, I, P, P, P, I, P, P], I),
-    "kvb_qkv_proj": ([P, P, P, I, P, P, P, P, P, P, P, P, P, P, c_size_t], I),
+    "kvb_qkv_proj": ([P, P, P, I, P, P, P, P, P, P, P, P, P, P, c_size_t, I], I),
     "kvb_rope": ([P, P, P, I, P, P, P, P, P], I),
     "kvb_blend_scatter": ([P, P, P, I, P, P, P, P, P, P, I, P, P, I, P, P, P], I),
     "kvb_sparse_query_attn": ([P, P, P, I, P, P, P, P, P, P, I, P, c_float, P, P, c_size_t], I),
@@ -215,9 +216,9 @@ def kvb_embed(ctx, stream, desc, T_max, n_rows, row_tok, tokens, vocab, table, h
 
 
 def kvb_qkv_proj(ctx, stream, desc, T_max, n_rows, row_tok, hidden, norm_w, w_qkv, tok_pos, q, k, v,
-                 ws=None, ws_bytes=0):
+                 ws=None, ws_bytes=0, flags=0):
     _call("kvb_qkv_proj", ctx, stream, desc, T_max, n_rows, row_tok, hidden, norm_w, w_qkv,
-          tok_pos, q, k, v, ws, ws_bytes)
+          tok_pos, q, k, v, ws, ws_bytes, flags)
 
 
 def kvb_rope(ctx, stream, desc, T_max, n_rows, row_tok, tok_pos, q, k):

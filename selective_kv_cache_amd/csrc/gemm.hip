@@ -709,7 +709,7 @@ kvb_status launch_rope(hipStream_t st, int T_max, const int32_t* n_rows, const i
 template <class T>
 static kvb_status qkv_impl(hipStream_t st, const kvb_model_desc* d, int T_max, const int32_t* n_rows,
                            const int32_t* row_tok, const void* hidden, const void* norm_w, const void* w_qkv,
-                           const int32_t* tok_pos, void* q, void* k, void* v, void* ws) {
+                           const int32_t* tok_pos, void* q, void* k, void* v, void* ws, bool split_k) {
   GemmArgs<T> p{};
   p.B = (const T*)w_qkv;
   p.M_max = T_max;
@@ -728,7 +728,9 @@ static kvb_status qkv_impl(hipStream_t st, const kvb_model_desc* d, int T_max, c
     KVB_TRY(rmsnorm_rows(st, (const bf16_t*)hidden, row_tok, n_rows, T_max, d->d_model, (const bf16_t*)norm_w,
                          d->rms_eps, a));
     p.A = a;
-    KVB_TRY((run_bf16<EPI_QKV, false>(st, p, "gemm_qkv")));
+    // split-K partials after the normalised rows, only when the caller allows it
+    void* sk_ws = split_k ? (void*)((char*)ws + ws_qkv_bytes(d, T_max)) : nullptr;
+    KVB_TRY((run_bf16<EPI_QKV, false>(st, p, "gemm_qkv", sk_ws)));
   } else {
     p.A = (const T*)hidden;
     p.a_rows = row_tok;
@@ -810,23 +812,25 @@ using namespace kvb;
 extern "C" kvb_status kvb_qkv_proj(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t T_max,
                                    const int32_t* n_rows, const int32_t* row_tok, const void* hidden,
                                    const void* norm_w, const void* w_qkv, const int32_t* tok_pos, void* q, void* k,
-                                   void* v, void* ws, size_t ws_bytes) {
+                                   void* v, void* ws, size_t ws_bytes, int32_t flags) {
   KVB_TRY(check_ctx(ctx));
   KVB_TRY(check_desc(desc));
   if (T_max < 0) return fail(KVB_ERR_INVALID_ARG, "T_max < 0");
+  if (flags != KVB_QKV_BATCH_INVARIANT && flags != KVB_QKV_SPLIT_K) return fail(KVB_ERR_INVALID_ARG, "bad flags");
   if (T_max == 0) return KVB_OK;
   KVB_CHECK_PTR(hidden, "hidden");
   KVB_CHECK_PTR(w_qkv, "w_qkv");
   KVB_CHECK_PTR(q, "q");
   KVB_CHECK_PTR(k, "k");
   KVB_CHECK_PTR(v, "v");
-  const size_t need = ws_qkv_bytes(desc, T_max);
+  const bool split_k = flags == KVB_QKV_SPLIT_K && desc->dtype == KVB_BF16;
+  const size_t need = ws_qkv_bytes(desc, T_max) + (split_k ? ws_gemm_sk_bytes(0) : 0);
   if (need && (!ws || ws_bytes < need)) return fail(KVB_ERR_WORKSPACE, "kvb_qkv_proj workspace too small");
   CtxScope scope(ctx);
   hipStream_t st = (hipStream_t)stream;
   if (desc->dtype == KVB_BF16)
-    return qkv_impl<bf16_t>(st, desc, T_max, n_rows, row_tok, hidden, norm_w, w_qkv, tok_pos, q, k, v, ws);
-  return qkv_impl<float>(st, desc, T_max, n_rows, row_tok, hidden, norm_w, w_qkv, tok_pos, q, k, v, ws);
+    return qkv_impl<bf16_t>(st, desc, T_max, n_rows, row_tok, hidden, norm_w, w_qkv, tok_pos, q, k, v, ws, split_k);
+  return qkv_impl<float>(st, desc, T_max, n_rows, row_tok, hidden, norm_w, w_qkv, tok_pos, q, k, v, ws, false);
 }
 
 extern "C" kvb_status kvb_mlp(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t T_max,

@@ -222,7 +222,7 @@ kvb_status kvb_workspace_size(kvb_ctx* ctx, const kvb_model_desc* desc, int32_t 
   KVB_CHECK_PTR(bytes, "bytes");
   if (max_rows < 0 || max_tokens < 0 || max_requests < 0) return fail(KVB_ERR_INVALID_ARG, "negative size");
   size_t b = ws_mlp_bytes(desc, max_rows, reinterpret_cast<Ctx*>(ctx)->n_cu);
-  b = std::max(b, ws_qkv_bytes(desc, max_rows));
+  b = std::max(b, ws_qkv_bytes(desc, max_rows) + (desc->dtype == KVB_BF16 ? ws_gemm_sk_bytes(0) : 0));
   b = std::max(b, ws_topk_bytes(max_tokens, max_requests));
   b = std::max(b, ws_refresh_bytes(max_tokens, max_requests));
   b = std::max(b, ws_attn_bytes(desc, max_rows, reinterpret_cast<Ctx*>(ctx)->n_cu));

@@ -382,8 +382,11 @@ class LinkEngine:
         self.slot_map = self.page_table[l - 1]
         K.kvb_slot_map(c, sh, ds, self.B, self.N, T, cu_rows, rows, self.reuse_slot[l - 1], self.new_pages[l],
                        self.cu_pages[l], self.slot_map, self.dst_slot)
+        # layer 1's keys must be bitwise those of the compile step (chunk 0 deviates by
+        # exactly 0): batch-invariant there; the selective layers may split K
+        flags = K.KVB_QKV_BATCH_INVARIANT if l == 1 else K.KVB_QKV_SPLIT_K
         K.kvb_qkv_proj(c, sh, ds, T, n_rows, rows, self.hidden, W["norm1"], W["w_qkv"], self.pos_l, self.q, self.k,
-                       self.v, self.ws, self.ws_bytes)
+                       self.v, self.ws, self.ws_bytes, flags)
         K.kvb_blend_scatter(c, sh, ds, T, n_rows, rows, self.k, self.v, self.k_pool, self.v_pool, self.n_pages,
                             src_slot, self.dst_slot, alpha_mode, alpha, d_out, cksim_out)
         K.kvb_sparse_query_attn(c, sh, ds, T, n_rows, rows, self.lo_l, self.q, self.k_pool, self.v_pool,
@@ -581,7 +584,7 @@ class LinkEngine:
         for l in range(1, L + 1):
             W = m.layers[l - 1]
             K.kvb_qkv_proj(c, sh, ds, B, None, None, self.hidden_dec, W["norm1"], W["w_qkv"], pos_d, self.q, self.k,
-                           self.v, self.ws, self.ws_bytes)
+                           self.v, self.ws, self.ws_bytes, K.KVB_QKV_SPLIT_K)
             K.kvb_blend_scatter(c, sh, ds, B, None, None, self.k, self.v, self.k_pool, self.v_pool, self.n_pages,
                                 None, slots_d[l - 1], K.KVB_ALPHA_ONE, None, None, None)
             K.kvb_sparse_query_attn(c, sh, ds, B, None, rows_d, self.lo_dec, self.q, self.k_pool, self.v_pool,

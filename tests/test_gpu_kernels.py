@@ -71,11 +71,13 @@ def weights(shape, g):
 # ------------------------------------------------------------------ Q/K/V projection + RoPE
 
 @pytest.mark.parametrize("name", ["bf16", "bf16_hd64", "fp32"])
-def test_qkv_proj_rope(ctx, name):
+@pytest.mark.parametrize("flags,T_max,n_valid", [(K.KVB_QKV_BATCH_INVARIANT, 200, 173), (K.KVB_QKV_SPLIT_K, 200, 173),
+                                                 (K.KVB_QKV_SPLIT_K, 7, 5), (K.KVB_QKV_SPLIT_K, 1, 1)])
+def test_qkv_proj_rope(ctx, name, flags, T_max, n_valid):
     s = SHAPES[name]
     g = np.random.default_rng(11)
     desc = K.model_desc(s)
-    n_tok, T_max, n_valid = 300, 200, 173
+    n_tok = 300
     dt = tdt(s)
     hidden = rand((n_tok, s.d_model), g, dtype=dt).to(DEV)
     W = weights(s, g)
@@ -85,9 +87,18 @@ def test_qkv_proj_rope(ctx, name):
     k = torch.full((T_max, s.n_kv_heads, s.head_dim), 7.0, dtype=dt, device=DEV)
     v = torch.full((T_max, s.n_kv_heads, s.head_dim), 7.0, dtype=dt, device=DEV)
     ws, wsb = workspace(ctx, desc, T_max)
+    K.kvb_timing_enable(ctx, "splitk")
     K.kvb_qkv_proj(ctx, sh(), desc, T_max, i32([n_valid]), i32(rows), hidden, W["norm1"], W["w_qkv"], i32(pos),
-                   q, k, v, ws, wsb)
+                   q, k, v, ws, wsb, flags)
+    split = "splitk_reduce" in K.kvb_timing_read(ctx)
+    K.kvb_timing_enable(ctx, None)
     torch.cuda.synchronize()
+    # the batch-invariant projection never splits K; a single row of the
+    # 512-wide bf16 shape does (the planner's choice elsewhere)
+    if flags == K.KVB_QKV_BATCH_INVARIANT or s.dtype == "fp32":
+        assert not split
+    elif name == "bf16" and T_max == 1:
+        assert split
     Wn = {kk: np64(vv) for kk, vv in W.items()}
     rq, rk, rv = OM.qkv(np64(hidden)[rows[:n_valid]], pos[rows[:n_valid]], Wn, s)
     assert max_rel_err(q[:n_valid], rq) < TOL[s.dtype]

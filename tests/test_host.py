@@ -127,6 +127,9 @@ def test_null_and_size_checks_enqueue_nothing(lib):
     assert e.value.status == K.KVB_ERR_WORKSPACE
     # zero-size calls are valid no-ops
     K.kvb_qkv_proj(FAKE_CTX, None, d, 0, None, None, None, None, None, None, None, None, None)
+    with pytest.raises(K.KvbError) as e:  # unknown flags
+        K.kvb_qkv_proj(FAKE_CTX, None, d, 4, None, None, 1, 1, 1, None, 1, 1, 1, None, 0, 2)
+    assert e.value.status == K.KVB_ERR_INVALID_ARG and "flags" in K.kvb_last_error()
     K.kvb_mlp(FAKE_CTX, None, d, 0, None, None, None, None, None, None, None, None, None, 0)
 
 
