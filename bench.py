@@ -120,24 +120,31 @@ def decode_leg(eng, st):
     """Decode continuation after the last link step: DECODE_TOKENS tokens per
     request, each a full pass over every layer at one row per request,
     attending to the link step's page table.  New tokens go to new pages (the
-    HBM-resident cache is not overwritten).  HIP events on the engine stream."""
+    HBM-resident cache is not overwritten).  The step is recorded as a HIP
+    graph on the first token and replayed for the others; the same tokens are
+    also timed with eager launches.  HIP events on the engine stream."""
     import numpy as np
     import torch
 
-    eng.decode_init(overwrite_first=False)
     toks = np.random.default_rng(11).integers(0, eng.shape.vocab, size=(DECODE_TOKENS, eng.B))
-    eng.decode_step(toks[0])  # first step: warm-up
     n = DECODE_TOKENS - 1
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a.record(st)
-    for t in range(1, DECODE_TOKENS):
-        eng.decode_step(toks[t])
-    b.record(st)
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / n
-    return {"ms_per_decode_step": ms, "tokens_per_s": eng.B / (ms * 1e-3), "requests": eng.B, "steps_timed": n,
-            "note": "one token per request per step after the link step, placed on new pages"}
+    out = {}
+    for graph in (True, False):
+        eng.decode_init(overwrite_first=False, graph=graph)
+        eng.decode_step(toks[0])  # first step: warm-up (and the recording)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(st)
+        for t in range(1, DECODE_TOKENS):
+            eng.decode_step(toks[t])
+        b.record(st)
+        torch.cuda.synchronize()
+        out["graph" if graph else "eager"] = a.elapsed_time(b) / n
+    ms = out["graph"]
+    return {"ms_per_decode_step": ms, "tokens_per_s": eng.B / (ms * 1e-3), "ms_per_decode_step_eager": out["eager"],
+            "requests": eng.B, "steps_timed": n,
+            "note": "one token per request per step after the link step, placed on new pages; HIP graph replays "
+                    "(eager launches alongside)"}
 
 
 def compile_step(eng, args, st, s):

@@ -492,11 +492,16 @@ class LinkEngine:
         return self.page_table
 
     # ------------------------------------------------------------------ decode continuation
-    def decode_init(self, overwrite_first: bool = True, consume_cache: bool = False):
+    def decode_init(self, overwrite_first: bool = True, consume_cache: bool = False, graph: bool = False):
         """Prepare decode steps after a link step (CacheSlide page, SLIDE: decode
         writes its K/V first into the original slots of the tokens recomputed in
         that layer, whose reused K/V the new pages superseded, and only then into
         newly allocated pages).
+
+        graph=True records one decode step (the page-table update and every
+        layer's launches) as a HIP graph on its first call and replays it for
+        each token; the step's token ids, rows, positions and slots reach the
+        graph through fixed device buffers written before each replay.
 
         Overwriting those slots changes the compile pages, so it needs either the
         host tier (every link step reloads them) or consume_cache=True.  Slots of
@@ -549,6 +554,14 @@ class LinkEngine:
         self.lo_dec = _i32(lo_dec, dev)
         self.dec_slots_h = np.full((L, B, md), -1, dtype=np.int64)  # slot of decode token t per layer, request
         self.hidden_dec = torch.zeros((B, self.shape.d_model), dtype=self.tdtype, device=dev)
+        # per-step inputs of a decode step, in fixed buffers (what a recorded graph reads)
+        self._dec_tok = torch.zeros(B, dtype=torch.int32, device=dev)
+        self._dec_rows = torch.zeros(B, dtype=torch.int32, device=dev)
+        self._dec_rows64 = torch.zeros(B, dtype=torch.int64, device=dev)
+        self._dec_pos = torch.zeros(B, dtype=torch.int32, device=dev)
+        self._dec_slots = torch.zeros((L, B), dtype=torch.int32, device=dev)
+        self._dec_graph_on = graph
+        self._dec_graph = None
 
     def _dec_slot(self, l: int, b: int, t: int) -> int:
         holes = self.dec_holes[l][b]
@@ -569,30 +582,52 @@ class LinkEngine:
         B, L, t = self.B, self.L, self.dec_t
         if t >= self.max_decode:
             raise ValueError("max_decode tokens already decoded")
-        c, sh, ds, dev, m = self.ctx, self.sh, self.desc, self.device, self.model
         rows = self.dec_cu + np.array(self.req_lens) + t            # decode-space ids of the new tokens
         slots = np.array([[self._dec_slot(l, b, t) for b in range(B)] for l in range(1, L + 1)], dtype=np.int64)
         self.dec_slots_h[:, :, t] = slots
-        pt = self.pt_dec
         with torch.cuda.stream(self.stream):
-            pt[:, torch.as_tensor(rows, device=dev)] = _i32(slots, dev)
-        rows_d = _i32(rows, dev)
-        pos_d = _i32(np.array(self.req_lens) + t, dev)
-        tok_d = _i32(np.asarray(tokens, dtype=np.int64), dev)
-        slots_d = _i32(slots, dev)
-        K.kvb_embed(c, sh, ds, B, None, None, tok_d, self.shape.vocab, m.embedding, self.hidden_dec)
+            self._dec_tok.copy_(torch.as_tensor(np.asarray(tokens, dtype=np.int32)))
+            self._dec_rows.copy_(torch.as_tensor(rows.astype(np.int32)))
+            self._dec_rows64.copy_(torch.as_tensor(rows.astype(np.int64)))
+            self._dec_pos.copy_(torch.as_tensor((np.array(self.req_lens) + t).astype(np.int32)))
+            self._dec_slots.copy_(torch.as_tensor(slots.astype(np.int32)))
+        if not self._dec_graph_on:
+            self._decode_body(self.stream)
+        elif self._dec_graph is None:
+            # first step: run it, then record it (a step is idempotent: the embedding
+            # resets the rows and every write repeats the same values)
+            self._decode_body(self.stream)
+            self.stream.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self._decode_body(torch.cuda.current_stream())
+            self._dec_graph = g
+        else:
+            with torch.cuda.stream(self.stream):
+                self._dec_graph.replay()
+        self.dec_t = t + 1
+        return self.hidden_dec
+
+    def _decode_body(self, stream):
+        """The launches of one decode step on `stream`, reading its per-step
+        inputs from the fixed decode buffers."""
+        B, L = self.B, self.L
+        c, ds, m = self.ctx, self.desc, self.model
+        sh = K.stream_handle(stream)
+        pt = self.pt_dec
+        with torch.cuda.stream(stream):
+            pt.index_copy_(1, self._dec_rows64, self._dec_slots)
+        K.kvb_embed(c, sh, ds, B, None, None, self._dec_tok, self.shape.vocab, m.embedding, self.hidden_dec)
         for l in range(1, L + 1):
             W = m.layers[l - 1]
-            K.kvb_qkv_proj(c, sh, ds, B, None, None, self.hidden_dec, W["norm1"], W["w_qkv"], pos_d, self.q, self.k,
-                           self.v, self.ws, self.ws_bytes, K.KVB_QKV_SPLIT_K)
+            K.kvb_qkv_proj(c, sh, ds, B, None, None, self.hidden_dec, W["norm1"], W["w_qkv"], self._dec_pos, self.q,
+                           self.k, self.v, self.ws, self.ws_bytes, K.KVB_QKV_SPLIT_K)
             K.kvb_blend_scatter(c, sh, ds, B, None, None, self.k, self.v, self.k_pool, self.v_pool, self.n_pages,
-                                None, slots_d[l - 1], K.KVB_ALPHA_ONE, None, None, None)
-            K.kvb_sparse_query_attn(c, sh, ds, B, None, rows_d, self.lo_dec, self.q, self.k_pool, self.v_pool,
+                                None, self._dec_slots[l - 1], K.KVB_ALPHA_ONE, None, None, None)
+            K.kvb_sparse_query_attn(c, sh, ds, B, None, self._dec_rows, self.lo_dec, self.q, self.k_pool, self.v_pool,
                                     self.n_pages, pt[l - 1], self.scale, self.o, self.ws, self.ws_bytes)
             K.kvb_mlp(c, sh, ds, B, None, None, self.o, W["w_o"], self.hidden_dec, W["norm2"], W["w_gate_up"],
                       W["w_down"], self.ws, self.ws_bytes)
-        self.dec_t = t + 1
-        return self.hidden_dec
 
     # ------------------------------------------------------------------ results
     def selected(self, which: Optional[int] = None) -> List[np.ndarray]:

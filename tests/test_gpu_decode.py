@@ -183,6 +183,32 @@ def test_decode_legolink_query_suffix_has_no_slot_to_overwrite():
     eng.close()
 
 
+def test_decode_graph_replays_match_eager():
+    """A decode step recorded as a HIP graph and replayed for later tokens gives
+    the eager steps' hidden rows and placement bit for bit, replay after replay
+    (host work and synchronisations between the replays)."""
+    w = wl.small_bf16(n_layers=3)
+    n_dec = 6
+    eng, E, layers = engine(w, "hbm", n_dec)
+    eng.run_compile()
+    toks = np.random.default_rng(3).integers(0, w.shape.vocab, size=(n_dec, eng.B))
+    runs = []
+    for graph in (False, True):
+        eng.run_link()
+        eng.decode_init(overwrite_first=False, graph=graph)
+        hs = []
+        for t in range(n_dec):
+            hs.append(eng.decode_step(toks[t]).clone())
+            torch.cuda.synchronize()
+            hs[-1] = hs[-1].cpu()
+        runs.append((hs, eng.dec_slots_h.copy(), eng.pt_dec.cpu().clone()))
+    (h0, s0, p0), (h1, s1, p1) = runs
+    assert np.array_equal(s0, s1) and torch.equal(p0, p1)
+    for t in range(n_dec):
+        assert torch.equal(h0[t], h1[t]), t
+    eng.close()
+
+
 def test_decode_overwrite_needs_a_reloadable_cache():
     w = wl.tiny(n_layers=2)
     eng, E, layers = engine(w, "hbm", 2)
