@@ -11,7 +11,7 @@
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: a lane ends with 16 scores of
 //     one query, which is already the B-operand layout of O^T = V^T P^T, so
 //     probabilities stay in registers; softmax statistics need one xor-32
-//     exchange per query;
+//     exchange per query (a lane-half swap, not an LDS permute);
 //   * V stays row-major in LDS; V^T operands come from the transposing LDS
 //     read of gfx950;
 //   * only tiles that cross a query's causal edge or its lower bound, or that
@@ -72,6 +72,22 @@ struct AttnGeom {
 };
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// this lane's index, recomputed where it is needed: a kept copy would hold a
+// register through the whole loop
+__device__ __forceinline__ int lane_id_opaque() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+// max of v over lanes l and l ^ 32 without an LDS round trip: the half swap of
+// gfx950 leaves one half of v in both halves of one result and the other half
+// in both halves of the other
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 // gfx950 transposing LDS read: in every 16-lane group, lane i receives element
 // i % 4 of the 8 bytes addressed by lanes i / 4 + 4 s of the group, s = 0..3.
@@ -207,12 +223,11 @@ attn_bf16_kernel(AttnArgs a) {
   wait_vmcnt<0>();
 
   // The per-lane parts of the load addresses are recomputed at every issue from
-  // `ln`, which the empty asm makes opaque: hoisted out of the loop they would
-  // take registers for the whole loop.
+  // the lane index: hoisted out of the loop they would take registers for the
+  // whole loop.
   // slot indices of tile X's 8 keys of this wave -> s_slot[X % 3][wave] (1 load per lane)
   auto issue_slots = [&](int X) {
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
+    const int ln = lane_id_opaque();
     int key = kbase + X * AKT + wave * 8 + (ln & 7);
     key = key < kmax ? key : kmax;  // keys past the block's last query are masked anyway
     dma4(a.slot_map + key, __builtin_amdgcn_readfirstlane(lds_addr(&s_slot[X % ANST][wave][0])));
@@ -224,8 +239,7 @@ attn_bf16_kernel(AttnArgs a) {
     uint8_t* kb = s_kv + st * TILE;
     uint8_t* vb = s_kv + (ANST + st) * TILE;
     uint32_t bad = 0;
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
+    const int ln = lane_id_opaque();
 #pragma unroll
     for (int i = 0; i < IPW; i++) {
       const int rl = i * RPI + ln / CPR;  // row among the wave's 8
@@ -315,19 +329,23 @@ attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; r++) sv[r] = sacc[r];
       if (need_mask) {
-        // invalid bits of this lane's 16 keys: bit 8 (r / 4) + r % 4 of iv
+        // register r holds key j0 + 32 kt + 4 g2 + kk, kk = 8 (r / 4) + r % 4:
+        // outside [qlo, qpos], or bit kk of iv set (no valid slot), it is
+        // excluded; the tests are selects, not branches
+        const int kb = j0 + 32 * kt + 4 * g2;
+        const int dq = qpos - kb, dl = qlo - kb;
         const uint32_t iv = (uint32_t)(inval >> (kt * 32 + 4 * g2));
 #pragma unroll
         for (int r = 0; r < 16; r++) {
-          const int kk = kt * 32 + 8 * (r >> 2) + 4 * g2 + (r & 3);
-          const int key = j0 + kk;
-          if (key > qpos || key < qlo || ((iv >> (8 * (r >> 2) + (r & 3))) & 1u)) sv[r] = -INFINITY;
+          const int kk = 8 * (r >> 2) + (r & 3);
+          const bool bad = (kk > dq) | (kk < dl) | (((iv >> kk) & 1u) != 0u);
+          sv[r] = bad ? -INFINITY : sv[r];
         }
       }
       float mx = sv[0];
 #pragma unroll
       for (int r = 1; r < 16; r++) mx = fmaxf(mx, sv[r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = max_xor32(mx);
       const float mxs = mx * a.scale_log2;
       const bool grow = mxs > moff + 8.f;
       const float corr = grow ? __builtin_amdgcn_exp2f(moff - mxs) : 1.f;

@@ -152,11 +152,62 @@ __global__ void __launch_bounds__(256) rmsnorm_rows_kernel(const bf16_t* __restr
   }
 }
 
+// The same arithmetic in the same order for K = 512 CPL: the whole row (and
+// the gains) is loaded into registers up front, so the row costs one memory
+// latency instead of one per chunk.
+template <int CPL>
+__global__ void __launch_bounds__(256) rmsnorm_rows_reg_kernel(const bf16_t* __restrict__ x,
+                                                               const int32_t* __restrict__ a_rows,
+                                                               const int32_t* __restrict__ n_rows, int T_max,
+                                                               const bf16_t* __restrict__ g, float eps,
+                                                               bf16_t* __restrict__ y) {
+  constexpr int K = 512 * CPL;
+  const int r = blockIdx.x * 4 + (int)(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (r >= row_count(n_rows, T_max)) return;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)(a_rows ? a_rows[r] : r) * K);
+  uint4* yr = reinterpret_cast<uint4*>(y + (size_t)r * K);
+  const uint4* gr = reinterpret_cast<const uint4*>(g);
+  uint4 xv[CPL], gv[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; i++) xv[i] = xr[lane + 64 * i];
+  if (g) {
+#pragma unroll
+    for (int i = 0; i < CPL; i++) gv[i] = gr[lane + 64 * i];
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < CPL; i++) {
+    float f[8];
+    unpack8(xv[i], f);
+#pragma unroll
+    for (int e = 0; e < 8; e++) s += f[e] * f[e];
+  }
+  s = wave_sum(s);
+  const float rinv = 1.f / sqrtf(s / (float)K + eps);
+#pragma unroll
+  for (int i = 0; i < CPL; i++) {
+    float f[8], w[8];
+    unpack8(xv[i], f);
+    if (g) unpack8(gv[i], w);
+#pragma unroll
+    for (int e = 0; e < 8; e++) f[e] = g ? f[e] * rinv * w[e] : f[e] * rinv;
+    yr[lane + 64 * i] = make_uint4(pack2_bf16(f[0], f[1]), pack2_bf16(f[2], f[3]), pack2_bf16(f[4], f[5]),
+                                   pack2_bf16(f[6], f[7]));
+  }
+}
+
 static kvb_status rmsnorm_rows(hipStream_t st, const bf16_t* x, const int32_t* a_rows, const int32_t* n_rows,
                                int T_max, int K, const bf16_t* g, float eps, bf16_t* y) {
   {
     LaunchTimer lt(st, "rmsnorm");
-    rmsnorm_rows_kernel<<<cdiv(T_max, 4), 256, 0, st>>>(x, a_rows, n_rows, T_max, K, g, eps, y);
+    const dim3 grid(cdiv(T_max, 4)), block(256);
+    switch (K) {
+      case 2048: rmsnorm_rows_reg_kernel<4><<<grid, block, 0, st>>>(x, a_rows, n_rows, T_max, g, eps, y); break;
+      case 4096: rmsnorm_rows_reg_kernel<8><<<grid, block, 0, st>>>(x, a_rows, n_rows, T_max, g, eps, y); break;
+      case 5120: rmsnorm_rows_reg_kernel<10><<<grid, block, 0, st>>>(x, a_rows, n_rows, T_max, g, eps, y); break;
+      case 8192: rmsnorm_rows_reg_kernel<16><<<grid, block, 0, st>>>(x, a_rows, n_rows, T_max, g, eps, y); break;
+      default: rmsnorm_rows_kernel<<<grid, block, 0, st>>>(x, a_rows, n_rows, T_max, K, g, eps, y);
+    }
   }
   return check_launch("rmsnorm_rows_kernel");
 }
