@@ -576,6 +576,117 @@ static kvb_status launch_splitk_reduce(hipStream_t st, const GemmArgs<bf16_t>& p
   return check_launch("splitk_reduce_kernel");
 }
 
+// One-row product (M_max = 1, on launches that may split K, so no bitwise
+// tie to the batched result is owed): the weights stream once from HBM and x
+// sits in LDS.  Each wave owns GV_NW consecutive outputs (with SwiGLU their
+// gate and up rows too); lane l takes the 16-byte chunks l, l + 64, ... of
+// every row, four v_dot2_f32_bf16 per chunk, then one butterfly per row.  The
+// epilogues are the tiled kernel's.
+constexpr int GV_NW = 2, GV_WAVES = 4;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot8_bf16(const uint4& w, const uint4& x, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x), __builtin_bit_cast(bf16x2_t, x.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.y), __builtin_bit_cast(bf16x2_t, x.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.z), __builtin_bit_cast(bf16x2_t, x.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.w), __builtin_bit_cast(bf16x2_t, x.w), acc, false);
+  return acc;
+}
+
+template <int MODE, bool DUAL>
+__global__ void __launch_bounds__(64 * GV_WAVES) gemv_bf16_kernel(GemmArgs<bf16_t> p) {
+  extern __shared__ __align__(16) uint8_t gv_x[];
+  if (row_count(p.n_rows, p.M_max) < 1) return;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int C = p.K / 8;  // 16-byte chunks per row
+  const uint4* xg = reinterpret_cast<const uint4*>(p.A);
+  uint4* xs = reinterpret_cast<uint4*>(gv_x);
+  {
+    // four 16-byte loads in flight per thread, then the tail
+    constexpr int TH = 64 * GV_WAVES;
+    int c = t;
+    for (; c + 3 * TH < C; c += 4 * TH) {
+      uint4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; u++) v[u] = xg[c + u * TH];
+#pragma unroll
+      for (int u = 0; u < 4; u++) xs[c + u * TH] = v[u];
+    }
+    for (; c < C; c += TH) xs[c] = xg[c];
+  }
+  __syncthreads();
+  const int nb = (blockIdx.x * GV_WAVES + wave) * GV_NW;
+  if (nb >= p.N) return;
+  constexpr int R = DUAL ? 2 * GV_NW : GV_NW;  // rows i < GV_NW: B; the rest: B2
+  const uint4* wr[R];
+#pragma unroll
+  for (int i = 0; i < GV_NW; i++) {
+    const int n = nb + i < p.N ? nb + i : p.N - 1;
+    wr[i] = reinterpret_cast<const uint4*>(p.B + (size_t)n * p.K);
+    if (DUAL) wr[GV_NW + i] = reinterpret_cast<const uint4*>(p.B2 + (size_t)n * p.K);
+  }
+  float acc[R];
+#pragma unroll
+  for (int i = 0; i < R; i++) acc[i] = 0.f;
+  // whole batches of 4 chunks per lane: all 4 R weight loads issued before
+  // any is used; then single chunks
+  int c = lane;
+  for (; c + 192 < C; c += 256) {
+    uint4 w[4][R];
+#pragma unroll
+    for (int u = 0; u < 4; u++)
+#pragma unroll
+      for (int i = 0; i < R; i++) w[u][i] = wr[i][c + 64 * u];
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const uint4 xv = xs[c + 64 * u];
+#pragma unroll
+      for (int i = 0; i < R; i++) acc[i] = dot8_bf16(w[u][i], xv, acc[i]);
+    }
+  }
+  for (; c < C; c += 64) {
+    const uint4 xv = xs[c];
+#pragma unroll
+    for (int i = 0; i < R; i++) acc[i] = dot8_bf16(wr[i][c], xv, acc[i]);
+  }
+  float v = 0.f, v2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < GV_NW; i++) {
+    const float a = wave_sum(acc[i]);
+    const float b = DUAL ? wave_sum(acc[GV_NW + i]) : 0.f;
+    if (lane == i) {
+      v = a;
+      v2 = b;
+    }
+  }
+  const int n = nb + lane;
+  if (lane >= GV_NW || n >= p.N) return;
+  bf16_t* dst;
+  if (MODE == EPI_SWIGLU) {
+    v = DUAL ? silu_bf16(v) * v2 : v;
+    dst = p.out0 + n;
+  } else if (MODE == EPI_QKV) {
+    if (n < p.n0) dst = p.out0 + n;
+    else if (n < p.n1) dst = p.out1 + (n - p.n0);
+    else dst = p.out2 + (n - p.n1);
+  } else {
+    const int rr = (MODE == EPI_RESID && p.resid_rows) ? p.resid_rows[0] : 0;
+    v += bf2f(p.resid[(size_t)rr * p.ldr + n]);
+    const int orow = (MODE == EPI_SCATTER && p.out_rows) ? p.out_rows[0] : 0;
+    dst = p.out0 + (size_t)orow * p.ldo + n;
+  }
+  *dst = (bf16_t)(pack2_bf16(v, 0.f) & 0xffffu);
+}
+
+template <int MODE, bool DUAL>
+static kvb_status launch_gemv(hipStream_t st, const GemmArgs<bf16_t>& p, const char* name) {
+  {
+    LaunchTimer lt(st, name);
+    gemv_bf16_kernel<MODE, DUAL><<<cdiv(p.N, GV_NW * GV_WAVES), 64 * GV_WAVES, (size_t)p.K * 2, st>>>(p);
+  }
+  return check_launch("gemv_bf16_kernel");
+}
+
 using TileL = Tile<256, 256, 2, 64, 2>;     // waves 128 x 64, 2 stages of K 64
 using TileL192 = Tile<192, 256, 2, 64, 2>;  // waves 96 x 64
 using TileM = Tile<256, 128, 4, 32, 4>;  // waves 64 x 64, 4 stages of K 32
@@ -608,6 +719,8 @@ static kvb_status run_bf16(hipStream_t st, const GemmArgs<bf16_t>& p, const char
   const size_t b_span = (DUAL ? (size_t)(p.B2 - p.B) + (size_t)p.N * p.K : (size_t)p.N * p.K) * 2;
   if (p.a_rows || (size_t)p.M_max * p.K * 2 > 0xffffffffu || b_span > 0xffffffffu)
     return fail(KVB_ERR_UNSUPPORTED, std::string(name) + ": operands beyond 4 GiB of one base");
+  // one row on a launch that may split K: the weight-streaming product
+  if (sk_ws && p.M_max == 1 && p.K % 8 == 0 && p.K <= 32768) return launch_gemv<MODE, DUAL>(st, p, name);
   Ctx* c = current_ctx();
   const long cus = c ? c->n_cu : 256;
   struct Shape { int bm, bn, kb; double eff, rate; bool split; };

@@ -21,6 +21,10 @@ DEV = "cuda:0"
 SHAPES = {
     "bf16": wl.ModelShape(n_layers=1, d_model=512, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=1536, dtype="bf16"),
     "bf16_hd64": wl.ModelShape(n_layers=1, d_model=256, n_q_heads=8, n_kv_heads=1, head_dim=64, ffn=512, dtype="bf16"),
+    # wide enough that a one-row product runs whole 4-chunk batches per lane
+    # (d = 2048) and a ragged tail (ffn = 2816)
+    "bf16_wide": wl.ModelShape(n_layers=1, d_model=2048, n_q_heads=16, n_kv_heads=4, head_dim=128, ffn=2816,
+                               dtype="bf16"),
     "fp32": wl.ModelShape(n_layers=1, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn=688, dtype="fp32"),
 }
 
@@ -70,7 +74,7 @@ def weights(shape, g):
 
 # ------------------------------------------------------------------ Q/K/V projection + RoPE
 
-@pytest.mark.parametrize("name", ["bf16", "bf16_hd64", "fp32"])
+@pytest.mark.parametrize("name", ["bf16", "bf16_hd64", "bf16_wide", "fp32"])
 @pytest.mark.parametrize("flags,T_max,n_valid", [(K.KVB_QKV_BATCH_INVARIANT, 200, 173), (K.KVB_QKV_SPLIT_K, 200, 173),
                                                  (K.KVB_QKV_SPLIT_K, 7, 5), (K.KVB_QKV_SPLIT_K, 1, 1)])
 def test_qkv_proj_rope(ctx, name, flags, T_max, n_valid):
@@ -93,12 +97,10 @@ def test_qkv_proj_rope(ctx, name, flags, T_max, n_valid):
     split = "splitk_reduce" in K.kvb_timing_read(ctx)
     K.kvb_timing_enable(ctx, None)
     torch.cuda.synchronize()
-    # the batch-invariant projection never splits K; a single row of the
-    # 512-wide bf16 shape does (the planner's choice elsewhere)
-    if flags == K.KVB_QKV_BATCH_INVARIANT or s.dtype == "fp32":
+    # the batch-invariant projection never splits K; nor does a single row
+    # that may (it takes the one-row weight-streaming product)
+    if flags == K.KVB_QKV_BATCH_INVARIANT or s.dtype == "fp32" or T_max == 1:
         assert not split
-    elif name == "bf16" and T_max == 1:
-        assert split
     Wn = {kk: np64(vv) for kk, vv in W.items()}
     rq, rk, rv = OM.qkv(np64(hidden)[rows[:n_valid]], pos[rows[:n_valid]], Wn, s)
     assert max_rel_err(q[:n_valid], rq) < TOL[s.dtype]
@@ -372,10 +374,11 @@ def test_topk_from_scores(ctx, req_lens):
 
 # ------------------------------------------------------------------ O-proj + MLP
 
-@pytest.mark.parametrize("name", ["bf16", "fp32"])
+@pytest.mark.parametrize("name", ["bf16", "bf16_wide", "fp32"])
 @pytest.mark.parametrize("T_max,n_valid", [(230, 201), (64, 64), (7, 5), (1, 1)])
 def test_mlp(ctx, name, T_max, n_valid):
-    """O-proj + MLP on gathered rows; the small batches take the 64-row tiles with split-K."""
+    """O-proj + MLP on gathered rows; the small batches take the 64-row tiles with split-K,
+    a single row the one-row product."""
     s = SHAPES[name]
     g = np.random.default_rng(8 + T_max)
     desc = K.model_desc(s)
