@@ -584,6 +584,7 @@ static kvb_status launch_splitk_reduce(hipStream_t st, const GemmArgs<bf16_t>& p
 // epilogues are the tiled kernel's.
 constexpr int GV_NW = 2, GV_WAVES = 4;
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float dot8_bf16(const uint4& w, const uint4& x, float acc) {
   acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x), __builtin_bit_cast(bf16x2_t, x.x), acc, false);
@@ -593,8 +594,10 @@ __device__ __forceinline__ float dot8_bf16(const uint4& w, const uint4& x, float
   return acc;
 }
 
+// (at most 4 waves per SIMD: the registers for a whole batch of loads in flight)
 template <int MODE, bool DUAL>
-__global__ void __launch_bounds__(64 * GV_WAVES) gemv_bf16_kernel(GemmArgs<bf16_t> p) {
+__global__ void __launch_bounds__(64 * GV_WAVES) __attribute__((amdgpu_waves_per_eu(1, 4)))
+gemv_bf16_kernel(GemmArgs<bf16_t> p) {
   extern __shared__ __align__(16) uint8_t gv_x[];
   if (row_count(p.n_rows, p.M_max) < 1) return;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -636,7 +639,13 @@ __global__ void __launch_bounds__(64 * GV_WAVES) gemv_bf16_kernel(GemmArgs<bf16_
 #pragma unroll
     for (int u = 0; u < 4; u++)
 #pragma unroll
-      for (int i = 0; i < R; i++) w[u][i] = wr[i][c + 64 * u];
+      for (int i = 0; i < R; i++) {
+        // streamed once: non-temporal, so the weights do not evict what the
+        // neighbouring launches keep in L2
+        const u32x4_t q = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(&wr[i][c + 64 * u]));
+        w[u][i] = make_uint4(q.x, q.y, q.z, q.w);
+      }
+    __builtin_amdgcn_sched_group_barrier(0x020, 4 * R, 0);  // every weight load of the batch first
 #pragma unroll
     for (int u = 0; u < 4; u++) {
       const uint4 xv = xs[c + 64 * u];
