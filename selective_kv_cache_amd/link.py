@@ -264,14 +264,22 @@ class LinkEngine:
     def _n_rows_ptr(self, which: int) -> int:
         return self.cu_rows[which].data_ptr() + 4 * self.B
 
-    def _read_rows(self, which: int) -> int:
-        """Total rows of selection buffer `which`, copied to the host once the
-        engine stream reaches this point."""
+    def _start_read_rows(self, which: int):
+        """Queue the copy of selection buffer `which`'s total row count to the host
+        at this point of the engine stream."""
         with torch.cuda.stream(self.stream):
             self._count_h.copy_(self.cu_rows[which][self.B:self.B + 1], non_blocking=True)
             self._count_ev.record(self.stream)
+
+    def _finish_read_rows(self) -> int:
         self._count_ev.synchronize()
         return int(self._count_h[0])
+
+    def _read_rows(self, which: int) -> int:
+        """Total rows of selection buffer `which`, copied to the host once the
+        engine stream reaches this point."""
+        self._start_read_rows(which)
+        return self._finish_read_rows()
 
     # ------------------------------------------------------------------ compile step
     def run_compile(self):
@@ -375,9 +383,11 @@ class LinkEngine:
             self._link_static(hook)
         self._tier_end()
 
-    def _layer_rows(self, l, T, n_rows, rows, cu_rows, src_slot, alpha_mode, alpha, d_out, cksim_out):
+    def _layer_rows(self, l, T, n_rows, rows, cu_rows, src_slot, alpha_mode, alpha, d_out, cksim_out,
+                    after_blend=None):
         """One recompute layer for the given rows: slot map, Q/K/V + RoPE, fusion and
-        scatter into new pages, attention over the spliced KV, O-proj + MLP."""
+        scatter into new pages, attention over the spliced KV, O-proj + MLP.
+        `after_blend` (optional) queues more work right after the fusion."""
         c, sh, ds, W = self.ctx, self.sh, self.desc, self.model.layers[l - 1]
         self.slot_map = self.page_table[l - 1]
         K.kvb_slot_map(c, sh, ds, self.B, self.N, T, cu_rows, rows, self.reuse_slot[l - 1], self.new_pages[l],
@@ -389,6 +399,8 @@ class LinkEngine:
                        self.v, self.ws, self.ws_bytes, flags)
         K.kvb_blend_scatter(c, sh, ds, T, n_rows, rows, self.k, self.v, self.k_pool, self.v_pool, self.n_pages,
                             src_slot, self.dst_slot, alpha_mode, alpha, d_out, cksim_out)
+        if after_blend:
+            after_blend()
         K.kvb_sparse_query_attn(c, sh, ds, T, n_rows, rows, self.lo_l, self.q, self.k_pool, self.v_pool,
                                 self.n_pages, self.slot_map, self.scale, self.o, self.ws, self.ws_bytes)
         K.kvb_mlp(c, sh, ds, T, n_rows, rows, self.o, W["w_o"], self.hidden, W["norm2"], W["w_gate_up"],
@@ -425,17 +437,30 @@ class LinkEngine:
             self._tier_need(l, -(-l // cfg.period) * cfg.period + 1 if exact else self.L)
             # the device count always bounds the rows: until the first refresh T is
             # the capacity, which the top-k does not fill when few tokens deviate
-            self._layer_rows(l, T, self._n_rows_ptr(cur), self.sel[cur], self.cu_rows[cur], self.reuse_slot[l - 1],
-                             cfg.alpha_mode, self.alpha, self.dev_l, self.cksim if refresh else None)
-            if hook:
-                hook(l, self)
-            if refresh:
+            # The refresh needs only this layer's cosine similarities, which the
+            # fusion writes, and it fills the other selection buffer, so it can run
+            # right after the fusion: the row count then reaches the host while the
+            # layer's attention and MLP still run.  With a hook (which inspects the
+            # state layer by layer) it runs after the layer; the results are the same.
+            def refresh_now(cur=cur, T=T):
                 K.kvb_cosine_refresh(c, sh, ds, B, N, self.cu_tok, T, self.cu_rows[cur], self.sel[cur], self.cksim,
                                      cfg.tau, cfg.refresh_rule, self.ranking, self.s_count, self.cursor,
                                      self.sel[1 - cur], self.cu_rows[1 - cur], self.ws, self.ws_bytes)
+                if exact:
+                    self._start_read_rows(1 - cur)
+
+            early = refresh and hook is None
+            self._layer_rows(l, T, self._n_rows_ptr(cur), self.sel[cur], self.cu_rows[cur], self.reuse_slot[l - 1],
+                             cfg.alpha_mode, self.alpha, self.dev_l, self.cksim if refresh else None,
+                             after_blend=refresh_now if early else None)
+            if hook:
+                hook(l, self)
+            if refresh:
+                if not early:
+                    refresh_now()
                 self.cur = 1 - cur
                 if exact:
-                    T = self._read_rows(self.cur)
+                    T = self._finish_read_rows()
                 if hook:
                     hook(("refresh", l), self)
 

@@ -343,22 +343,24 @@ def test_cacheblend_teacher_forced(make):
 
 
 def test_link_is_deterministic_and_repeatable():
-    """Two link runs on the same compiled cache give bitwise-identical results."""
+    """Link runs on the same compiled cache give bitwise-identical results, whether the
+    refresh runs right after the fusion (no hook) or after the layer (a hook)."""
     w = wl.small_bf16(n_layers=5)
     eng, E, W = build_engine(w, tau=0.5)
     eng.run_compile()
     outs = []
-    for _ in range(2):
-        eng.run_link()
+    for hook in (None, None, lambda *_: None):
+        eng.run_link(hook=hook)
         torch.cuda.synchronize()
         outs.append((eng.hidden.clone(), eng.k_pool.clone(), eng.v_pool.clone(), eng.selected()[0].copy(),
                      eng.alpha.clone(), eng.d.clone(), eng.ranking.clone()))
-    a, b = outs
-    for x, y in zip(a, b):
-        if isinstance(x, np.ndarray):
-            assert np.array_equal(x, y)
-        else:
-            assert torch.equal(x, y)
+    a = outs[0]
+    for b in outs[1:]:
+        for x, y in zip(a, b):
+            if isinstance(x, np.ndarray):
+                assert np.array_equal(x, y)
+            else:
+                assert torch.equal(x, y)
     eng.close()
 
 
