@@ -101,7 +101,7 @@ def cpu_baseline(w, eng, rec_state, step_flops, layers=(2, 3, 4)):
         S = np.asarray(state.S_k, dtype=np.int64)
         f_sum += S.size * per_row + 4.0 * Hq * hd * float(np.sum(S + 1))
         t0 = time.perf_counter()
-        OL.wca_layer(state, l, s, Wl, Kr, Vr, w.tau, w.period, s.n_layers)
+        OL.wca_layer(state, l, s, Wl, Kr, Vr, l in OL.refresh_layers(s.n_layers, w.period), w.tau)
         t_sum += time.perf_counter() - t0
         del Wl, Kr, Vr
     info = threadpool_info()

@@ -119,15 +119,30 @@ def chunk_blocks(request):
 
 # ---------------------------------------------------------------- CacheSlide
 
+def refresh_layers(n_layers: int, period: int) -> List[int]:
+    """Layers after which the similarity gate runs (1-based).
+
+    The CacheSlide page (Algorithm 2) checks CKSim every fourth layer.  The
+    gate after layer l changes the set used from layer l+1 on, so a gate after
+    the last layer would change nothing: it runs after l = period, 2*period, ...
+    with l < n_layers.
+    """
+    return list(range(period, n_layers, period))
+
+
 @dataclass
 class WCAState:
-    """Per-request state of Weighted Correction Attention between layers."""
-    h: np.ndarray                 # [N, d] residual stream (stale rows keep their last value)
-    alpha: np.ndarray             # [N]
+    """Per-request state of Weighted Correction Attention between layers.
+
+    Rows of `h` outside the current set keep the last value computed for them:
+    a token that joins the set at a refresh enters with the output of the last
+    layer that recomputed it (layer 1 for a token never selected before)."""
+    h: np.ndarray                 # [N, d] residual stream
+    alpha: np.ndarray             # [N] correction weight of each token's latest recompute
     d: np.ndarray                 # [N] layer-1 deviation
-    ranking: List[int]
-    cursor: int
-    S_k: List[int]                # ascending
+    ranking: List[int]            # tokens with d > 0, largest d first (ties: lower index)
+    cursor: int                   # ranking entries used so far
+    S_k: List[int]                # the set recomputed by the next layer, ascending
     layer: int = 1                # last layer done
 
 
@@ -148,42 +163,54 @@ def wca_layer1(request, shape, E, W1: dict, reuse_K1: np.ndarray, k_cap: int):
     return WCAState(h=h2, alpha=alpha.copy(), d=d, ranking=ranking, cursor=cursor, S_k=S_k), out
 
 
+def corrected_cache(S: np.ndarray, k_rec, v_rec, reuse_K, reuse_V, weight: np.ndarray, dtype: str):
+    """The layer's logical K/V after the weighted correction of the rows S.
+
+    Rows S hold weight * recomputed + (1 - weight) * cached (the fusion of the
+    CacheSlide page, one value of the weight per token for K and V alike),
+    rounded once to storage; every other row is the cached one.
+    Returns (K, V, fused K rows, fused V rows)."""
+    Kb = M.store(Sel.blend(weight, k_rec, reuse_K[S]), dtype)
+    Vb = M.store(Sel.blend(weight, v_rec, reuse_V[S]), dtype)
+    K = np.array(reuse_K, dtype=np.float64, copy=True)
+    V = np.array(reuse_V, dtype=np.float64, copy=True)
+    K[S] = Kb
+    V[S] = Vb
+    return K, V, Kb, Vb
+
+
 def wca_layer(state: WCAState, layer: int, shape, W: dict, reuse_K: np.ndarray, reuse_V: np.ndarray,
-              tau: float, period: int, n_layers: int, alpha_mode: str = "lag", rule: str = "literal",
+              gate: bool, tau: float = 0.12, alpha_mode: str = "lag", rule: str = "literal",
               attn_rows: Optional[np.ndarray] = None):
     """One layer l >= 2 for the tokens of S_k.  Mutates `state`; returns outputs.
 
-    attn_rows (indices into S_k) limits attention, MLP and the hidden update to
-    a sample of rows (used at full size); fusion, alpha and the refresh always
-    cover all of S_k.
+    The rows of S_k are recomputed from their current hidden state; their
+    deviation from the cached keys gives this layer's alpha.  The cache of the
+    layer is corrected with the alpha the token carried into the layer (its
+    latest one; `alpha_mode` "current" uses this layer's, "one" plain
+    replacement), the selected rows attend over it and their residual stream
+    advances.  With `gate` the similarity check then updates S_k for the next
+    layer.  attn_rows (indices into S_k) limits attention, MLP and the hidden
+    update to a sample of rows (full-size checks); the cache, alpha and the
+    gate always cover all of S_k.
     """
     S = np.asarray(state.S_k, dtype=np.int64)
-    q, k, v = M.qkv(state.h[S], S, W, shape)
-    kr, vr = reuse_K[S], reuse_V[S]
+    h_in = state.h[S].copy()
+    q, k, v = M.qkv(h_in, S, W, shape)
+    kr = reuse_K[S]
     d_l = Sel.deviation(k, kr)
     a_new = Sel.alpha_of(d_l, Sel.row_sq(kr))
-    if alpha_mode == "lag":
-        a_use = state.alpha[S].copy()
-    elif alpha_mode == "current":
-        a_use = a_new
-    elif alpha_mode == "one":          # alpha forced to 1: plain recompute (pin only)
-        a_use = np.ones_like(a_new)
-    else:
-        raise ValueError(alpha_mode)
-    Kb = M.store(Sel.blend(a_use, k, kr), shape.dtype)
-    Vb = M.store(Sel.blend(a_use, v, vr), shape.dtype)
-    K_log = np.array(reuse_K, dtype=np.float64, copy=True)
-    V_log = np.array(reuse_V, dtype=np.float64, copy=True)
-    K_log[S] = Kb
-    V_log[S] = Vb
+    a_use = {"lag": lambda: state.alpha[S].copy(), "current": lambda: a_new,
+             "one": lambda: np.ones_like(a_new)}[alpha_mode]()
+    K_log, V_log, Kb, Vb = corrected_cache(S, k, v, reuse_K, reuse_V, a_use, shape.dtype)
+    state.alpha[S] = a_new
     rows = np.arange(S.size) if attn_rows is None else np.asarray(attn_rows, dtype=np.int64)
     o = M.attention_rows_fast(q[rows], S[rows], K_log, V_log, np.zeros(rows.size, dtype=np.int64), shape)
-    h_rows = M.post_attention(state.h[S[rows]], o, W, shape)
+    h_rows = M.post_attention(h_in[rows], o, W, shape)
     state.h[S[rows]] = h_rows
-    state.alpha[S] = a_new
-    out = dict(S=S, q=q, k_rec=k, v_rec=v, K_blend=Kb, V_blend=Vb, d=d_l, alpha_used=a_use,
+    out = dict(S=S, h_in=h_in, q=q, k_rec=k, v_rec=v, K_blend=Kb, V_blend=Vb, d=d_l, alpha_used=a_use,
                alpha_new=a_new, o=o, h_rows=h_rows, rows=rows, K_log=K_log, V_log=V_log)
-    if layer % period == 0 and layer < n_layers:
+    if gate:
         c = Sel.cksim(k, kr)
         S_next, cur, retired = Sel.refresh(state.S_k, c, tau, state.ranking, state.cursor, rule)
         state.S_k, state.cursor = S_next, cur
@@ -197,12 +224,13 @@ def wca_link(request, shape, E, W, compiled, k_cap: int, tau: float, period: int
              alpha_mode: str = "lag", rule: str = "literal", keep: bool = True):
     """Free-running CacheSlide link step of one request.  Returns (state, per-layer outputs)."""
     L = shape.n_layers
+    gates = set(refresh_layers(L, period))
     K1, _ = splice(request, compiled, 1)
     state, out1 = wca_layer1(request, shape, E, W(1), K1, k_cap)
     outs = [out1]
     for l in range(2, L + 1):
         Kl, Vl = splice(request, compiled, l)
-        o = wca_layer(state, l, shape, W(l), Kl, Vl, tau, period, L, alpha_mode, rule)
+        o = wca_layer(state, l, shape, W(l), Kl, Vl, l in gates, tau, alpha_mode, rule)
         outs.append(o if keep else {k: o[k] for k in ("S", "h_rows", "S_next")})
     return state, outs
 
@@ -237,7 +265,7 @@ def cacheblend_link(request, shape, E, W, compiled, k_cap: int, keep: bool = Tru
     outs = [out1]
     for l in range(2, L + 1):
         Kl, Vl = splice(request, compiled, l)
-        o = wca_layer(state, l, shape, W(l), Kl, Vl, tau=0.0, period=L + 1, n_layers=L, alpha_mode="one")
+        o = wca_layer(state, l, shape, W(l), Kl, Vl, gate=False, alpha_mode="one")
         outs.append(o if keep else {k: o[k] for k in ("S", "h_rows", "S_next")})
     return state, outs
 

@@ -332,6 +332,7 @@ class LinkEngine:
             raise RuntimeError("reuse_tier='host': call stage_reuse_to_host() after run_compile()")
         self._tier_enq = 0
         self._tier_ev = [None] * (self.L + 1)
+        self._tier_loaded = {}   # layer -> "k" or "kv": what this step copied in
         if self.cfg.tier_overlap:
             if getattr(self, "copy_stream", None) is None:
                 self.copy_stream = torch.cuda.Stream(self.device)  # default priority
@@ -339,13 +340,30 @@ class LinkEngine:
             start.record(self.stream)
             self.copy_stream.wait_event(start)  # the previous step is done with the pool
 
-    def _tier_copy(self, l: int, stream_handle: int):
+    def _tier_copy(self, l: int, stream_handle: int, keys_only: Optional[bool] = None):
         # layer 1 of CacheSlide and of the CacheBlend-style link reads reused keys
         # only (the deviation compares keys)
-        keys_only = l == 1 and self.cfg.mode != "legolink"
+        if keys_only is None:
+            keys_only = l == 1 and self.cfg.mode != "legolink"
         K.kvb_pages_copy(self.ctx, stream_handle, self.desc, K.KVB_COPY_H2D, self.host_k,
                          None if keys_only else self.host_v, self.k_pool, None if keys_only else self.v_pool,
                          self.layer_reuse_pages[l])
+        self._tier_loaded[l] = "k" if keys_only else "kv"
+
+    def _tier_fill_for_decode(self, pt: np.ndarray):
+        """Before decode: copy in the reused K/V of every layer whose page table
+        still points at reused slots but whose pages the last link step did not
+        load (layers it skipped, or loaded keys only), so decode never attends
+        over an evicted page."""
+        if self.cfg.reuse_tier != "host" or getattr(self, "host_k", None) is None:
+            return
+        loaded = getattr(self, "_tier_loaded", {})
+        for l in range(1, self.L + 1):
+            if loaded.get(l) == "kv":
+                continue
+            rs = self.reuse_slot_h[l - 1]
+            if np.any((pt[l - 1] == rs) & (rs >= 0)):
+                self._tier_copy(l, self.sh, keys_only=False)
 
     def _tier_need(self, l: int, runs_until: int):
         """Before layer l: its reused pages are in the pool.  Layers up to
@@ -543,6 +561,7 @@ class LinkEngine:
                 if ids:
                     K.kvb_pool_release(self.pool, ids)
         pt = self.final_page_table().cpu().numpy()
+        self._tier_fill_for_decode(pt)
         cu = self.cu_tok_h
         # decode token space: request b's prompt at dcu[b] .. dcu[b] + N_b, then its max_decode tokens
         self.dec_cu = np.array([cu[b] + b * md for b in range(B)], dtype=np.int64)

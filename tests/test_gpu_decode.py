@@ -48,12 +48,12 @@ def shared_pair(seed=0):
     return wl.Workload("tiny-shared-pair", shape, "cacheslide", reqs, seed=seed)
 
 
-def engine(w, tier, n_dec, mode=None):
+def engine(w, tier, n_dec, mode=None, tau=None):
     s = w.shape
     E = wl.embedding_table(w, DEV)
     layers = [wl.layer_weights(w, l, DEV) for l in range(1, s.n_layers + 1)]
-    cfg = LinkConfig(mode=mode or w.mode, ratio=w.ratio, tau=w.tau, period=w.period, lego_k=w.lego_k,
-                     reuse_tier=tier)
+    cfg = LinkConfig(mode=mode or w.mode, ratio=w.ratio, tau=w.tau if tau is None else tau, period=w.period,
+                     lego_k=w.lego_k, reuse_tier=tier)
     return LinkEngine(Model(s, E, layers), w.requests, cfg, device=DEV, max_decode=n_dec), E, layers
 
 
@@ -76,7 +76,10 @@ def expected_holes(eng, pt, l, b):
     return out
 
 
-def check_decode(eng, E, layers, pt, toks, hs, overwrite_first):
+def check_decode(eng, E, layers, pt, toks, hs, overwrite_first, compiled=None):
+    """compiled: the oracle's compile-step K/V per chunk uid.  When given, a prompt
+    token whose page-table entry is its reused slot is read from there instead of
+    from the pool (so a reused page that was never loaded back shows)."""
     s = eng.shape
     L, B = s.n_layers, eng.B
     n_before = eng.n_compile_pages + sum(len(p) for req in eng.link_pages for p in req[1:])
@@ -112,8 +115,14 @@ def check_decode(eng, E, layers, pt, toks, hs, overwrite_first):
                 q, kk, vv = OM.qkv(h, np.array([Nb + t]), W[l - 1], s)
                 keys = np.concatenate([pt[l - 1][eng.cu_tok_h[b]:eng.cu_tok_h[b + 1]],
                                        eng.dec_slots_h[l - 1, b, :t]]).astype(np.int64)
-                Kl = np.concatenate([pool_rows(eng, eng.k_pool, keys), kk])
-                Vl = np.concatenate([pool_rows(eng, eng.v_pool, keys), vv])
+                Kp, Vp = pool_rows(eng, eng.k_pool, keys), pool_rows(eng, eng.v_pool, keys)
+                if compiled is not None:
+                    seg = slice(eng.cu_tok_h[b], eng.cu_tok_h[b + 1])
+                    reused = pt[l - 1][seg] == eng.reuse_slot_h[l - 1][seg]
+                    Kc, Vc = OL.splice(eng.requests[b], compiled, l, s)
+                    Kp[:Nb][reused], Vp[:Nb][reused] = Kc[reused], Vc[reused]
+                Kl = np.concatenate([Kp, kk])
+                Vl = np.concatenate([Vp, vv])
                 o = OM.attention_rows(q, np.array([Nb + t]), Kl, Vl, np.array([0]), s)
                 h = OM.post_attention(h, o, W[l - 1], s)
             got = np64(hs[t][b:b + 1])
@@ -121,11 +130,11 @@ def check_decode(eng, E, layers, pt, toks, hs, overwrite_first):
             assert err < tol, (b, t, err)
 
 
-def run(w, tier, overwrite_first, n_dec, consume=False, mode=None):
-    eng, E, layers = engine(w, tier, n_dec, mode)
+def run(w, tier, overwrite_first, n_dec, consume=False, mode=None, evict=False, tau=None):
+    eng, E, layers = engine(w, tier, n_dec, mode, tau)
     eng.run_compile()
     if tier == "host":
-        eng.stage_reuse_to_host()
+        eng.stage_reuse_to_host(evict=evict)
     eng.run_link()
     pt = eng.final_page_table().cpu().numpy().copy()
     first = dict(hidden=eng.hidden.clone(), k=eng.k_pool[eng.n_compile_pages:].clone())
@@ -148,6 +157,24 @@ def test_decode_tiny_host_tier(overwrite_first):
     eng.run_link()
     torch.cuda.synchronize()
     assert torch.equal(eng.hidden, first["hidden"])
+    eng.close()
+
+
+@pytest.mark.parametrize("overwrite_first", [True, False])
+def test_decode_after_evicted_host_tier(overwrite_first):
+    """Reused KV evicted to the host tier, and a set that empties at the first gate
+    (every token retires, the ranking is exhausted): layers 5-8 run no row, so
+    the link step loads none of their reused pages.  Decode must still attend
+    over the compile step's K/V there; the reference reads those rows from the
+    oracle's compile step, not from the pool."""
+    w = wl.tiny(n_layers=8, lens=(400, 40))
+    eng, E, layers, pt, toks, hs, first = run(w, "host", overwrite_first, n_dec=6, evict=True, tau=1.5)
+    skipped = [l for l in range(1, 9) if np.array_equal(pt[l - 1], eng.reuse_slot_h[l - 1])]
+    assert skipped == [5, 6, 7, 8]
+    E64 = np64(E)
+    W = {l: {kk: np64(vv) for kk, vv in layers[l - 1].items()} for l in range(1, 9)}
+    compiled = OL.compile_chunks(w.compile_chunks, w.shape, E64, W.__getitem__)
+    check_decode(eng, E, layers, pt, toks, hs, overwrite_first, compiled=compiled)
     eng.close()
 
 

@@ -120,16 +120,24 @@ def check_rows(eng, w, l, Wl, st, rows, h_in, alpha_in, tol, fused):
     assert max_rel_err(np64(st["hidden"][g_idx]), h_out) < tol
 
 
-def run_fullsize(w, check_layers, seed=0):
+def run_fullsize(w, check_layers, seed=0, rule="literal", table_only=()):
+    """Link step at full size, then the checks above on the listed layers.
+
+    Every listed layer must recompute rows, except the CacheSlide layers in
+    `table_only`: the set has emptied before them, and for those the layer's
+    final page table must be the reused slots and its new pages untouched."""
     s = w.shape
     L = s.n_layers
     keep = set(check_layers) | {l - 1 for l in check_layers if l > 1}
-    eng, _, _ = build_engine(w)
+    eng, _, _ = build_engine(w, rule=rule)
     rec = LayerRecorder(keep)
     eng.run_compile()
     eng.run_link(hook=rec)
     torch.cuda.synchronize()
-    print(f"[{w.name}] link step done, checking layers {sorted(check_layers)}", flush=True)
+    rows_per_layer = ([len(rows_in_order(eng, rec.after[l])) for l in sorted(check_layers) if l > 1]
+                      if eng.cfg.mode == "cacheslide" else "static")
+    print(f"[{w.name}, {rule}] link step done, checking layers {sorted(check_layers)} "
+          f"(rows {rows_per_layer} after layer 1)", flush=True)
     plan = page_plan_check(eng, w)
     E = wl.embedding_table(w, DEV)
     g = np.random.default_rng(seed)
@@ -149,7 +157,17 @@ def run_fullsize(w, check_layers, seed=0):
         else:
             rows = rows_in_order(eng, st)
         if cacheslide and l > 1 and not rows:
-            continue  # no row left: the engine skips the layer, nothing is written
+            # no row left: the engine skips the layer and writes nothing
+            assert l in table_only, f"layer {l} recomputes no row"
+            pt = eng.final_page_table()[l - 1].cpu().numpy()
+            for b, req in enumerate(w.requests):
+                assert np.array_equal(pt[cu[b]:cu[b + 1]], OP.reuse_slots(req, plan, l))
+                pages = torch.as_tensor(eng.link_pages[b][l], device=DEV, dtype=torch.int64)
+                assert int(torch.count_nonzero(eng.k_pool[pages])) == 0
+                assert int(torch.count_nonzero(eng.v_pool[pages])) == 0
+            print(f"[{w.name}] layer {l}: no rows, page table and new pages checked", flush=True)
+            continue
+        assert l not in table_only, f"layer {l} was expected to recompute nothing"
         # slot map of the layer, bit-exact, request by request
         for b, req in enumerate(w.requests):
             S_b = np.array([gg for _, gg, bb in rows if bb == b], dtype=np.int64) - cu[b]
@@ -209,7 +227,7 @@ def run_fullsize(w, check_layers, seed=0):
                 S_b = list(ga[m] - cu[b])
                 ranking = list(st["ranking"][seg][: int(st["s_count"][b])] - cu[b])
                 S_next, cur_next, _ = OS.refresh(S_b, c_gpu[m], float(np.float32(w.tau)), ranking,
-                                                 int(st["cursor"][b]), "literal")
+                                                 int(st["cursor"][b]), rule)
                 assert list(gr["sel"][gr["cu_rows"][b]:gr["cu_rows"][b + 1]] - cu[b]) == S_next
                 assert int(gr["cursor"][b]) == cur_next
         del Wl
@@ -219,6 +237,14 @@ def run_fullsize(w, check_layers, seed=0):
 @pytest.mark.timeout(300)
 def test_mistral_cacheslide_8k_fullsize():
     run_fullsize(wl.mistral_cacheslide(), check_layers=[1, 2, 4, 5, 12, 13])
+
+
+@pytest.mark.timeout(300)
+def test_mistral_cacheslide_8k_sustained_fullsize():
+    """The 8192-token request under the alternative retire rule (CKSim > 1 - tau):
+    on these weights no token retires, so all 2129 rows run in every layer up
+    to 32 (the schedule the sustained benchmark leg times)."""
+    run_fullsize(wl.mistral_cacheslide(), check_layers=[2, 16, 17, 32], rule="dissim")
 
 
 @pytest.mark.timeout(300)
@@ -284,4 +310,13 @@ def test_mistral_cacheblend_8k_fullsize():
 
 @pytest.mark.timeout(600)
 def test_llama70_cacheslide_32k_fullsize():
-    run_fullsize(wl.llama70_cacheslide(), check_layers=[1, 2, 5, 80])
+    """Layers 1, 2 and 5 in full; under the literal rule the set has emptied long
+    before layer 80, whose page table and new pages are checked."""
+    run_fullsize(wl.llama70_cacheslide(), check_layers=[1, 2, 5, 80], table_only=(80,))
+
+
+@pytest.mark.timeout(600)
+def test_llama70_cacheslide_32k_sustained_fullsize():
+    """The Llama-3-70B-shaped request under the alternative retire rule: all
+    8519 rows run in every layer, checked at layers 2, 17, 40 (a gate) and 80."""
+    run_fullsize(wl.llama70_cacheslide(), check_layers=[2, 17, 40, 80], rule="dissim")

@@ -256,8 +256,11 @@ def _attn_case(s, g, req_lens, n_sel, extra_pages=4):
 
 
 @pytest.mark.parametrize("name", ["bf16", "bf16_hd64", "fp32"])
-@pytest.mark.parametrize("req_lens,n_sel", [([700], 180), ([300, 517, 64], 240), ([33], 33)])
-def test_sparse_query_attention(ctx, name, req_lens, n_sel):
+@pytest.mark.parametrize("req_lens,n_sel", [([700], 180), ([300, 517, 64], 240), ([33], 33), ([2500], 7)])
+@pytest.mark.parametrize("split", [False, True], ids=["unsplit", "split"])
+def test_sparse_query_attention(ctx, name, req_lens, n_sel, split):
+    """With workspace, bf16 cuts each block's key range over several workgroups
+    and merges their partial results (split-KV); without, one pass per block."""
     s = SHAPES[name]
     g = np.random.default_rng(sum(req_lens) + n_sel)
     desc = K.model_desc(s)
@@ -269,8 +272,15 @@ def test_sparse_query_attention(ctx, name, req_lens, n_sel):
     rows_dev = np.concatenate([rows, np.zeros(9, dtype=rows.dtype)])
     q = rand((T_max, s.n_q_heads, s.head_dim), g, 1.5, dtype=dt).to(DEV)
     o = torch.full((T_max, s.q_dim), 3.0, dtype=dt, device=DEV)
+    ws, wsb = workspace(ctx, desc, T_max, n_tok) if split else (None, 0)
+    if split:
+        ws.fill_(0xFF)   # partial results must not depend on the workspace's previous contents
+    K.kvb_timing_enable(ctx, "attention_merge")
     K.kvb_sparse_query_attn(ctx, sh(), desc, T_max, i32([n_valid]), i32(rows_dev), i32(lo), q, kp, vp, n_pages,
-                            i32(slot_map), 1.0 / np.sqrt(s.head_dim), o, None, 0)
+                            i32(slot_map), 1.0 / np.sqrt(s.head_dim), o, ws, wsb)
+    merged = K.kvb_timing_read(ctx).get("attention_merge", {}).get("count", 0)
+    K.kvb_timing_enable(ctx, None)
+    assert merged == (1 if split and s.dtype == "bf16" else 0)
     torch.cuda.synchronize()
     Klog, Vlog = _rows_at(kp, slot_map, s), _rows_at(vp, slot_map, s)
     ref = OM.attention_rows(np64(q)[:n_valid], rows, Klog, Vlog, lo[rows], s)

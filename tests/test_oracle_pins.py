@@ -168,7 +168,7 @@ def test_wca_select_all_alpha_one_is_prefill():
     st.S_k = list(range(req.n_tokens))
     for l in (2, 3):
         Kl, Vl = OL.splice(req, compiled, l)
-        OL.wca_layer(st, l, w.shape, W(l), Kl, Vl, tau=0.12, period=100, n_layers=3, alpha_mode="one")
+        OL.wca_layer(st, l, w.shape, W(l), Kl, Vl, gate=False, alpha_mode="one")
     _, _, hr = torch_prefill(req.tokens, w.shape, E, W, 3)
     assert np.allclose(st.h, hr, rtol=1e-10, atol=1e-10)
 
@@ -518,3 +518,47 @@ def test_wca_alpha_lag_and_refresh_consistency():
             assert new <= set(st.ranking)
             assert not (set(o["retired"]) & set(o["S_next"]))
     assert seen_retire
+
+
+# ------------------------------------------------------------ refresh timing and the stale carry (hand-worked)
+
+def test_refresh_schedule_golden():
+    g = json.load(open(os.path.join(GOLDEN, "refresh_timing.json")))
+    for c in g["schedules"]:
+        assert OL.refresh_layers(c["n_layers"], c["period"]) == c["gates_after"], c
+
+
+@pytest.mark.parametrize("case", [0, 1])
+def test_all_retire_schedule_and_stale_carry(case):
+    """Every token retires at every gate: the oracle's set of each layer is the
+    golden's ranking slice, the gate runs exactly after the golden's layers,
+    and a token that joins enters with layer 1's output, checked against the
+    library decoder's first layer over the spliced prompt."""
+    gold = json.load(open(os.path.join(GOLDEN, "refresh_timing.json")))
+    g = gold["all_retire"]
+    c = g["cases"][case]
+    L = c["n_layers"]
+    w = tiny64(n_layers=L, lens=(40, 60, 60, 60))
+    E, W = oracle_inputs(w)
+    req = w.requests[0]
+    compiled = OL.compile_chunks(w.compile_chunks, w.shape, E, W)
+    k = int(np.floor(0.26 * req.n_tokens))
+    st, outs = OL.wca_link(req, w.shape, E, W, compiled, k, tau=g["tau"], period=c["period"], rule=g["rule"])
+    ranking = outs[0]["ranking"]
+    assert len(ranking) >= 3 * k
+    gated = [l for l in range(2, L + 1) if "cksim" in outs[l - 1]]
+    sched = [x for x in gold["schedules"] if x["n_layers"] == L and x["period"] == c["period"]]
+    assert gated == sched[0]["gates_after"]
+    for l in range(2, L + 1):
+        lo, hi = c["rank_slices"][str(l)]
+        assert list(outs[l - 1]["S"]) == sorted(ranking[lo * k: hi * k]), l
+    _, _, h1 = torch_prefill(req.tokens, w.shape, E, W, 1)
+    for l in c["fresh_layers"]:
+        S = outs[l - 1]["S"]
+        assert np.allclose(outs[l - 1]["h_in"], h1[S], rtol=1e-10, atol=1e-10), l
+    # a layer that is not the first after a gate starts from the previous layer's output rows
+    for l in range(3, L + 1):
+        if l not in c["fresh_layers"]:
+            prev = outs[l - 2]
+            assert np.array_equal(outs[l - 1]["S"], prev["S"])
+            assert np.array_equal(outs[l - 1]["h_in"], prev["h_rows"])
