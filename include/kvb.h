@@ -272,6 +272,25 @@ kvb_status kvb_deviation_topk(kvb_ctx* ctx, void* stream, const kvb_model_desc* 
                               int32_t* s_count, int32_t* sel, int32_t* cu_rows, int32_t* cursor,
                               void* ws, size_t ws_bytes);
 
+/* Allocation-free variant of kvb_deviation_topk, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, results and errors as
+ * kvb_deviation_topk, without ws / ws_bytes: the top-k keys and flags live in
+ * a fixed 2 MiB device array of the library (one per GPU, held until the
+ * process ends, its address looked up in kvb_create or on the first call on a
+ * device).  Batches of more than KVB_NOALLOC_MAX_TOKENS tokens or
+ * KVB_NOALLOC_MAX_REQUESTS requests are refused with KVB_ERR_WORKSPACE before
+ * anything is enqueued.  The call allocates nothing.  Every call on a GPU
+ * shares that GPU's array: calls that may overlap on one GPU (other streams,
+ * other threads) race and must be ordered by the caller. */
+#define KVB_NOALLOC_MAX_TOKENS 131072
+#define KVB_NOALLOC_MAX_REQUESTS 4096
+kvb_status kvb_deviation_topk_noalloc(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t B,
+                                      int32_t n_tok, const int32_t* cu_tok, const void* k_rec,
+                                      const void* k_pool, int32_t n_pages, const int32_t* reuse_slot,
+                                      const int32_t* k_cap, float* d, float* alpha, int32_t* ranking,
+                                      int32_t* s_count, int32_t* sel, int32_t* cu_rows, int32_t* cursor);
+
 /* Top-k selection from a per-token score already computed (the ranking, S and
  * S_k rules of kvb_deviation_topk, for a selection whose score is not the key
  * deviation, e.g. kvb_attnmap_deviation).  d [n_tok] float (>= 0) is read

@@ -25,6 +25,7 @@ KVB_ALPHA_LAG, KVB_ALPHA_CURRENT, KVB_ALPHA_ONE = 0, 1, 2
 KVB_REFRESH_LITERAL, KVB_REFRESH_DISSIM = 0, 1
 KVB_COPY_H2D, KVB_COPY_D2H = 0, 1
 KVB_QKV_BATCH_INVARIANT, KVB_QKV_SPLIT_K = 0, 1
+KVB_NOALLOC_MAX_TOKENS, KVB_NOALLOC_MAX_REQUESTS = 131072, 4096
 
 
 class KvbError(RuntimeError):
@@ -62,6 +63,7 @@ _SIGS = {
     "kvb_sparse_query_attn": ([P, P, P, I, P, P, P, P, P, P, I, P, c_float, P, P, c_size_t], I),
     "kvb_mlp": ([P, P, P, I, P, P, P, P, P, P, P, P, P, c_size_t], I),
     "kvb_deviation_topk": ([P, P, P, I, I, P, P, P, I, P, P, P, P, P, P, P, P, P, P, c_size_t], I),
+    "kvb_deviation_topk_noalloc": ([P, P, P, I, I, P, P, P, I, P, P, P, P, P, P, P, P, P], I),
     "kvb_topk": ([P, P, P, I, I, P, P, P, P, P, P, P, P, P, c_size_t], I),
     "kvb_attnmap_deviation": ([P, P, P, I, P, P, P, P, I, P, c_float, P, P, c_size_t], I),
     "kvb_cosine_refresh": ([P, P, P, I, I, P, I, P, P, P, c_float, I, P, P, P, P, P, P, c_size_t], I),
@@ -247,6 +249,12 @@ def kvb_deviation_topk(ctx, stream, desc, B, n_tok, cu_tok, k_rec, k_pool, n_pag
                        ranking, s_count, sel, cu_rows, cursor, ws, ws_bytes):
     _call("kvb_deviation_topk", ctx, stream, desc, B, n_tok, cu_tok, k_rec, k_pool, n_pages,
           reuse_slot, k_cap, d, alpha, ranking, s_count, sel, cu_rows, cursor, ws, ws_bytes)
+
+
+def kvb_deviation_topk_noalloc(ctx, stream, desc, B, n_tok, cu_tok, k_rec, k_pool, n_pages, reuse_slot, k_cap, d,
+                               alpha, ranking, s_count, sel, cu_rows, cursor):
+    _call("kvb_deviation_topk_noalloc", ctx, stream, desc, B, n_tok, cu_tok, k_rec, k_pool, n_pages,
+          reuse_slot, k_cap, d, alpha, ranking, s_count, sel, cu_rows, cursor)
 
 
 def kvb_topk(ctx, stream, desc, B, n_tok, cu_tok, d, k_cap, ranking, s_count, sel, cu_rows, cursor, ws, ws_bytes):

@@ -61,6 +61,11 @@ kvb_status check_ctx(const kvb_ctx* c);
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 
+// Device address of this device's fixed scratch of the allocation-free top-k
+// (first call on a device looks it up); setup is called by kvb_create.
+kvb_status noalloc_scratch(int device, void** out);
+kvb_status noalloc_scratch_setup(int device);
+
 // workspace layouts (bytes), shared by kvb_workspace_size and the entry points
 size_t ws_mlp_bytes(const kvb_model_desc* d, int32_t max_rows, int n_cu);
 size_t ws_gemm_sk_bytes(int n_cu);

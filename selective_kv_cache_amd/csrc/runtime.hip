@@ -145,6 +145,16 @@ kvb_status kvb_create(int32_t device, kvb_ctx** out) {
   hipError_t e = hipGetDeviceCount(&n);
   if (e != hipSuccess) return fail(KVB_ERR_HIP, std::string("hipGetDeviceCount: ") + hipGetErrorString(e));
   if (device < 0 || device >= n) return fail(KVB_ERR_INVALID_ARG, "device index out of range");
+  // with `device` current, look up the device address of the fixed scratch of
+  // the allocation-free entry point once for this device
+  int prev = 0;
+  e = hipGetDevice(&prev);
+  if (e != hipSuccess) return fail(KVB_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (prev != device && (e = hipSetDevice(device)) != hipSuccess)
+    return fail(KVB_ERR_HIP, std::string("hipSetDevice: ") + hipGetErrorString(e));
+  const kvb_status s = noalloc_scratch_setup(device);
+  if (prev != device) hipSetDevice(prev);
+  if (s != KVB_OK) return s;
   Ctx* c = new Ctx();
   c->device = device;
   int cu = 0;

@@ -15,6 +15,8 @@
 // deterministic and independent of launch shapes.
 #include "common.h"
 
+#include <mutex>
+
 namespace kvb {
 
 template <class T>
@@ -247,6 +249,81 @@ static kvb_status launch_topk(hipStream_t st, int B, int n_tok, const int32_t* c
   return check_launch("compact_kernel");
 }
 
+// ------------------------------------------------ allocation-free top-k scratch
+// kvb_deviation_topk_noalloc keeps the top-k keys and flags in this fixed
+// array instead of a caller workspace.  Each GPU holds its own copy until the
+// process ends; host code takes its device address from hipGetSymbolAddress
+// (the array's name is not a device address on the host) and keeps it per
+// device.  The sorted keys and flags are always written before they are read,
+// so nothing in it needs clearing between calls.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)2 << 20;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+constexpr int NOALLOC_MAX_DEVICES = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[NOALLOC_MAX_DEVICES] = {};
+
+// Device address of this device's scratch (the device is current).  The first
+// call on a device looks it up; later calls return the kept pointer.
+kvb_status noalloc_scratch(int device, void** out) {
+  if (device < 0 || device >= NOALLOC_MAX_DEVICES) return fail(KVB_ERR_UNSUPPORTED, "device index beyond 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(KVB_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[device] = p;
+  }
+  *out = g_scratch_ptr[device];
+  return KVB_OK;
+}
+
+// Called by kvb_create with `device` current, so the lookup happens at set-up.
+kvb_status noalloc_scratch_setup(int device) {
+  void* p = nullptr;
+  return noalloc_scratch(device, &p);
+}
+
+static kvb_status check_deviation_topk(const kvb_model_desc* desc, int32_t B, int32_t n_tok, const int32_t* cu_tok,
+                                       const void* k_rec, const void* k_pool, int32_t n_pages,
+                                       const int32_t* reuse_slot, const int32_t* k_cap, float* d, float* alpha,
+                                       int32_t* ranking, int32_t* s_count, int32_t* sel, int32_t* cu_rows,
+                                       int32_t* cursor) {
+  KVB_TRY(check_desc(desc));
+  if (B <= 0 || n_tok < 0 || n_pages < 0) return fail(KVB_ERR_INVALID_ARG, "B <= 0 or negative size");
+  KVB_CHECK_PTR(cu_tok, "cu_tok");
+  KVB_CHECK_PTR(k_cap, "k_cap");
+  KVB_CHECK_PTR(s_count, "s_count");
+  KVB_CHECK_PTR(cu_rows, "cu_rows");
+  KVB_CHECK_PTR(cursor, "cursor");
+  if (n_tok > 0) {
+    KVB_CHECK_PTR(k_rec, "k_rec");
+    KVB_CHECK_PTR(k_pool, "k_pool");
+    KVB_CHECK_PTR(reuse_slot, "reuse_slot");
+    KVB_CHECK_PTR(d, "d");
+    KVB_CHECK_PTR(alpha, "alpha");
+    KVB_CHECK_PTR(ranking, "ranking");
+    KVB_CHECK_PTR(sel, "sel");
+  }
+  if (desc->n_kv_heads * desc->head_dim / 8 > 1024) return fail(KVB_ERR_UNSUPPORTED, "n_kv_heads * head_dim > 8192");
+  return KVB_OK;
+}
+
+static kvb_status run_deviation_topk(hipStream_t st, const kvb_model_desc* desc, int32_t B, int32_t n_tok,
+                                     const int32_t* cu_tok, const void* k_rec, const void* k_pool, int32_t n_pages,
+                                     const int32_t* reuse_slot, const int32_t* k_cap, float* d, float* alpha,
+                                     int32_t* ranking, int32_t* s_count, int32_t* sel, int32_t* cu_rows,
+                                     int32_t* cursor, void* ws) {
+  if (desc->dtype == KVB_BF16)
+    KVB_TRY(launch_deviation<bf16_t>(st, n_tok, k_rec, k_pool, n_pages, reuse_slot, d, alpha, desc->n_kv_heads,
+                                     desc->head_dim));
+  else
+    KVB_TRY(launch_deviation<float>(st, n_tok, k_rec, k_pool, n_pages, reuse_slot, d, alpha, desc->n_kv_heads,
+                                    desc->head_dim));
+  return launch_topk(st, B, n_tok, cu_tok, d, k_cap, ranking, s_count, sel, cu_rows, cursor, ws);
+}
+
 }  // namespace kvb
 
 using namespace kvb;
@@ -279,33 +356,35 @@ extern "C" kvb_status kvb_deviation_topk(kvb_ctx* ctx, void* stream, const kvb_m
                                          float* alpha, int32_t* ranking, int32_t* s_count, int32_t* sel,
                                          int32_t* cu_rows, int32_t* cursor, void* ws, size_t ws_bytes) {
   KVB_TRY(check_ctx(ctx));
-  KVB_TRY(check_desc(desc));
-  if (B <= 0 || n_tok < 0 || n_pages < 0) return fail(KVB_ERR_INVALID_ARG, "B <= 0 or negative size");
-  KVB_CHECK_PTR(cu_tok, "cu_tok");
-  KVB_CHECK_PTR(k_cap, "k_cap");
-  KVB_CHECK_PTR(s_count, "s_count");
-  KVB_CHECK_PTR(cu_rows, "cu_rows");
-  KVB_CHECK_PTR(cursor, "cursor");
-  if (n_tok > 0) {
-    KVB_CHECK_PTR(k_rec, "k_rec");
-    KVB_CHECK_PTR(k_pool, "k_pool");
-    KVB_CHECK_PTR(reuse_slot, "reuse_slot");
-    KVB_CHECK_PTR(d, "d");
-    KVB_CHECK_PTR(alpha, "alpha");
-    KVB_CHECK_PTR(ranking, "ranking");
-    KVB_CHECK_PTR(sel, "sel");
-  }
+  KVB_TRY(check_deviation_topk(desc, B, n_tok, cu_tok, k_rec, k_pool, n_pages, reuse_slot, k_cap, d, alpha, ranking,
+                               s_count, sel, cu_rows, cursor));
   if (!ws || ws_bytes < ws_topk_bytes(n_tok, B)) return fail(KVB_ERR_WORKSPACE, "kvb_deviation_topk workspace too small");
-  if (desc->n_kv_heads * desc->head_dim / 8 > 1024) return fail(KVB_ERR_UNSUPPORTED, "n_kv_heads * head_dim > 8192");
   CtxScope scope(ctx);
-  hipStream_t st = (hipStream_t)stream;
-  if (desc->dtype == KVB_BF16)
-    KVB_TRY(launch_deviation<bf16_t>(st, n_tok, k_rec, k_pool, n_pages, reuse_slot, d, alpha, desc->n_kv_heads,
-                                     desc->head_dim));
-  else
-    KVB_TRY(launch_deviation<float>(st, n_tok, k_rec, k_pool, n_pages, reuse_slot, d, alpha, desc->n_kv_heads,
-                                    desc->head_dim));
-  return launch_topk(st, B, n_tok, cu_tok, d, k_cap, ranking, s_count, sel, cu_rows, cursor, ws);
+  return run_deviation_topk((hipStream_t)stream, desc, B, n_tok, cu_tok, k_rec, k_pool, n_pages, reuse_slot, k_cap,
+                            d, alpha, ranking, s_count, sel, cu_rows, cursor, ws);
+}
+
+extern "C" kvb_status kvb_deviation_topk_noalloc(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t B,
+                                                 int32_t n_tok, const int32_t* cu_tok, const void* k_rec,
+                                                 const void* k_pool, int32_t n_pages, const int32_t* reuse_slot,
+                                                 const int32_t* k_cap, float* d, float* alpha, int32_t* ranking,
+                                                 int32_t* s_count, int32_t* sel, int32_t* cu_rows, int32_t* cursor) {
+  KVB_TRY(check_ctx(ctx));
+  KVB_TRY(check_deviation_topk(desc, B, n_tok, cu_tok, k_rec, k_pool, n_pages, reuse_slot, k_cap, d, alpha, ranking,
+                               s_count, sel, cu_rows, cursor));
+  if (n_tok > KVB_NOALLOC_MAX_TOKENS || B > KVB_NOALLOC_MAX_REQUESTS ||
+      ws_topk_bytes(n_tok, B) > NOALLOC_SCRATCH_BYTES)
+    return fail(KVB_ERR_WORKSPACE, "kvb_deviation_topk_noalloc: more than " + std::to_string(KVB_NOALLOC_MAX_TOKENS) +
+                                       " tokens or " + std::to_string(KVB_NOALLOC_MAX_REQUESTS) +
+                                       " requests for its fixed scratch");
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KVB_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  void* ws = nullptr;
+  KVB_TRY(noalloc_scratch(dev, &ws));
+  CtxScope scope(ctx);
+  return run_deviation_topk((hipStream_t)stream, desc, B, n_tok, cu_tok, k_rec, k_pool, n_pages, reuse_slot, k_cap,
+                            d, alpha, ranking, s_count, sel, cu_rows, cursor, ws);
 }
 
 extern "C" kvb_status kvb_cosine_refresh(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t B,
