@@ -117,7 +117,7 @@ kvb_status kvb_workspace_size(kvb_ctx* ctx, const kvb_model_desc* desc, int32_t 
  * HIP events on its stream; filter == NULL turns timing off.  Kernel names:
  * embed, rmsnorm, gemm_qkv, rope, blend_scatter, attention, attention_merge, gemm_oproj, gemm_swiglu,
  * gemm_down, splitk_reduce, deviation, topk_sort, topk_rank, topk_compact, refresh_flag,
- * refresh_compact, slot_copy, slot_scatter, attnmap, attnmap_reduce. */
+ * refresh_compact, slot_copy, slot_scatter, page_dirty, attnmap, attnmap_reduce. */
 kvb_status kvb_timing_enable(kvb_ctx* ctx, const char* filter);
 /* Waits for the recorded events and folds them into per-kernel totals, then
  * sets *needed to the size of the JSON text {"name": {"count": n, "ms": t}, ...}
@@ -347,12 +347,31 @@ kvb_status kvb_cosine_refresh(kvb_ctx* ctx, void* stream, const kvb_model_desc* 
  *   slot_map[row_tok[r]] = dst_slot[r]
  * Rows whose rank exceeds the request's page list get dst_slot = -1 and keep
  * their reuse slot.  reuse_slot may be NULL (slot_map starts at -1).
- * row_tok NULL = identity (then cu_rows doubles as cu_tok). */
+ * row_tok NULL = identity (then cu_rows doubles as cu_tok).
+ * page_dirty (device int32 [n_pages], or NULL): SLIDE's per-page dirty
+ * counters (CacheSlide page, SLIDE implementation paragraph: from layer 2 on,
+ * a page holding selected tokens is dirty, and its counter is updated whenever
+ * the slot mapping routes a selected token to it): page_dirty[dst_slot[r] /
+ * page_size] += 1 for every row given a slot below n_pages * page_size.  The
+ * caller clears the counters when it starts a link step and passes them for
+ * the selective layers (2..L) only. */
 kvb_status kvb_slot_map(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t B,
                         int32_t n_tok, int32_t T_max, const int32_t* cu_rows,
                         const int32_t* row_tok, const int32_t* reuse_slot,
                         const int32_t* new_pages, const int32_t* cu_pages, int32_t* slot_map,
-                        int32_t* dst_slot);
+                        int32_t* dst_slot, int32_t n_pages, int32_t* page_dirty);
+
+/* Dirty-page counters during decode (CacheSlide page, SLIDE: the policy of
+ * the link step applies during decode as well, whose tokens are written
+ * first into the superseded slots of the selected tokens, then into fresh
+ * pages).  For r < *n_rows (n_rows NULL = T_max): if 0 <= slots[r] <
+ * n_pages * page_size, page_dirty[slots[r] / page_size] += 1.  slots: device
+ * int32 [T_max], the slots the K/V of the rows were written to;
+ * page_dirty: device int32 [n_pages].  Counts are exact whatever the order of
+ * the increments. */
+kvb_status kvb_page_dirty_add(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t T_max,
+                              const int32_t* n_rows, const int32_t* slots, int32_t n_pages,
+                              int32_t* page_dirty);
 
 #ifdef __cplusplus
 }

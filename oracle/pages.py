@@ -102,3 +102,36 @@ def slot_map(reuse_slot_l: np.ndarray, selected: np.ndarray, new_pages_l: List[i
     if sel.size:
         m[sel] = slot_of(new_pages_l, np.arange(sel.size), page_size)
     return m
+
+
+# ---------------------------------------------------------------- dirty pages (SLIDE)
+
+def dirty_counts(n_pages: int, layer_routes, decode_slots=(), page_size: int = 16) -> np.ndarray:
+    """SLIDE's per-page dirty counters after a link step and its decode tokens.
+
+    CacheSlide page, SLIDE paragraphs: from layer 2 on, a page that holds
+    selected tokens is dirty, and its counter goes up each time the slot
+    mapping routes a selected token to it; decode follows the same policy.
+    layer_routes[l-1] = (slot_map of layer l, tokens selected at layer l) for
+    l = 1..L; layer 1 is not counted.  decode_slots: every slot a decode
+    token's K/V was written to (all layers).  Returns int64 [n_pages].
+    """
+    counts = np.zeros(int(n_pages), dtype=np.int64)
+    for layer, (smap, S) in enumerate(layer_routes, start=1):
+        if layer < 2:
+            continue
+        for i in S:
+            counts[int(smap[int(i)]) // page_size] += 1
+    for slot in decode_slots:
+        counts[int(slot) // page_size] += 1
+    return counts
+
+
+def spill_order(counts, pages) -> List[int]:
+    """The order SLIDE evicts `pages` in: clean pages (counter 0) first, then
+    dirty pages by counter, largest first.  Ties: lower page id first."""
+    pages = sorted(int(p) for p in pages)
+    clean = [p for p in pages if counts[p] == 0]
+    dirty = [p for p in pages if counts[p] != 0]
+    dirty.sort(key=lambda p: (-int(counts[p]), p))
+    return clean + dirty

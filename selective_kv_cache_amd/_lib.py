@@ -67,7 +67,8 @@ _SIGS = {
     "kvb_topk": ([P, P, P, I, I, P, P, P, P, P, P, P, P, P, c_size_t], I),
     "kvb_attnmap_deviation": ([P, P, P, I, P, P, P, P, I, P, c_float, P, P, c_size_t], I),
     "kvb_cosine_refresh": ([P, P, P, I, I, P, I, P, P, P, c_float, I, P, P, P, P, P, P, c_size_t], I),
-    "kvb_slot_map": ([P, P, P, I, I, I, P, P, P, P, P, P, P], I),
+    "kvb_slot_map": ([P, P, P, I, I, I, P, P, P, P, P, P, P, I, P], I),
+    "kvb_page_dirty_add": ([P, P, P, I, P, P, I, P], I),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -275,6 +276,10 @@ def kvb_cosine_refresh(ctx, stream, desc, B, n_tok, cu_tok, T_max, cu_rows_in, s
 
 
 def kvb_slot_map(ctx, stream, desc, B, n_tok, T_max, cu_rows, row_tok, reuse_slot, new_pages, cu_pages, slot_map,
-                 dst_slot):
+                 dst_slot, n_pages=0, page_dirty=None):
     _call("kvb_slot_map", ctx, stream, desc, B, n_tok, T_max, cu_rows, row_tok, reuse_slot,
-          new_pages, cu_pages, slot_map, dst_slot)
+          new_pages, cu_pages, slot_map, dst_slot, n_pages, page_dirty)
+
+
+def kvb_page_dirty_add(ctx, stream, desc, T_max, n_rows, slots, n_pages, page_dirty):
+    _call("kvb_page_dirty_add", ctx, stream, desc, T_max, n_rows, slots, n_pages, page_dirty)

@@ -317,7 +317,8 @@ __global__ void copy_slots_kernel(int n_tok, const int32_t* __restrict__ reuse_s
 __global__ void scatter_slots_kernel(int B, int T_max, const int32_t* __restrict__ cu_rows,
                                      const int32_t* __restrict__ row_tok, const int32_t* __restrict__ new_pages,
                                      const int32_t* __restrict__ cu_pages, int32_t* __restrict__ slot_map,
-                                     int32_t* __restrict__ dst_slot, int n_tok) {
+                                     int32_t* __restrict__ dst_slot, int n_tok, int n_pages,
+                                     int32_t* __restrict__ page_dirty) {
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= T_max || r >= cu_rows[B]) return;
   int lo = 0, hi = B;  // find b with cu_rows[b] <= r < cu_rows[b+1]
@@ -334,6 +335,17 @@ __global__ void scatter_slots_kernel(int B, int T_max, const int32_t* __restrict
   if (dst_slot) dst_slot[r] = slot;
   const int g = row_tok ? row_tok[r] : r;
   if (slot >= 0 && g >= 0 && g < n_tok) slot_map[g] = slot;
+  // SLIDE's dirty-page counter: one more selected token routed into this page
+  if (page_dirty && slot >= 0 && (slot >> 4) < n_pages) atomicAdd(&page_dirty[slot >> 4], 1);
+}
+
+// page_dirty[slot / 16] += 1 for every valid slot of rows r < *n_rows
+__global__ void page_dirty_add_kernel(int T_max, const int32_t* __restrict__ n_rows, const int32_t* __restrict__ slots,
+                                      int n_pages, int32_t* __restrict__ page_dirty) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= T_max || (n_rows && r >= *n_rows)) return;
+  const int s = slots[r];
+  if (s >= 0 && (s >> 4) < n_pages) atomicAdd(&page_dirty[s >> 4], 1);
 }
 
 }  // namespace kvb
@@ -425,10 +437,10 @@ extern "C" kvb_status kvb_blend_scatter(kvb_ctx* ctx, void* stream, const kvb_mo
 extern "C" kvb_status kvb_slot_map(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t B, int32_t n_tok,
                                    int32_t T_max, const int32_t* cu_rows, const int32_t* row_tok,
                                    const int32_t* reuse_slot, const int32_t* new_pages, const int32_t* cu_pages,
-                                   int32_t* slot_map, int32_t* dst_slot) {
+                                   int32_t* slot_map, int32_t* dst_slot, int32_t n_pages, int32_t* page_dirty) {
   KVB_TRY(check_ctx(ctx));
   KVB_TRY(check_desc(desc));
-  if (B < 0 || n_tok < 0 || T_max < 0) return fail(KVB_ERR_INVALID_ARG, "negative size");
+  if (B < 0 || n_tok < 0 || T_max < 0 || n_pages < 0) return fail(KVB_ERR_INVALID_ARG, "negative size");
   KVB_CHECK_PTR(slot_map, "slot_map");
   CtxScope scope(ctx);
   hipStream_t st = (hipStream_t)stream;
@@ -443,6 +455,22 @@ extern "C" kvb_status kvb_slot_map(kvb_ctx* ctx, void* stream, const kvb_model_d
   KVB_CHECK_PTR(cu_pages, "cu_pages");
   LaunchTimer lt(st, "slot_scatter");
   scatter_slots_kernel<<<cdiv(T_max, 256), 256, 0, st>>>(B, T_max, cu_rows, row_tok, new_pages, cu_pages, slot_map,
-                                                         dst_slot, n_tok);
+                                                         dst_slot, n_tok, n_pages, page_dirty);
   return check_launch("scatter_slots_kernel");
+}
+
+extern "C" kvb_status kvb_page_dirty_add(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t T_max,
+                                         const int32_t* n_rows, const int32_t* slots, int32_t n_pages,
+                                         int32_t* page_dirty) {
+  KVB_TRY(check_ctx(ctx));
+  KVB_TRY(check_desc(desc));
+  if (T_max < 0 || n_pages < 0) return fail(KVB_ERR_INVALID_ARG, "negative size");
+  if (T_max == 0) return KVB_OK;
+  KVB_CHECK_PTR(slots, "slots");
+  KVB_CHECK_PTR(page_dirty, "page_dirty");
+  CtxScope scope(ctx);
+  hipStream_t st = (hipStream_t)stream;
+  LaunchTimer lt(st, "page_dirty");
+  page_dirty_add_kernel<<<cdiv(T_max, 256), 256, 0, st>>>(T_max, n_rows, slots, n_pages, page_dirty);
+  return check_launch("page_dirty_add_kernel");
 }

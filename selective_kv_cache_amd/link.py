@@ -46,6 +46,16 @@ def _npages(n: int) -> int:
     return (int(n) + PAGE - 1) // PAGE
 
 
+def spill_order(counts, pages) -> List[int]:
+    """SLIDE's eviction order of `pages` (CacheSlide page, SLIDE paragraphs:
+    clean pages go first, then dirty pages in descending order of their
+    selected-token counter); equal counters by lower page id."""
+    pages = sorted(int(p) for p in pages)
+    clean = [p for p in pages if counts[p] == 0]
+    dirty = sorted((p for p in pages if counts[p] != 0), key=lambda p: (-int(counts[p]), p))
+    return clean + dirty
+
+
 class Model:
     """Weights of a decoder stack resident on the device (caller-provided tensors)."""
 
@@ -240,6 +250,9 @@ class LinkEngine:
         self.slot_map = self.page_table[0]  # the layer being run
         self._pt_reuse_rows = set()         # layers skipped by the last step: their rows still to fill
         self.dst_slot = torch.zeros(rows_max, dtype=torch.int32, device=dev)
+        # SLIDE's dirty-page counters: selected tokens routed into each page from
+        # layer 2 on, then the decode tokens written into it (cleared per link step)
+        self.page_dirty = torch.zeros(self.n_pages, dtype=torch.int32, device=dev)
         self.ws_bytes = K.kvb_workspace_size(self.ctx, self.desc, rows_max, max(self.N, self.Nc), self.B)
         self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
         self.cur = 0
@@ -392,6 +405,8 @@ class LinkEngine:
     # ------------------------------------------------------------------ link step
     def run_link(self, hook: Optional[Callable] = None):
         self._pt_reuse_rows = set()
+        with torch.cuda.stream(self.stream):
+            self.page_dirty.zero_()
         self._tier_begin()
         if self.cfg.mode == "cacheslide":
             self._link_cacheslide(hook)
@@ -409,7 +424,8 @@ class LinkEngine:
         c, sh, ds, W = self.ctx, self.sh, self.desc, self.model.layers[l - 1]
         self.slot_map = self.page_table[l - 1]
         K.kvb_slot_map(c, sh, ds, self.B, self.N, T, cu_rows, rows, self.reuse_slot[l - 1], self.new_pages[l],
-                       self.cu_pages[l], self.slot_map, self.dst_slot)
+                       self.cu_pages[l], self.slot_map, self.dst_slot, self.n_pages,
+                       self.page_dirty if l >= 2 else None)
         # layer 1's keys must be bitwise those of the compile step (chunk 0 deviates by
         # exactly 0): batch-invariant there; the selective layers may split K
         flags = K.KVB_QKV_BATCH_INVARIANT if l == 1 else K.KVB_QKV_SPLIT_K
@@ -661,6 +677,8 @@ class LinkEngine:
         pt = self.pt_dec
         with torch.cuda.stream(stream):
             pt.index_copy_(1, self._dec_rows64, self._dec_slots)
+        # every layer's K/V of the new tokens goes to the slots placed for it: their pages are dirty
+        K.kvb_page_dirty_add(c, sh, ds, L * B, None, self._dec_slots, self.n_pages, self.page_dirty)
         K.kvb_embed(c, sh, ds, B, None, None, self._dec_tok, self.shape.vocab, m.embedding, self.hidden_dec)
         for l in range(1, L + 1):
             W = m.layers[l - 1]
@@ -674,6 +692,14 @@ class LinkEngine:
                       W["w_down"], self.ws, self.ws_bytes)
 
     # ------------------------------------------------------------------ results
+    def spill_order(self, pages=None) -> List[int]:
+        """Pages in SLIDE's eviction order under memory pressure (clean pages
+        first, then dirty pages by their counter, largest first), from the
+        device counters (host copy, synchronises).  `pages`: the candidates
+        (default: every page of the pool)."""
+        counts = self.page_dirty.cpu().numpy()
+        return spill_order(counts, range(self.n_pages) if pages is None else pages)
+
     def selected(self, which: Optional[int] = None) -> List[np.ndarray]:
         """Current S_k per request (host copy, synchronises)."""
         w = self.cur if which is None else which

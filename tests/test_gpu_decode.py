@@ -28,6 +28,7 @@ if ROOT not in sys.path:
 import workloads as wl  # noqa: E402
 from oracle import link as OL  # noqa: E402
 from oracle import model as OM  # noqa: E402
+from oracle import pages as OP  # noqa: E402
 from selective_kv_cache_amd.link import LinkConfig, LinkEngine, Model  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -103,6 +104,14 @@ def check_decode(eng, E, layers, pt, toks, hs, overwrite_first, compiled=None):
                 assert len(set(pages.tolist())) == len(pages) and np.array_equal(app // 16, pages[j // 16])
             rows = eng.dec_cu[b] + eng.req_lens[b] + np.arange(n_dec)
             assert np.array_equal(pt_dec[l - 1, rows], slots)
+    # SLIDE's dirty-page counters: the link step's selected tokens (layers >= 2, read
+    # off the page table) and every decode token's K/V write
+    routes = []
+    for l in range(1, L + 1):
+        S = np.flatnonzero(pt[l - 1] != eng.reuse_slot_h[l - 1])
+        routes.append((pt[l - 1], S))
+    want = OP.dirty_counts(eng.n_pages, routes, eng.dec_slots_h[:, :, :n_dec].reshape(-1))
+    assert np.array_equal(eng.page_dirty.cpu().numpy(), want)
     # hidden state of every decode token after the last layer vs the oracle
     E64 = np64(E)
     W = [{kk: np64(vv) for kk, vv in layers[l].items()} for l in range(L)]
@@ -228,9 +237,9 @@ def test_decode_graph_replays_match_eager():
             hs.append(eng.decode_step(toks[t]).clone())
             torch.cuda.synchronize()
             hs[-1] = hs[-1].cpu()
-        runs.append((hs, eng.dec_slots_h.copy(), eng.pt_dec.cpu().clone()))
-    (h0, s0, p0), (h1, s1, p1) = runs
-    assert np.array_equal(s0, s1) and torch.equal(p0, p1)
+        runs.append((hs, eng.dec_slots_h.copy(), eng.pt_dec.cpu().clone(), eng.page_dirty.cpu().clone()))
+    (h0, s0, p0, c0), (h1, s1, p1, c1) = runs
+    assert np.array_equal(s0, s1) and torch.equal(p0, p1) and torch.equal(c0, c1)
     for t in range(n_dec):
         assert torch.equal(h0[t], h1[t]), t
     eng.close()

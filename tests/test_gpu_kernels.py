@@ -548,9 +548,12 @@ def test_slot_map(ctx):
     T = len(sel)
     slot_map = torch.zeros(n_tok, dtype=torch.int32, device=DEV)
     dst = torch.zeros(T, dtype=torch.int32, device=DEV)
+    n_pages = 600
+    dirty = torch.zeros(n_pages, dtype=torch.int32, device=DEV)
+    dirty[405] = 7           # counters accumulate over calls
     K.kvb_slot_map(ctx, sh(), desc, B, n_tok, T, i32(cu_rows), i32(sel), i32(reuse),
                    i32(np.concatenate(pages)), i32(np.concatenate([[0], np.cumsum([len(p) for p in pages])])),
-                   slot_map, dst)
+                   slot_map, dst, n_pages, dirty)
     torch.cuda.synchronize()
     sm, ds = slot_map.cpu().numpy(), dst.cpu().numpy()
     exp = reuse.astype(np.int64).copy()
@@ -561,6 +564,27 @@ def test_slot_map(ctx):
         assert list(got[:n_ok]) == list(OP.slot_of(pages[b], np.arange(n_ok)))
         assert np.all(got[n_ok:] == -1)
     assert np.array_equal(sm, exp)
+    # dirty counters: every selected token routed to a new page, layer-2 style
+    routes = [(np.zeros(n_tok, dtype=np.int64), np.zeros(0, dtype=np.int64)), (exp, np.concatenate(
+        [sels[b][:min(len(sels[b]), len(pages[b]) * 16)] for b in range(B)]))]
+    want = OP.dirty_counts(n_pages, routes)
+    want[405] += 7
+    assert np.array_equal(dirty.cpu().numpy(), want)
+
+
+def test_page_dirty_add(ctx):
+    """Decode-style counter updates: slots past the row count, negative or past
+    the pool are ignored; repeated pages accumulate."""
+    desc = K.model_desc(SHAPES["bf16"])
+    g = np.random.default_rng(9)
+    n_pages = 50
+    slots = g.integers(-20, n_pages * 16 + 40, size=700).astype(np.int32)
+    slots[:100] = g.integers(0, 32, size=100)        # many hits on pages 0 and 1
+    dirty = torch.zeros(n_pages, dtype=torch.int32, device=DEV)
+    K.kvb_page_dirty_add(ctx, sh(), desc, 700, i32([650]), i32(slots), n_pages, dirty)
+    torch.cuda.synchronize()
+    ok = slots[:650][(slots[:650] >= 0) & (slots[:650] < n_pages * 16)]
+    assert np.array_equal(dirty.cpu().numpy(), OP.dirty_counts(n_pages, [], ok))
 
 
 def test_embed(ctx):

@@ -272,6 +272,9 @@ def teacher_forced_wca(w, tau, tol, tier="hbm", rule="literal"):
             n_refresh += len(retired) > 0
             cur_state = cur_next
             prev = dict(gl, sel=gr["sel"], cu_rows=gr["cu_rows"])
+    # SLIDE's dirty-page counters: the selected tokens each layer >= 2 routed into each page
+    routes = [(rec.after[l]["slot_map"].cpu().numpy(), rows_of(rec.after[l])) for l in range(1, L + 1)]
+    assert np.array_equal(eng.page_dirty.cpu().numpy(), OP.dirty_counts(eng.n_pages, routes))
     eng.close()
     return n_refresh
 

@@ -192,3 +192,13 @@ def test_attnmap_and_topk_checks(lib):
     with pytest.raises(K.KvbError) as e:
         K.kvb_topk(FAKE_CTX, None, d, 1, 8, 1, 1, 1, 1, 1, 1, 1, 1, 1, 8)
     assert e.value.status == K.KVB_ERR_WORKSPACE
+
+
+def test_host_spill_order_matches_oracle(rng):
+    from oracle import pages as OP
+    from selective_kv_cache_amd.link import spill_order
+    for _ in range(50):
+        n = int(rng.integers(1, 40))
+        counts = rng.integers(0, 4, n) * (rng.random(n) > 0.4)
+        pages = rng.choice(n, int(rng.integers(0, n + 1)), replace=False)
+        assert spill_order(counts, pages) == OP.spill_order(counts, pages)

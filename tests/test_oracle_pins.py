@@ -562,3 +562,42 @@ def test_all_retire_schedule_and_stale_carry(case):
             prev = outs[l - 2]
             assert np.array_equal(outs[l - 1]["S"], prev["S"])
             assert np.array_equal(outs[l - 1]["h_in"], prev["h_rows"])
+
+
+# ------------------------------------------------------------ SLIDE dirty-page counters (hand-worked)
+
+def test_dirty_counts_and_spill_order_golden():
+    g = json.load(open(os.path.join(GOLDEN, "dirty_pages.json")))
+    rq = g["request"]
+    ch = lambda uid, n: wl.Chunk(uid=uid, kind="fixed", tokens=np.zeros(n, dtype=np.int32))
+    req = wl.Request([ch(i, n) for i, n in enumerate(rq["chunks"])])
+    L, N = rq["n_layers"], req.n_tokens
+    alloc = OP.PageAllocator(rq["n_pages"])
+    plan = OP.compile_plan(req.chunks, L, alloc)
+    assert {str(k): v for k, v in plan.items()} == g["compile_pages"]
+    new = {l: alloc.alloc(len(g["new_pages"][str(l)])) for l in range(1, L + 1)}
+    assert {str(l): p for l, p in new.items()} == g["new_pages"]
+    routes = []
+    for l in range(1, L + 1):
+        S = np.arange(N) if g["selected"][str(l)] == "all" else np.asarray(g["selected"][str(l)])
+        sm = OP.slot_map(OP.reuse_slots(req, plan, l), S, new[l])
+        if l > 1:
+            assert list(sm[S]) == g["new_slots_worked"][str(l)]
+        routes.append((sm, S))
+    # overwrite-first decode placement: the reused slots of each layer's recomputed tokens, in token order
+    n_dec = g["decode_tokens"]
+    dec = []
+    for l, (sm, S) in enumerate(routes, start=1):
+        dec += list(OP.reuse_slots(req, plan, l)[np.sort(S)][:n_dec])
+    assert dec == g["decode_slots_worked"]["slots"]
+    want_link = np.zeros(rq["n_pages"], dtype=np.int64)
+    for p, c in g["counts_after_link"].items():
+        want_link[int(p)] = c
+    assert np.array_equal(OP.dirty_counts(rq["n_pages"], routes), want_link)
+    want = np.zeros(rq["n_pages"], dtype=np.int64)
+    for p, c in g["counts_after_decode"].items():
+        want[int(p)] = c
+    counts = OP.dirty_counts(rq["n_pages"], routes, dec)
+    assert np.array_equal(counts, want)
+    assert OP.spill_order(counts, range(rq["n_pages"])) == g["spill_order_after_decode"]
+
