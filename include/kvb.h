@@ -195,7 +195,10 @@ kvb_status kvb_qkv_proj(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, 
 
 /* In-place rotate-half RoPE of q [T, Hq, hd] and k [T, Hkv, hd] at positions
  * tok_pos[row_tok[r]]: pair (j, j + hd/2) rotated by pos * base^(-2j/hd).
- * Angles are formed in double precision. */
+ * Recomputed tokens are given their correct absolute positions in the
+ * spliced prompt, while the compile step encodes every chunk from position 0
+ * (EPIC page, section 4.1), so the link step passes global positions and the
+ * compile step chunk-local ones.  Angles are formed in double precision. */
 kvb_status kvb_rope(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t T_max,
                     const int32_t* n_rows, const int32_t* row_tok, const int32_t* tok_pos, void* q,
                     void* k);
