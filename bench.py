@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--no-compile", action="store_true", help="skip timing the compile step")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode continuation leg")
     ap.add_argument("--no-cacheblend", action="store_true", help="skip the CacheBlend-style selection leg")
+    ap.add_argument("--no-sustained", action="store_true", help="skip the sustained-set leg")
+    ap.add_argument("--rule", choices=["literal", "dissim"], default="literal",
+                    help="retire rule of the timed step (dissim: the set stays at k on these weights)")
     ap.add_argument("--profile-only", action="store_true", help="warmup + timed steps only (for rocprofv3)")
     return ap.parse_args()
 
@@ -67,6 +70,117 @@ def kernel_work(eng, layer_rows, layer_pos, shape):
     # the embedding gathers every token's row, except in LegoLink (its static rows only)
     w["embed"] += (eng.T_sel if eng.cfg.mode == "legolink" else eng.N) * 2.0 * d * esz
     return w, rows_per_layer
+
+
+def record_schedule(eng):
+    """Realised rows and summed visible-key counts per layer of one link step
+    (deterministic), plus the state after layer 1 (CacheSlide)."""
+    import numpy as np
+    import torch
+
+    cfg = eng.cfg
+    layer_rows, layer_pos, state1 = [], [], {}
+
+    def hook(key, e):
+        if isinstance(key, tuple):
+            return
+        torch.cuda.synchronize()
+        if key == 1 and cfg.mode == "cacheslide":
+            layer_rows.append(e.N)
+            layer_pos.append(float(sum(n * (n + 1) / 2 for n in e.req_lens)))
+            cu = e.cu_rows[e.cur].cpu().numpy()
+            ns = int(e.s_count[0].item())
+            state1.update(hidden=e.hidden.clone(), alpha=e.alpha.clone(), d=e.d.clone(),
+                          ranking=e.ranking[:ns].cpu().numpy().copy(),
+                          sel=e.sel[e.cur][:cu[-1]].cpu().numpy().copy())
+            return
+        if cfg.mode == "cacheslide":
+            cu = e.cu_rows[e.cur].cpu().numpy()
+            sel = e.sel[e.cur][:cu[-1]].cpu().numpy()
+        else:
+            cu = e.lego_cu.cpu().numpy()
+            sel = e.lego_sel[:cu[-1]].cpu().numpy()
+        lo = e.lo_l.cpu().numpy()
+        layer_rows.append(int(cu[-1]))
+        layer_pos.append(float(np.sum(sel - lo[sel] + 1)))
+
+    eng.run_link(hook=hook)
+    torch.cuda.synchronize()
+    return layer_rows, layer_pos, state1
+
+
+def kernel_breakdown(eng, args):
+    """Per-kernel time of one link step (untimed pass, every launch bracketed by
+    HIP events), after warm-up."""
+    from selective_kv_cache_amd import _lib as K
+
+    for _ in range(max(args.warmup, 1)):
+        eng.run_link()
+    K.kvb_timing_enable(eng.ctx, "")
+    eng.run_link()
+    breakdown = K.kvb_timing_read(eng.ctx)
+    K.kvb_timing_enable(eng.ctx, None)
+    return breakdown
+
+
+def per_kernel_rates(breakdown, work):
+    per_kernel = {}
+    for name, v in breakdown.items():
+        b = BOUND.get(name)
+        entry = {"ms_per_step": round(v["ms"], 4), "launches": v["count"]}
+        if b and work.get(name):
+            if b == "mfma":
+                a_ = work[name] / (v["ms"] * 1e-3) / 1e12
+                entry.update(achieved_tflops=round(a_, 1), frac=round(a_ / PEAK_BF16_TFLOPS, 4))
+            else:
+                a_ = work[name] / (v["ms"] * 1e-3) / 1e9
+                entry.update(achieved_gbs=round(a_, 1), frac=round(a_ / PEAK_HBM_GBS, 4))
+        per_kernel[name] = entry
+    return per_kernel
+
+
+def sustained_leg(eng, args, st, s):
+    """The same request under the alternative retire rule (CKSim > 1 - tau), with
+    which no token retires on these weights: every layer 2..L recomputes the
+    full layer-1 selection, the schedule the method keeps when retired tokens
+    are refilled from a ranking that does not run out.  Timed like the
+    headline step (HIP events on the engine stream), with its own per-kernel
+    breakdown and rates."""
+    import numpy as np
+    import torch
+
+    from selective_kv_cache_amd import _lib as K
+
+    cfg = eng.cfg
+    saved = cfg.refresh_rule
+    cfg.refresh_rule = K.KVB_REFRESH_DISSIM
+    layer_rows, layer_pos, state1 = record_schedule(eng)
+    work, rows_per_layer = kernel_work(eng, layer_rows, layer_pos, s)
+    breakdown = kernel_breakdown(eng, args)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(st)
+        eng.run_link()
+        b.record(st)
+    torch.cuda.synchronize()
+    step_ms = [a.elapsed_time(b) for a, b in ev]
+    cfg.refresh_rule = saved
+    ms = float(np.mean(step_ms))
+    mfma_work = sum(work[k] for k, b in BOUND.items() if b == "mfma")
+    n_sel = len(state1["sel"])
+    return {"rule": "dissim", "ms_per_step": ms,
+            "step_ms_p10_median_p90": [float(np.percentile(step_ms, 10)), float(np.median(step_ms)),
+                                       float(np.percentile(step_ms, 90))],
+            "selected_tokens_per_s": n_sel / (ms * 1e-3),
+            "recomputed_row_layers": int(sum(rows_per_layer)),
+            "recomputed_row_layers_per_s": float(sum(rows_per_layer)) / (ms * 1e-3),
+            "rows_per_layer": rows_per_layer,
+            "algorithmic_mfma_tflop": mfma_work / 1e12,
+            "step_mfma_frac": mfma_work / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "kernels": per_kernel_rates(breakdown, work),
+            "note": "retire when CKSim > 1 - tau: no token retires on these weights, so every layer recomputes "
+                    "the layer-1 selection; same engine, weights and compiled cache as the headline step"}
 
 
 BOUND = {"gemm_qkv": "mfma", "gemm_oproj": "mfma", "gemm_swiglu": "mfma", "gemm_down": "mfma", "attention": "mfma",
@@ -346,52 +460,19 @@ def main():
     t_setup = time.perf_counter()
     E = wl.embedding_table(w, dev)
     layers = [wl.layer_weights(w, l, dev) for l in range(1, s.n_layers + 1)]
-    cfg = LinkConfig(mode=w.mode, ratio=w.ratio, tau=w.tau, period=w.period, lego_k=w.lego_k)
+    cfg = LinkConfig(mode=w.mode, ratio=w.ratio, tau=w.tau, period=w.period, lego_k=w.lego_k,
+                     refresh_rule=K.KVB_REFRESH_DISSIM if args.rule == "dissim" else K.KVB_REFRESH_LITERAL)
     eng = LinkEngine(Model(s, E, layers), w.requests, cfg, device=dev, max_decode=DECODE_TOKENS)
     eng.run_compile()
     torch.cuda.synchronize()
     print(f"# setup {time.perf_counter() - t_setup:.1f}s: {w.name}, N={eng.N}, pages={eng.n_pages}", file=sys.stderr,
           flush=True)
 
-    # realised rows / positions per layer (deterministic): one recorded run
-    layer_rows, layer_pos, state1 = [], [], {}
-
-    def hook(key, e):
-        if isinstance(key, tuple):
-            return
-        torch.cuda.synchronize()
-        if key == 1 and cfg.mode == "cacheslide":
-            layer_rows.append(e.N)
-            layer_pos.append(float(sum(n * (n + 1) / 2 for n in e.req_lens)))
-            cu = e.cu_rows[e.cur].cpu().numpy()
-            ns = int(e.s_count[0].item())
-            state1.update(hidden=e.hidden.clone(), alpha=e.alpha.clone(), d=e.d.clone(),
-                          ranking=e.ranking[:ns].cpu().numpy().copy(),
-                          sel=e.sel[e.cur][:cu[-1]].cpu().numpy().copy())
-            return
-        if cfg.mode == "cacheslide":
-            cu = e.cu_rows[e.cur].cpu().numpy()
-            sel = e.sel[e.cur][:cu[-1]].cpu().numpy()
-        else:
-            cu = e.lego_cu.cpu().numpy()
-            sel = e.lego_sel[:cu[-1]].cpu().numpy()
-        lo = e.lo_l.cpu().numpy()
-        layer_rows.append(int(cu[-1]))
-        layer_pos.append(float(np.sum(sel - lo[sel] + 1)))
-
-    eng.run_link(hook=hook)
-    torch.cuda.synchronize()
+    layer_rows, layer_pos, state1 = record_schedule(eng)
     work, rows_per_layer = kernel_work(eng, layer_rows, layer_pos, s)
     # selected tokens of the link step: |S_k| chosen at layer 1 (CacheSlide) or the static set (LegoLink)
     n_selected = len(state1["sel"]) if cfg.mode == "cacheslide" else eng.T_sel
-
-    # per-kernel breakdown (untimed pass, every launch bracketed)
-    for _ in range(max(args.warmup, 1)):
-        eng.run_link()
-    K.kvb_timing_enable(eng.ctx, "")
-    eng.run_link()
-    breakdown = K.kvb_timing_read(eng.ctx)
-    K.kvb_timing_enable(eng.ctx, None)
+    breakdown = kernel_breakdown(eng, args)
     dominant = max(breakdown, key=lambda k: breakdown[k]["ms"])
 
     # timed steps: HIP events on the engine stream around each step; the dominant
@@ -446,18 +527,7 @@ def main():
                 traffic = t.get("bytes_per_launch")
         except Exception:
             traffic = None
-    per_kernel = {}
-    for name, v in breakdown.items():
-        b = BOUND.get(name)
-        entry = {"ms_per_step": round(v["ms"], 4), "launches": v["count"]}
-        if b and work.get(name):
-            if b == "mfma":
-                a_ = work[name] / (v["ms"] * 1e-3) / 1e12
-                entry.update(achieved_tflops=round(a_, 1), frac=round(a_ / PEAK_BF16_TFLOPS, 4))
-            else:
-                a_ = work[name] / (v["ms"] * 1e-3) / 1e9
-                entry.update(achieved_gbs=round(a_, 1), frac=round(a_ / PEAK_HBM_GBS, 4))
-        per_kernel[name] = entry
+    per_kernel = per_kernel_rates(breakdown, work)
     B = eng.B
     out = {
         "metric": "link-step selected-tokens/s",
@@ -485,6 +555,8 @@ def main():
         "step_ms_p10_median_p90": [float(np.percentile(step_ms, 10)), float(np.median(step_ms)),
                                    float(np.percentile(step_ms, 90))],
     }
+    if cfg.mode == "cacheslide" and not args.no_sustained:
+        out["sustained"] = sustained_leg(eng, args, st, s)
     if not args.no_decode:
         out["decode"] = decode_leg(eng, st)
     if cfg.mode == "cacheslide":
