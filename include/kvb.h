@@ -117,7 +117,7 @@ kvb_status kvb_workspace_size(kvb_ctx* ctx, const kvb_model_desc* desc, int32_t 
  * HIP events on its stream; filter == NULL turns timing off.  Kernel names:
  * embed, rmsnorm, gemm_qkv, rope, blend_scatter, attention, attention_merge, gemm_oproj, gemm_swiglu,
  * gemm_down, splitk_reduce, deviation, topk_sort, topk_rank, topk_compact, refresh_flag,
- * refresh_compact, slot_copy, slot_scatter, page_dirty, attnmap, attnmap_reduce. */
+ * refresh_compact, slot_copy, slot_scatter, page_dirty, rope_fuse, attnmap, attnmap_reduce. */
 kvb_status kvb_timing_enable(kvb_ctx* ctx, const char* filter);
 /* Waits for the recorded events and folds them into per-kernel totals, then
  * sets *needed to the size of the JSON text {"name": {"count": n, "ms": t}, ...}
@@ -192,6 +192,25 @@ kvb_status kvb_qkv_proj(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, 
                         const int32_t* n_rows, const int32_t* row_tok, const void* hidden,
                         const void* norm_w, const void* w_qkv, const int32_t* tok_pos, void* q,
                         void* k, void* v, void* ws, size_t ws_bytes, int32_t flags);
+
+/* Q/K/V projection, RoPE, and the fusion + scatter of the recomputed K/V
+ * into the page pool: what kvb_qkv_proj (with tok_pos) followed by
+ * kvb_blend_scatter on its k and v computes (EPIC page, section 4, LegoLink
+ * step 2; CacheSlide page, Algorithm 2 fusion line and alpha definition;
+ * SLIDE's new pages), with the rotation, the fusion and the scatter done in
+ * one pass over each row after the projection.  The arguments are
+ * kvb_qkv_proj's, then kvb_blend_scatter's from k_pool on (dst_slot required;
+ * src_slot NULL: KVB_ALPHA_ONE only and d_out / cksim_out NULL), then ws,
+ * ws_bytes and flags as for kvb_qkv_proj.  q, k, v and every pool, alpha,
+ * d_out and cksim_out value are those of the two-call sequence.  Workspace:
+ * kvb_workspace_size. */
+kvb_status kvb_qkv_fused(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t T_max,
+                         const int32_t* n_rows, const int32_t* row_tok, const void* hidden,
+                         const void* norm_w, const void* w_qkv, const int32_t* tok_pos, void* q,
+                         void* k, void* v, void* k_pool, void* v_pool, int32_t n_pages,
+                         const int32_t* src_slot, const int32_t* dst_slot, int32_t alpha_mode,
+                         float* alpha, float* d_out, float* cksim_out, void* ws, size_t ws_bytes,
+                         int32_t flags);
 
 /* In-place rotate-half RoPE of q [T, Hq, hd] and k [T, Hkv, hd] at positions
  * tok_pos[row_tok[r]]: pair (j, j + hd/2) rotated by pos * base^(-2j/hd).

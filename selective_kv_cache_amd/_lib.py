@@ -58,6 +58,7 @@ _SIGS = {
     "kvb_pages_copy": ([P, P, P, I, P, P, P, P, P, I], I),
     "kvb_embed": ([P, P, P, I, P, P, P, I, P, P], I),
     "kvb_qkv_proj": ([P, P, P, I, P, P, P, P, P, P, P, P, P, P, c_size_t, I], I),
+    "kvb_qkv_fused": ([P, P, P, I, P, P, P, P, P, P, P, P, P, P, P, I, P, P, I, P, P, P, P, c_size_t, I], I),
     "kvb_rope": ([P, P, P, I, P, P, P, P, P], I),
     "kvb_blend_scatter": ([P, P, P, I, P, P, P, P, P, P, I, P, P, I, P, P, P], I),
     "kvb_sparse_query_attn": ([P, P, P, I, P, P, P, P, P, P, I, P, c_float, P, P, c_size_t], I),
@@ -222,6 +223,12 @@ def kvb_qkv_proj(ctx, stream, desc, T_max, n_rows, row_tok, hidden, norm_w, w_qk
                  ws=None, ws_bytes=0, flags=0):
     _call("kvb_qkv_proj", ctx, stream, desc, T_max, n_rows, row_tok, hidden, norm_w, w_qkv,
           tok_pos, q, k, v, ws, ws_bytes, flags)
+
+
+def kvb_qkv_fused(ctx, stream, desc, T_max, n_rows, row_tok, hidden, norm_w, w_qkv, tok_pos, q, k, v, k_pool, v_pool,
+                  n_pages, src_slot, dst_slot, alpha_mode, alpha, d_out, cksim_out, ws=None, ws_bytes=0, flags=0):
+    _call("kvb_qkv_fused", ctx, stream, desc, T_max, n_rows, row_tok, hidden, norm_w, w_qkv, tok_pos, q, k, v,
+          k_pool, v_pool, n_pages, src_slot, dst_slot, alpha_mode, alpha, d_out, cksim_out, ws, ws_bytes, flags)
 
 
 def kvb_rope(ctx, stream, desc, T_max, n_rows, row_tok, tok_pos, q, k):

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
+#include <math.h>
 
 #include <string>
 #include <vector>
@@ -161,6 +162,41 @@ __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
   typedef float f2_t __attribute__((ext_vector_type(2)));
   typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){a, b}, b2_t));
+}
+
+// slot s of head h in a K or V pool laid out [page][head][16][hd]
+__device__ __forceinline__ size_t pool_off(int slot, int h, int Hkv, int hd) {
+  return (((size_t)(slot >> 4) * Hkv + h) * 16 + (slot & 15)) * hd;
+}
+
+// CacheSlide's correction weight d / ||K_reuse||^2 (0 if both are 0, 1 if
+// only the norm is 0)
+__device__ __forceinline__ float alpha_rule(float d, float nrm) {
+  if (nrm > 0.f) return d / nrm;
+  return d == 0.f ? 0.f : 1.f;
+}
+
+// Rotate-half RoPE frequencies base^(-2j/hd), j < hd / 2, in double precision,
+// formed on the host and passed to the kernels by value.
+struct RopeFreq {
+  double f[64];
+};
+
+inline RopeFreq rope_freq(int hd, float base) {
+  RopeFreq rf{};
+  for (int j = 0; j < hd / 2 && j < 64; j++) rf.f[j] = exp2(-2.0 * (double)j / (double)hd * log2((double)base));
+  return rf;
+}
+
+// cosine and sine of the angle pos * f: formed and reduced to [-pi, pi] in
+// double precision, then sincos in float
+__device__ __forceinline__ float2 rope_cs(int pos, double f) {
+  const double a = (double)pos * f;
+  const double twopi = 6.283185307179586;
+  const double red = fma(-rint(a / twopi), twopi, a);
+  float s, c;
+  sincosf((float)red, &s, &c);
+  return make_float2(c, s);
 }
 
 // wave64 reductions

@@ -6,6 +6,8 @@
 // bitwise reproducible from run to run and from batch to batch.
 #include "common.h"
 
+#include <algorithm>
+
 namespace kvb {
 
 // ------------------------------------------------------------------ embedding
@@ -34,26 +36,25 @@ __global__ void embed_kernel(int T_max, const int32_t* __restrict__ n_rows, cons
 template <class T> __device__ __forceinline__ void load8(const T* p, float* o);
 template <class T> __device__ __forceinline__ void store8(T* p, const float* v);
 
+// the two halves of a rotated pair, with the products and their one fused
+// add spelled out so that every kernel rounds them the same way
+__device__ __forceinline__ float rot_lo(float x1, float x2, float c, float s) { return fmaf(x1, c, -(x2 * s)); }
+__device__ __forceinline__ float rot_hi(float x2, float x1, float c, float s) { return fmaf(x2, c, x1 * s); }
+
 template <class T>
 __global__ void __launch_bounds__(256) rope_kernel(int T_max, const int32_t* __restrict__ n_rows,
                                                    const int32_t* __restrict__ row_tok,
                                                    const int32_t* __restrict__ tok_pos, T* __restrict__ q,
-                                                   T* __restrict__ k, int Hq, int Hkv, int hd, float base) {
+                                                   T* __restrict__ k, int Hq, int Hkv, int hd, RopeFreq rf) {
   const int r = blockIdx.x;
   if (r >= row_count(n_rows, T_max)) return;
   const int g = row_tok ? row_tok[r] : r;
-  const double pos = (double)tok_pos[g];
   const int half = hd / 2;
   __shared__ float cs[64], sn[64];
   if (threadIdx.x < half) {
-    const int j = threadIdx.x;
-    const double a = pos * exp2(-2.0 * (double)j / (double)hd * log2((double)base));
-    const double twopi = 6.283185307179586;
-    const double red = fma(-rint(a / twopi), twopi, a);
-    float s, c;
-    sincosf((float)red, &s, &c);
-    cs[j] = c;
-    sn[j] = s;
+    const float2 c = rope_cs(tok_pos[g], rf.f[threadIdx.x]);
+    cs[threadIdx.x] = c.x;
+    sn[threadIdx.x] = c.y;
   }
   __syncthreads();
   // one item = 8 consecutive pairs (j .. j+7, j+half .. j+half+7) of one head
@@ -67,21 +68,14 @@ __global__ void __launch_bounds__(256) rope_kernel(int T_max, const int32_t* __r
     load8<T>(x + j + half, x2);
 #pragma unroll
     for (int e = 0; e < 8; e++) {
-      const float c = cs[j + e], sv = sn[j + e];
-      y1[e] = x1[e] * c - x2[e] * sv;
-      y2[e] = x2[e] * c + x1[e] * sv;
+      y1[e] = rot_lo(x1[e], x2[e], cs[j + e], sn[j + e]);
+      y2[e] = rot_hi(x2[e], x1[e], cs[j + e], sn[j + e]);
     }
     store8<T>(x + j, y1);
     store8<T>(x + j + half, y2);
   }
 }
 
-// ------------------------------------------------------------------ pool addressing
-
-__device__ __forceinline__ size_t pool_off(int slot, int h, int Hkv, int hd) {
-  // page-major: [page][head][16][hd]
-  return (((size_t)(slot >> 4) * Hkv + h) * 16 + (slot & 15)) * hd;
-}
 
 // 8 consecutive elements of a row as float
 template <class T> __device__ __forceinline__ void load8(const T* p, float* o);
@@ -168,10 +162,7 @@ __device__ RowSums row_sums(const float* a, const float* b, bool active, int Hkv
   return s;
 }
 
-__device__ __forceinline__ float alpha_rule(float d, float nrm) {
-  if (nrm > 0.f) return d / nrm;
-  return d == 0.f ? 0.f : 1.f;
-}
+
 
 // ------------------------------------------------------------------ fusion + scatter
 // One block per row; thread t owns elements 8t..8t+7 of the [Hkv*hd] row.
@@ -241,6 +232,163 @@ __global__ void blend_scatter_kernel(int T_max, const int32_t* __restrict__ n_ro
   store8<T>(v_pool + pool_off(dst, h, Hkv, hd) + e0, vo);
 }
 
+// ------------------------------------------------------------------ RoPE + fusion + scatter
+// What rope_kernel followed by blend_scatter_kernel computes, in one pass over
+// the row: one block per row.  The Q vectors (8 elements each) are rotated in
+// place; then thread t owns vector t of the row's [K | V] (a head's hd / 8
+// vectors in consecutive lanes, as in blend_scatter_kernel): K is rotated and
+// stored, and K and V are fused with the cached rows and scattered to the new
+// slot.  RoPE takes the partner half of each pair from the lane hd / 16 away;
+// the per-head K sums use row_sums' butterfly and head order.
+
+// in-place rotate-half of one 8-element vector, vector vi of its head (VPH
+// vectors per head): pairs j .. j + 7 with j = (vi % (VPH / 2)) * 8
+template <int VPH>
+__device__ __forceinline__ void rotate8(float (&x)[8], int vi, const float2* cs) {
+  float w[8];
+#pragma unroll
+  for (int e = 0; e < 8; e++) w[e] = __shfl_xor(x[e], VPH / 2, 64);
+  const int j = (vi % (VPH / 2)) * 8;
+  if (vi < VPH / 2) {
+#pragma unroll
+    for (int e = 0; e < 8; e++) x[e] = rot_lo(x[e], w[e], cs[j + e].x, cs[j + e].y);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; e++) x[e] = rot_hi(x[e], w[e], cs[j + e].x, cs[j + e].y);
+  }
+}
+
+template <class T> __device__ __forceinline__ float round_to(float v);
+template <> __device__ __forceinline__ float round_to<float>(float v) { return v; }
+template <> __device__ __forceinline__ float round_to<bf16_t>(float v) { return bf2f(f2bf(v)); }
+
+template <class T, int VPH, int QI>
+__global__ void __launch_bounds__(1024) rope_fuse_kernel(int T_max, const int32_t* __restrict__ n_rows,
+                                                         const int32_t* __restrict__ row_tok,
+                                                         const int32_t* __restrict__ tok_pos, T* __restrict__ q,
+                                                         T* __restrict__ k, const T* __restrict__ v,
+                                                         T* __restrict__ k_pool, T* __restrict__ v_pool, int n_slots,
+                                                         const int32_t* __restrict__ src_slot,
+                                                         const int32_t* __restrict__ dst_slot, int alpha_mode,
+                                                         float* __restrict__ alpha, float* __restrict__ d_out,
+                                                         float* __restrict__ cksim_out, int Hq, int Hkv, int hd,
+                                                         RopeFreq rf) {
+  __shared__ float2 cs[64];
+  __shared__ float sh[4 * 64];
+  const int r = blockIdx.x;
+  if (r >= row_count(n_rows, T_max)) return;
+  const int t = threadIdx.x, nth = blockDim.x;
+  const int nq = Hq * VPH, nk = Hkv * VPH;
+  // every load that depends on the row alone is issued first, so their
+  // latencies overlap the token lookups and the angles
+  const bool act = t < 2 * nk, is_k = t < nk;
+  const int u = is_k ? t : t - nk, h = u / VPH, e0 = (u % VPH) * 8;
+  float xq[QI][8], x[8], ru[8];
+  T* qr = q + (size_t)r * Hq * hd;
+  if (tok_pos) {
+#pragma unroll
+    for (int i = 0; i < QI; i++) {
+      const int iv = i * nth + t;
+      if (iv < nq) load8<T>(qr + iv * 8, xq[i]);
+      else {
+#pragma unroll
+        for (int e = 0; e < 8; e++) xq[i][e] = 0.f;
+      }
+    }
+  }
+  if (act) load8<T>(is_k ? k + (size_t)r * nk * 8 + u * 8 : v + (size_t)r * nk * 8 + u * 8, x);
+  else {
+#pragma unroll
+    for (int e = 0; e < 8; e++) x[e] = 0.f;
+  }
+  const int g = row_tok ? row_tok[r] : r;
+  const int src = src_slot ? src_slot[g] : -1;
+  const bool have_src = src_slot && src >= 0 && src < n_slots;
+#pragma unroll
+  for (int e = 0; e < 8; e++) ru[e] = 0.f;
+  if (act && have_src) load8<T>((is_k ? k_pool : v_pool) + pool_off(src, h, Hkv, hd) + e0, ru);
+  const float a_old = (src_slot && alpha && alpha_mode == KVB_ALPHA_LAG) ? alpha[g] : 1.f;
+  if (tok_pos && t < hd / 2) cs[t] = rope_cs(tok_pos[g], rf.f[t]);
+  __syncthreads();
+  if (tok_pos) {
+    // Q rotated in place (every lane runs each step, so the exchanges see whole heads)
+#pragma unroll
+    for (int i = 0; i < QI; i++) {
+      const int iv = i * nth + t;
+      rotate8<VPH>(xq[i], iv % VPH, cs);
+      if (iv < nq) store8<T>(qr + iv * 8, xq[i]);
+    }
+    // K rotated and stored; V lanes take part in the exchange and keep their values
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) y[e] = x[e];
+    rotate8<VPH>(y, u % VPH, cs);
+    if (is_k) {
+#pragma unroll
+      for (int e = 0; e < 8; e++) x[e] = round_to<T>(y[e]);  // the stored rotated key
+      if (act) store8<T>(k + (size_t)r * nk * 8 + u * 8, x);
+    }
+  }
+  float a_use = 1.f;
+  if (src_slot) {
+    float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+    if (act && is_k) {
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const float df = x[i] - ru[i];
+        p0 += df * df;
+        p1 += ru[i] * ru[i];
+        p2 += x[i] * ru[i];
+        p3 += x[i] * x[i];
+      }
+    }
+    p0 = head_reduce<VPH>(p0);
+    p1 = head_reduce<VPH>(p1);
+    p2 = head_reduce<VPH>(p2);
+    p3 = head_reduce<VPH>(p3);
+    if (act && is_k && (u % VPH) == 0) {
+      sh[h * 4 + 0] = p0;
+      sh[h * 4 + 1] = p1;
+      sh[h * 4 + 2] = p2;
+      sh[h * 4 + 3] = p3;
+    }
+    __syncthreads();
+    float d = 0.f, nrm = 0.f, cks = 0.f;
+    for (int hh = 0; hh < Hkv; hh++) {
+      d += sh[hh * 4 + 0];
+      nrm += sh[hh * 4 + 1];
+      const float na = sh[hh * 4 + 3], nb = sh[hh * 4 + 1];
+      float c;
+      if (na == 0.f && nb == 0.f) c = 1.f;
+      else if (na == 0.f || nb == 0.f) c = 0.f;
+      else c = sh[hh * 4 + 2] / (sqrtf(na) * sqrtf(nb));
+      cks += c;
+    }
+    cks /= (float)Hkv;
+    const float a_new = alpha_rule(d, nrm);
+    if (alpha_mode == KVB_ALPHA_LAG) a_use = a_old;
+    else if (alpha_mode == KVB_ALPHA_CURRENT) a_use = a_new;
+    // alpha[g] was read before the first barrier, so thread 0 may overwrite it
+    if (t == 0) {
+      if (alpha && alpha_mode != KVB_ALPHA_ONE) alpha[g] = a_new;
+      if (d_out) d_out[r] = d;
+      if (cksim_out) cksim_out[r] = cks;
+    }
+  }
+  const int dst = dst_slot[r];
+  if (!act || dst < 0 || dst >= n_slots) return;
+  float o[8];
+  if (src_slot && a_use != 1.f) {
+    const float b = 1.f - a_use;
+#pragma unroll
+    for (int i = 0; i < 8; i++) o[i] = a_use * x[i] + b * ru[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; i++) o[i] = x[i];
+  }
+  store8<T>((is_k ? k_pool : v_pool) + pool_off(dst, h, Hkv, hd) + e0, o);
+}
+
 // ------------------------------------------------------------------ deviation (layer 1)
 // d[g], alpha[g] and the 64-bit sort key (~bits(d) << 32 | g) for every token.
 
@@ -299,7 +447,7 @@ kvb_status launch_rope(hipStream_t st, int T_max, const int32_t* n_rows, const i
   if (T_max == 0) return KVB_OK;
   LaunchTimer lt(st, "rope");
   rope_kernel<T><<<T_max, 256, 0, st>>>(T_max, n_rows, row_tok, tok_pos, (T*)q, (T*)k, d->n_q_heads, d->n_kv_heads,
-                                        d->head_dim, d->rope_base);
+                                        d->head_dim, rope_freq(d->head_dim, d->rope_base));
   return check_launch("rope_kernel");
 }
 template kvb_status launch_rope<float>(hipStream_t, int, const int32_t*, const int32_t*, const int32_t*, void*, void*,
@@ -473,4 +621,62 @@ extern "C" kvb_status kvb_page_dirty_add(kvb_ctx* ctx, void* stream, const kvb_m
   LaunchTimer lt(st, "page_dirty");
   page_dirty_add_kernel<<<cdiv(T_max, 256), 256, 0, st>>>(T_max, n_rows, slots, n_pages, page_dirty);
   return check_launch("page_dirty_add_kernel");
+}
+
+extern "C" kvb_status kvb_qkv_fused(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, int32_t T_max,
+                                    const int32_t* n_rows, const int32_t* row_tok, const void* hidden,
+                                    const void* norm_w, const void* w_qkv, const int32_t* tok_pos, void* q, void* k,
+                                    void* v, void* k_pool, void* v_pool, int32_t n_pages, const int32_t* src_slot,
+                                    const int32_t* dst_slot, int32_t alpha_mode, float* alpha, float* d_out,
+                                    float* cksim_out, void* ws, size_t ws_bytes, int32_t flags) {
+  KVB_TRY(check_ctx(ctx));
+  KVB_TRY(check_desc(desc));
+  if (T_max < 0 || n_pages < 0) return fail(KVB_ERR_INVALID_ARG, "negative size");
+  if (alpha_mode != KVB_ALPHA_LAG && alpha_mode != KVB_ALPHA_CURRENT && alpha_mode != KVB_ALPHA_ONE)
+    return fail(KVB_ERR_INVALID_ARG, "bad alpha_mode");
+  if (T_max == 0) return KVB_OK;
+  KVB_CHECK_PTR(k_pool, "k_pool");
+  KVB_CHECK_PTR(v_pool, "v_pool");
+  KVB_CHECK_PTR(dst_slot, "dst_slot");
+  if (!src_slot && (alpha_mode != KVB_ALPHA_ONE || d_out || cksim_out))
+    return fail(KVB_ERR_INVALID_ARG, "without src_slot only KVB_ALPHA_ONE and no d_out / cksim_out");
+  if ((long)n_pages * 16 > 0x7fffffffL) return fail(KVB_ERR_INVALID_ARG, "too many pages for int32 slots");
+  const int Hkv = desc->n_kv_heads, hd = desc->head_dim;
+  const int nkv = 2 * Hkv * hd / 8;  // K and V vectors of a row, one per thread
+  if (nkv > 1024 || Hkv > 64 || (long)desc->n_q_heads * hd / 8 > 8L * std::max(64, (nkv + 63) / 64 * 64)) {
+    KVB_TRY(kvb_qkv_proj(ctx, stream, desc, T_max, n_rows, row_tok, hidden, norm_w, w_qkv, tok_pos, q, k, v, ws,
+                         ws_bytes, flags));
+    return kvb_blend_scatter(ctx, stream, desc, T_max, n_rows, row_tok, k, v, k_pool, v_pool, n_pages, src_slot,
+                             dst_slot, alpha_mode, alpha, d_out, cksim_out);
+  }
+  // the projection without RoPE, then the rotation, fusion and scatter in one pass
+  KVB_TRY(kvb_qkv_proj(ctx, stream, desc, T_max, n_rows, row_tok, hidden, norm_w, w_qkv, nullptr, q, k, v, ws,
+                       ws_bytes, flags));
+  CtxScope scope(ctx);
+  hipStream_t st = (hipStream_t)stream;
+  const int threads = std::max(64, (nkv + 63) / 64 * 64);
+  const int qi = cdiv((long)desc->n_q_heads * hd / 8, threads);  // Q vectors per thread
+  const RopeFreq rf = rope_freq(hd, desc->rope_base);
+  const int ns = n_pages * 16;
+  LaunchTimer lt(st, "rope_fuse");
+#define KVB_ROPE_FUSE(T, VPH, QI)                                                                              \
+  rope_fuse_kernel<T, VPH, QI><<<T_max, threads, 0, st>>>(T_max, n_rows, row_tok, tok_pos, (T*)q, (T*)k,       \
+                                                          (const T*)v, (T*)k_pool, (T*)v_pool, ns, src_slot,   \
+                                                          dst_slot, alpha_mode, alpha, d_out, cksim_out,       \
+                                                          desc->n_q_heads, Hkv, hd, rf)
+#define KVB_ROPE_FUSE_QI(T, VPH)                     \
+  if (qi <= 1) KVB_ROPE_FUSE(T, VPH, 1);             \
+  else if (qi <= 2) KVB_ROPE_FUSE(T, VPH, 2);        \
+  else if (qi <= 4) KVB_ROPE_FUSE(T, VPH, 4);        \
+  else KVB_ROPE_FUSE(T, VPH, 8);
+  if (desc->dtype == KVB_BF16) {
+    if (hd == 128) { KVB_ROPE_FUSE_QI(bf16_t, 16) }
+    else { KVB_ROPE_FUSE_QI(bf16_t, 8) }
+  } else {
+    if (hd == 128) { KVB_ROPE_FUSE_QI(float, 16) }
+    else { KVB_ROPE_FUSE_QI(float, 8) }
+  }
+#undef KVB_ROPE_FUSE_QI
+#undef KVB_ROPE_FUSE
+  return check_launch("rope_fuse_kernel");
 }

@@ -304,10 +304,9 @@ class LinkEngine:
         K.kvb_embed(c, sh, ds, Nc, None, None, self.tok_c, self.shape.vocab, m.embedding, self.hidden_c)
         for l in range(1, self.L + 1):
             W = m.layers[l - 1]
-            K.kvb_qkv_proj(c, sh, ds, Nc, None, None, self.hidden_c, W["norm1"], W["w_qkv"], self.pos_c,
-                           self.q, self.k, self.v, self.ws, self.ws_bytes)
-            K.kvb_blend_scatter(c, sh, ds, Nc, None, None, self.k, self.v, self.k_pool, self.v_pool, self.n_pages,
-                                None, self.comp_slot[l - 1], K.KVB_ALPHA_ONE, None, None, None)
+            K.kvb_qkv_fused(c, sh, ds, Nc, None, None, self.hidden_c, W["norm1"], W["w_qkv"], self.pos_c,
+                            self.q, self.k, self.v, self.k_pool, self.v_pool, self.n_pages, None,
+                            self.comp_slot[l - 1], K.KVB_ALPHA_ONE, None, None, None, self.ws, self.ws_bytes)
             if l < self.L:
                 K.kvb_sparse_query_attn(c, sh, ds, Nc, None, None, self.lo_c, self.q, self.k_pool, self.v_pool,
                                         self.n_pages, self.comp_slot[l - 1], self.scale, self.o, self.ws,
@@ -429,10 +428,10 @@ class LinkEngine:
         # layer 1's keys must be bitwise those of the compile step (chunk 0 deviates by
         # exactly 0): batch-invariant there; the selective layers may split K
         flags = K.KVB_QKV_BATCH_INVARIANT if l == 1 else K.KVB_QKV_SPLIT_K
-        K.kvb_qkv_proj(c, sh, ds, T, n_rows, rows, self.hidden, W["norm1"], W["w_qkv"], self.pos_l, self.q, self.k,
-                       self.v, self.ws, self.ws_bytes, flags)
-        K.kvb_blend_scatter(c, sh, ds, T, n_rows, rows, self.k, self.v, self.k_pool, self.v_pool, self.n_pages,
-                            src_slot, self.dst_slot, alpha_mode, alpha, d_out, cksim_out)
+        # projection, RoPE, fusion with the cached rows and scatter to the new slots
+        K.kvb_qkv_fused(c, sh, ds, T, n_rows, rows, self.hidden, W["norm1"], W["w_qkv"], self.pos_l, self.q,
+                        self.k, self.v, self.k_pool, self.v_pool, self.n_pages, src_slot, self.dst_slot, alpha_mode,
+                        alpha, d_out, cksim_out, self.ws, self.ws_bytes, flags)
         if after_blend:
             after_blend()
         K.kvb_sparse_query_attn(c, sh, ds, T, n_rows, rows, self.lo_l, self.q, self.k_pool, self.v_pool,
@@ -682,10 +681,10 @@ class LinkEngine:
         K.kvb_embed(c, sh, ds, B, None, None, self._dec_tok, self.shape.vocab, m.embedding, self.hidden_dec)
         for l in range(1, L + 1):
             W = m.layers[l - 1]
-            K.kvb_qkv_proj(c, sh, ds, B, None, None, self.hidden_dec, W["norm1"], W["w_qkv"], self._dec_pos, self.q,
-                           self.k, self.v, self.ws, self.ws_bytes, K.KVB_QKV_SPLIT_K)
-            K.kvb_blend_scatter(c, sh, ds, B, None, None, self.k, self.v, self.k_pool, self.v_pool, self.n_pages,
-                                None, self._dec_slots[l - 1], K.KVB_ALPHA_ONE, None, None, None)
+            K.kvb_qkv_fused(c, sh, ds, B, None, None, self.hidden_dec, W["norm1"], W["w_qkv"], self._dec_pos,
+                            self.q, self.k, self.v, self.k_pool, self.v_pool, self.n_pages, None,
+                            self._dec_slots[l - 1], K.KVB_ALPHA_ONE, None, None, None, self.ws, self.ws_bytes,
+                            K.KVB_QKV_SPLIT_K)
             K.kvb_sparse_query_attn(c, sh, ds, B, None, self._dec_rows, self.lo_dec, self.q, self.k_pool, self.v_pool,
                                     self.n_pages, pt[l - 1], self.scale, self.o, self.ws, self.ws_bytes)
             K.kvb_mlp(c, sh, ds, B, None, None, self.o, W["w_o"], self.hidden_dec, W["norm2"], W["w_gate_up"],

@@ -227,6 +227,132 @@ def test_blend_scatter(ctx, name, mode):
     assert np.array_equal(_rows_at(kp, untouched, s), _rows_at(kp0, untouched, s))
 
 
+@pytest.mark.parametrize("name", ["bf16", "bf16_hd64", "bf16_wide", "fp32"])
+@pytest.mark.parametrize("mode,cached", [(K.KVB_ALPHA_LAG, True), (K.KVB_ALPHA_ONE, True), (K.KVB_ALPHA_ONE, False),
+                                         (K.KVB_ALPHA_CURRENT, True)], ids=["lag", "one", "one-nocache", "current"])
+@pytest.mark.parametrize("flags,T_max,n_valid", [(K.KVB_QKV_BATCH_INVARIANT, 200, 173), (K.KVB_QKV_SPLIT_K, 200, 173),
+                                                 (K.KVB_QKV_SPLIT_K, 1, 1)], ids=["inv", "splitk", "one-row"])
+def test_qkv_fused(ctx, name, mode, cached, flags, T_max, n_valid):
+    """Projection, then RoPE + fusion + scatter in one pass: bitwise the result of
+    kvb_qkv_proj (with positions) followed by kvb_blend_scatter on the same
+    inputs; Q/K/V against the oracle, and the fused rows, d, alpha and CKSim
+    against the oracle applied to the call's own recomputed K/V."""
+    s = SHAPES[name]
+    g = np.random.default_rng(31 + mode + 7 * T_max)
+    desc = K.model_desc(s)
+    dt = tdt(s)
+    n_tok, n_pages = 300, 64
+    hidden = rand((n_tok, s.d_model), g, dtype=dt).to(DEV)
+    W = weights(s, g)
+    rows = np.sort(g.choice(n_tok, T_max, replace=False))
+    pos = g.integers(0, 32768, n_tok)
+    kp, vp = _pool(s, n_pages, g)
+    perm = g.permutation(n_pages * 16)
+    src_slot = perm[:n_tok]
+    dst = perm[n_tok:n_tok + T_max].copy()
+    if T_max > 1:
+        dst[4] = -1                                   # a row with no new slot: nothing scattered
+        kp[src_slot[rows[6]] // 16, :, src_slot[rows[6]] % 16, :] = 0   # a zero cached key
+    kp0, vp0 = kp.clone(), vp.clone()
+    alpha0 = g.uniform(-0.5, 2.0, n_tok).astype(np.float32)
+    alpha0[rows[0]] = 1.0
+    ws, wsb = workspace(ctx, desc, T_max, n_tok)
+
+    def run(fused):
+        o = dict(q=torch.full((T_max, s.n_q_heads, s.head_dim), 7.0, dtype=dt, device=DEV),
+                 k=torch.full((T_max, s.n_kv_heads, s.head_dim), 7.0, dtype=dt, device=DEV),
+                 v=torch.full((T_max, s.n_kv_heads, s.head_dim), 7.0, dtype=dt, device=DEV),
+                 kp=kp0.clone(), vp=vp0.clone(), alpha=torch.tensor(alpha0, device=DEV),
+                 d=torch.full((T_max,), -1.0, device=DEV), ck=torch.full((T_max,), -9.0, device=DEV))
+        blend = (o["kp"], o["vp"], n_pages, i32(src_slot) if cached else None, i32(dst), mode,
+                 o["alpha"] if cached else None, o["d"] if cached else None, o["ck"] if cached else None)
+        if fused:
+            K.kvb_timing_enable(ctx, "")
+            K.kvb_qkv_fused(ctx, sh(), desc, T_max, i32([n_valid]), i32(rows), hidden, W["norm1"], W["w_qkv"],
+                            i32(pos), o["q"], o["k"], o["v"], *blend, ws, wsb, flags)
+            o["launched"] = K.kvb_timing_read(ctx)
+            K.kvb_timing_enable(ctx, None)
+        else:
+            K.kvb_qkv_proj(ctx, sh(), desc, T_max, i32([n_valid]), i32(rows), hidden, W["norm1"], W["w_qkv"],
+                           i32(pos), o["q"], o["k"], o["v"], ws, wsb, flags)
+            K.kvb_blend_scatter(ctx, sh(), desc, T_max, i32([n_valid]), i32(rows), o["k"], o["v"], *blend)
+        torch.cuda.synchronize()
+        return o
+
+    ref, got = run(False), run(True)
+    assert "rope_fuse" in got["launched"] and "rope" not in got["launched"] and "blend_scatter" not in got["launched"]
+    for key in ("q", "k", "v", "kp", "vp", "alpha", "d", "ck"):
+        assert torch.equal(got[key], ref[key]), key
+    q, k, v, kp, vp, alpha, d_out, ck = (got[x] for x in ("q", "k", "v", "kp", "vp", "alpha", "d", "ck"))
+    n = n_valid
+    Wn = {kk: np64(vv) for kk, vv in W.items()}
+    rq, rk, rv = OM.qkv(np64(hidden)[rows[:n]], pos[rows[:n]], Wn, s)
+    tol = TOL[s.dtype]
+    assert max_rel_err(q[:n], rq) < tol and max_rel_err(k[:n], rk) < tol and max_rel_err(v[:n], rv) < tol
+    assert torch.all(q[n:] == 7.0) and torch.all(k[n:] == 7.0) and torch.all(v[n:] == 7.0)
+    kr, vr = np64(k)[:n], np64(v)[:n]                 # the call's own recomputed rows
+    reuse_k = _rows_at(kp0, src_slot[rows[:n]], s)
+    reuse_v = _rows_at(vp0, src_slot[rows[:n]], s)
+    ok = dst[:n] >= 0
+    if cached:
+        d_ref = OS.deviation(kr, reuse_k)
+        a_new = OS.alpha_of(d_ref, OS.row_sq(reuse_k))
+        a_use = {K.KVB_ALPHA_LAG: alpha0[rows[:n]].astype(np.float64), K.KVB_ALPHA_CURRENT: a_new,
+                 K.KVB_ALPHA_ONE: np.ones(n)}[mode]
+        kb = OM.store(OS.blend(a_use, kr, reuse_k), s.dtype)
+        vb = OM.store(OS.blend(a_use, vr, reuse_v), s.dtype)
+        assert np.allclose(np64(d_out)[:n], d_ref, rtol=2e-5, atol=1e-6) and np.all(np64(d_out)[n:] == -1.0)
+        assert np.allclose(np64(ck)[:n], OS.cksim(kr, reuse_k), atol=2e-5)
+        a_got = np64(alpha)
+        if mode == K.KVB_ALPHA_ONE:
+            assert np.array_equal(a_got, alpha0.astype(np.float64))
+        else:
+            assert np.allclose(a_got[rows[:n]], a_new, rtol=2e-5, atol=1e-7)
+        if mode == K.KVB_ALPHA_LAG:    # alpha = 1: the recomputed row itself
+            assert np.array_equal(_rows_at(kp, dst[:1], s), kr[:1])
+    else:
+        kb, vb = kr, vr
+    assert max_rel_err(_rows_at(kp, dst[:n][ok], s), kb[ok]) < tol
+    assert max_rel_err(_rows_at(vp, dst[:n][ok], s), vb[ok]) < tol
+    if mode == K.KVB_ALPHA_ONE:
+        assert np.array_equal(_rows_at(kp, dst[:n][ok], s), kr[ok])
+    # nothing else in the pools moved
+    touched = np.zeros(n_pages * 16, bool)
+    touched[dst[:n][ok]] = True
+    untouched = np.flatnonzero(~touched)
+    assert np.array_equal(_rows_at(kp, untouched, s), _rows_at(kp0, untouched, s))
+    assert np.array_equal(_rows_at(vp, untouched, s), _rows_at(vp0, untouched, s))
+
+
+def test_qkv_fused_rows_are_batch_invariant(ctx):
+    """With KVB_QKV_BATCH_INVARIANT a row's rotated q/k/v and its scattered K/V
+    are bitwise the same whatever batch it sits in."""
+    s = SHAPES["bf16"]
+    g = np.random.default_rng(8)
+    desc = K.model_desc(s)
+    n_tok, n_pages = 400, 64
+    hidden = rand((n_tok, s.d_model), g, dtype=torch.bfloat16).to(DEV)
+    W = weights(s, g)
+    pos = i32(g.integers(0, 5000, n_tok))
+    outs = []
+    for rows in (np.arange(0, 150), np.concatenate([np.arange(250, 400), np.arange(0, 150)])):
+        T = len(rows)
+        q = torch.empty((T, s.n_q_heads, s.head_dim), dtype=torch.bfloat16, device=DEV)
+        k = torch.empty((T, s.n_kv_heads, s.head_dim), dtype=torch.bfloat16, device=DEV)
+        v = torch.empty_like(k)
+        kp = torch.zeros((n_pages, s.n_kv_heads, 16, s.head_dim), dtype=torch.bfloat16, device=DEV)
+        vp = torch.zeros_like(kp)
+        ws, wsb = workspace(ctx, desc, T, n_tok)
+        K.kvb_qkv_fused(ctx, sh(), desc, T, None, i32(rows), hidden, W["norm1"], W["w_qkv"], pos, q, k, v, kp, vp,
+                        n_pages, None, i32(rows), K.KVB_ALPHA_ONE, None, None, None, ws, wsb)
+        outs.append((q, k, v, kp, vp))
+    torch.cuda.synchronize()
+    for a, b in zip(outs[0][:3], outs[1][:3]):
+        assert torch.equal(a[:150], b[150:300])
+    for a, b in zip(outs[0][3:], outs[1][3:]):   # the slots of tokens 0..149 (the second batch also wrote others)
+        assert np.array_equal(_rows_at(a, np.arange(150), s), _rows_at(b, np.arange(150), s))
+
+
 def test_blend_scatter_without_cache(ctx):
     s = SHAPES["bf16"]
     g = np.random.default_rng(2)
