@@ -15,7 +15,8 @@
 //   * V stays row-major in LDS; V^T operands come from the transposing LDS
 //     read of gfx950;
 //   * only tiles that cross a query's causal edge or its lower bound, or that
-//     hold a key without a valid slot, are masked; blocks run longest first;
+//     hold a key without a valid slot, are masked; blocks run longest first,
+//     each XCD taking whole KV heads so its L2 holds the K/V its blocks share;
 //   * split-KV: with few query blocks the key range of each block is cut into
 //     n_split parts whose partial (O, offset, sum) a merge kernel combines.
 // fp32 path: one wave per (row, query head), plain online softmax.
@@ -134,8 +135,30 @@ attn_bf16_kernel(AttnArgs a) {
   const int G = a.Hq / a.Hkv;
   const int TB = AQ / G;  // tokens per block
   const int M = row_count(a.n_rows, a.T_max);
-  const int qb = a.n_qblocks - 1 - (int)blockIdx.x;  // longest first
-  const int h = blockIdx.y, split = blockIdx.z;
+  // Workgroups go to the 8 XCDs round-robin by id, each XCD with its own L2
+  // (4 MiB, about the K/V of one head over 8K tokens): give every XCD whole KV
+  // heads (or every head a fixed set of XCDs), so the K/V rows a block streams
+  // are the ones the other blocks on its XCD stream too.
+  int h, item;
+  {
+    const int L = blockIdx.x, xcd = L & 7, i = L >> 3;
+    const int per_head = a.n_qblocks * a.n_split;
+    if (a.Hkv % 8 == 0) {
+      const int hp = a.Hkv / 8;
+      h = xcd * hp + i % hp;
+      item = i / hp;
+    } else if (8 % a.Hkv == 0) {
+      const int xp = 8 / a.Hkv;
+      h = xcd / xp;
+      item = i * xp + xcd % xp;
+    } else {
+      h = L / per_head;
+      item = L % per_head;
+    }
+    if (h >= a.Hkv || item >= per_head) return;
+  }
+  const int qb = a.n_qblocks - 1 - item / a.n_split;  // longest first
+  const int split = item % a.n_split;
   const int r0 = qb * TB;
   if (r0 >= M) return;
   const int t = threadIdx.x, lane = t & 63;
@@ -595,7 +618,12 @@ extern "C" kvb_status kvb_sparse_query_attn(kvb_ctx* ctx, void* stream, const kv
       a.part_o = (float*)ws;
       a.part_ml = (float*)((char*)ws + part);
     }
-    dim3 grid(a.n_qblocks, Hkv, n_split);
+    // one block per (query block, KV head, split) item, in the XCD order the kernel decodes
+    const long per_head = (long)a.n_qblocks * n_split;
+    long blocks = per_head * Hkv;
+    if (Hkv % 8 != 0 && 8 % Hkv == 0) blocks = 8L * ((per_head + 8 / Hkv - 1) / (8 / Hkv));
+    if (blocks > 0x7fffffffL) return fail(KVB_ERR_UNSUPPORTED, "attention grid too large");
+    const dim3 grid((unsigned)blocks);
     {
       LaunchTimer lt(st, "attention");
       if (hd == 128) attn_bf16_kernel<128><<<grid, ATHREADS, 0, st>>>(a);
