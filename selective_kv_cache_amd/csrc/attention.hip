@@ -452,7 +452,213 @@ attn_bf16_kernel(AttnArgs a) {
   }
 }
 
-// merge of split-KV partials: one wave per (row, head); base-2 exponents
+__device__ __forceinline__ void unpack8_bf16(const uint4& a, float (&f)[8]) {
+  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+// ------------------------------------------------------------ few query rows
+// One block per (row, KV head, key split), RW waves, each wave taking whole
+// 64-key tiles of the split in turn; every query head of the GQA group rides
+// along.  For a handful of rows (decode: one token per request) this reads
+// each row's K/V once instead of running 256-row query blocks that are almost
+// empty.  Per 64-key tile:
+//   S^T = K Q^T    v_mfma_f32_16x16x32_bf16 on four 16-key subtiles, K rows
+//                  loaded straight from the pool (lane l: key l % 16, dims
+//                  8 (l / 16) + 32 ks .. + 7); query column c = head c of the
+//                  group (columns >= G are zero);
+//   softmax        per head, base 2, exact running maximum; probabilities go
+//                  to the wave's LDS scratch, one row of 16 columns per key;
+//   O += P V       on the vector units: lane l owns dims 8 (l % LPK) .. + 7 of
+//                  every head for keys KPI i + l / LPK, V rows loaded straight
+//                  from the pool; at the end the key groups are summed.
+// The waves' (offset, sum, O) are combined in LDS and written as one split's
+// partial (or, with one split, normalised to the output).
+constexpr int RW = 4;  // waves per block
+constexpr int ROWS_SPLIT_MAX = 32;
+
+template <int HD, int G>
+__global__ void __launch_bounds__(64 * RW) attn_rows_kernel(AttnArgs a) {
+  static_assert(G >= 1 && G <= 16, "group fits the 16 query columns");
+  constexpr int KS = HD / 32;    // k32 steps over the head dim
+  constexpr int LPK = HD / 8;    // lanes per key row in the V layout
+  constexpr int KPI = 64 / LPK;  // keys per V load instruction
+  constexpr int NI = 64 / KPI;   // V loads per 64-key tile
+  __shared__ float s_p[RW][64][16];       // probabilities of the wave's tile: [key][query column]
+  __shared__ float s_corr[RW][16];        // the tile's rescale factor per head
+  __shared__ float s_o[RW][G][HD];        // per-wave results, combined at the end
+  __shared__ float s_ml[RW][G][2];
+
+  const int L = blockIdx.x;
+  const int split = L % a.n_split, h = (L / a.n_split) % a.Hkv, r = L / (a.n_split * a.Hkv);
+  const int M = row_count(a.n_rows, a.T_max);
+  if (r >= M) return;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int qc = lane & 15, kq = lane >> 4;     // S layout: query column, key quarter
+  const int vj = lane % LPK, vg = lane / LPK;   // V layout: dim chunk, key group
+
+  const int g = a.row_tok ? a.row_tok[r] : r;  // the row's token: keys tok_lo[g] .. g
+  const int lo = a.tok_lo[g];
+  const int ntiles = (g - lo) / 64 + 1;
+  const int tb = (int)((long)ntiles * split / a.n_split), te = (int)((long)ntiles * (split + 1) / a.n_split);
+
+  bf16x8_t qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ks++) {
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (qc < G) v = *reinterpret_cast<const uint4*>(a.q + ((size_t)r * a.Hq + h * G + qc) * HD + 32 * ks + 8 * kq);
+    qf[ks] = __builtin_bit_cast(bf16x8_t, v);
+  }
+
+  float m_run = -INFINITY;  // running offset (base 2) of head qc, same in the 4 lanes of a column
+  float l_run = 0.f;        // this lane's share of head qc's sum
+  float oacc[G][8];
+#pragma unroll
+  for (int c = 0; c < G; c++)
+#pragma unroll
+    for (int e = 0; e < 8; e++) oacc[c][e] = 0.f;
+
+  for (int T = tb + wave; T < te; T += RW) {
+    const int k0 = lo + T * 64;
+    // slot of key k0 + lane; keys past the row's token or without a valid slot are masked
+    const int key = k0 + lane;
+    int slot = key <= g ? a.slot_map[key] : -1;
+    const bool ok = (unsigned)slot < (unsigned)a.n_slots;
+    const uint64_t valid = __ballot(ok);
+    slot = ok ? slot : 0;
+    auto prow = [&](int sl) {
+      return (size_t)((uint32_t)(sl >> 4) * (uint32_t)(a.Hkv * 16) + (uint32_t)(h * 16 + (sl & 15))) * HD;
+    };
+    // K fragments of the four 16-key subtiles, V rows of the lane's keys
+    uint4 kr[4][KS], vr[NI];
+#pragma unroll
+    for (int qq = 0; qq < 4; qq++) {
+      const size_t base = prow(__shfl(slot, 16 * qq + qc, 64)) + 8 * kq;
+#pragma unroll
+      for (int ks = 0; ks < KS; ks++) kr[qq][ks] = *reinterpret_cast<const uint4*>(a.k_pool + base + 32 * ks);
+    }
+#pragma unroll
+    for (int i = 0; i < NI; i++)
+      vr[i] = *reinterpret_cast<const uint4*>(a.v_pool + prow(__shfl(slot, KPI * i + vg, 64)) + 8 * vj);
+
+    // scores: sacc[qq][e] = S[key 16 qq + 4 kq + e][column qc]
+    f32x4_t sacc[4];
+#pragma unroll
+    for (int qq = 0; qq < 4; qq++) {
+      sacc[qq] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ks++)
+        sacc[qq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[qq][ks]), qf[ks],
+                                                            sacc[qq], 0, 0, 0);
+    }
+    float sv[16];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int qq = 0; qq < 4; qq++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int kk = 16 * qq + 4 * kq + e;
+        const bool in = (valid >> kk) & 1u;
+        sv[4 * qq + e] = in ? sacc[qq][e] * a.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, sv[4 * qq + e]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float corr = m_run == -INFINITY ? (m_new == -INFINITY ? 1.f : 0.f) : exp2f(m_run - m_new);
+    m_run = m_new;
+    const float sub = m_new == -INFINITY ? 0.f : m_new;
+    float ls = 0.f;
+#pragma unroll
+    for (int qq = 0; qq < 4; qq++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const float p = exp2f(sv[4 * qq + e] - sub);  // exp2(-inf) = 0 for masked keys
+        ls += p;
+        s_p[wave][16 * qq + 4 * kq + e][qc] = p;
+      }
+    l_run = l_run * corr + ls;
+    if (kq == 0) s_corr[wave][qc] = corr;
+    // (the wave's own LDS writes are read back in order: no barrier needed)
+    float cf[G];
+#pragma unroll
+    for (int c = 0; c < G; c++) cf[c] = s_corr[wave][c];
+#pragma unroll
+    for (int c = 0; c < G; c++)
+#pragma unroll
+      for (int e = 0; e < 8; e++) oacc[c][e] *= cf[c];
+#pragma unroll
+    for (int i = 0; i < NI; i++) {
+      float v8[8];
+      unpack8_bf16(vr[i], v8);
+      const float* pk = &s_p[wave][KPI * i + vg][0];
+#pragma unroll
+      for (int c = 0; c < G; c++) {
+        const float p = pk[c];
+#pragma unroll
+        for (int e = 0; e < 8; e++) oacc[c][e] = fmaf(p, v8[e], oacc[c][e]);
+      }
+    }
+  }
+
+  // sum the key groups: lanes with the same dim chunk
+#pragma unroll
+  for (int off = LPK; off < 64; off <<= 1)
+#pragma unroll
+    for (int c = 0; c < G; c++)
+#pragma unroll
+      for (int e = 0; e < 8; e++) oacc[c][e] += __shfl_xor(oacc[c][e], off, 64);
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (lane < LPK) {
+#pragma unroll
+    for (int c = 0; c < G; c++)
+#pragma unroll
+      for (int e = 0; e < 8; e++) s_o[wave][c][8 * vj + e] = oacc[c][e];
+  }
+  if (lane < G) {
+    s_ml[wave][lane][0] = m_run;
+    s_ml[wave][lane][1] = l_run;
+  }
+  __syncthreads();
+  // combine the waves: thread (c, d) for head c, dim d
+  for (int idx = t; idx < G * HD; idx += 64 * RW) {
+    const int c = idx / HD, d = idx % HD;
+    float mb = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < RW; w++) mb = fmaxf(mb, s_ml[w][c][0]);
+    float lsum = 0.f, osum = 0.f;
+#pragma unroll
+    for (int w = 0; w < RW; w++) {
+      const float mw = s_ml[w][c][0];
+      const float f = mw == -INFINITY ? 0.f : exp2f(mw - mb);
+      lsum += f * s_ml[w][c][1];
+      osum += f * s_o[w][c][d];
+    }
+    const int hq = h * G + c;
+    if (a.n_split == 1) {
+      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+      a.o[((size_t)r * a.Hq + hq) * HD + d] = (bf16_t)(pack2_bf16(osum * inv, 0.f) & 0xffffu);
+    } else {
+      const size_t row = ((size_t)split * a.T_max + r) * a.Hq + hq;
+      a.part_o[row * HD + d] = osum;
+      if (d == 0) {
+        a.part_ml[row * 2 + 0] = mb;
+        a.part_ml[row * 2 + 1] = lsum;
+      }
+    }
+  }
+}
+
+// merge of split-KV partials: one wave per (row, head); base-2 exponents.
+// Lane s reads split s's (offset, sum) once; the weighted sums then run over
+// the splits in order with each weight broadcast from its lane, so the loads
+// of different splits are independent (no chain of dependent loads per split).
 template <int HD>
 __global__ void __launch_bounds__(256) attn_merge_kernel(int T_max, const int32_t* __restrict__ n_rows, int Hq,
                                                          int n_split, const float* __restrict__ part_o,
@@ -460,22 +666,76 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(int T_max, const int32_
   const int w = (blockIdx.x * blockDim.x + threadIdx.x) >> 6, lane = threadIdx.x & 63;
   const int M = row_count(n_rows, T_max);
   if (w >= M * Hq) return;
+  const size_t stride = (size_t)T_max * Hq;  // rows of one split
   float mx = -INFINITY;
-  for (int s = 0; s < n_split; s++) mx = fmaxf(mx, part_ml[((size_t)s * T_max * Hq + w) * 2]);
-  float l = 0.f;
   float acc[HD / 64] = {};
-  for (int s = 0; s < n_split; s++) {
-    const size_t row = (size_t)s * T_max * Hq + w;
-    const float ms = part_ml[row * 2], ls = part_ml[row * 2 + 1];
-    const float f = (ms == -INFINITY) ? 0.f : exp2f(ms - mx);
-    l += ls * f;
+  float l = 0.f;
+  for (int s0 = 0; s0 < n_split; s0 += 64) {
+    const int s = s0 + lane;
+    const float ms = s < n_split ? part_ml[(s * stride + w) * 2] : -INFINITY;
+    mx = fmaxf(mx, ms);
+  }
 #pragma unroll
-    for (int e = 0; e < HD / 64; e++) acc[e] += f * part_o[row * HD + lane + 64 * e];
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  for (int s0 = 0; s0 < n_split; s0 += 64) {
+    const int sl = s0 + lane;
+    float f = 0.f, ls = 0.f;
+    if (sl < n_split) {
+      const float ms = part_ml[(sl * stride + w) * 2];
+      ls = part_ml[(sl * stride + w) * 2 + 1];
+      f = (ms == -INFINITY) ? 0.f : exp2f(ms - mx);
+    }
+    const int ns = min(64, n_split - s0);
+#pragma unroll 8
+    for (int j = 0; j < ns; j++) {
+      const float fj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), j));
+      const float lj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ls), j));
+      const size_t row = (size_t)(s0 + j) * stride + w;
+      l += lj * fj;
+#pragma unroll
+      for (int e = 0; e < HD / 64; e++) acc[e] += fj * part_o[row * HD + lane + 64 * e];
+    }
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
   for (int e = 0; e < HD / 64; e++)
     o[(size_t)w * HD + lane + 64 * e] = (bf16_t)(pack2_bf16(acc[e] * inv, 0.f) & 0xffffu);
+}
+
+// The same merge with one 256-thread block per (row, head), for many splits
+// and few rows: every split's partial is loaded at once (one memory round
+// trip, staged in LDS), then thread d runs the merge of dim d with the
+// arithmetic and order of attn_merge_kernel, so the output is bitwise the same.
+constexpr int MERGE_WIDE_MAX = 64;
+template <int HD>
+__global__ void __launch_bounds__(256) attn_merge_wide_kernel(int T_max, const int32_t* __restrict__ n_rows, int Hq,
+                                                              int n_split, const float* __restrict__ part_o,
+                                                              const float* __restrict__ part_ml,
+                                                              bf16_t* __restrict__ o) {
+  __shared__ float s_o[MERGE_WIDE_MAX][HD];
+  __shared__ float s_ml[MERGE_WIDE_MAX][2];
+  const int w = blockIdx.x, t = threadIdx.x;  // w: (row, head)
+  const int M = row_count(n_rows, T_max);
+  if (w >= M * Hq) return;
+  const size_t stride = (size_t)T_max * Hq;
+  for (int i = t; i < n_split * 2; i += 256) s_ml[i >> 1][i & 1] = part_ml[((i >> 1) * stride + w) * 2 + (i & 1)];
+  for (int i = t; i < n_split * (HD / 4); i += 256) {
+    const int sp = i / (HD / 4), c = i % (HD / 4);
+    *reinterpret_cast<float4*>(&s_o[sp][4 * c]) = *reinterpret_cast<const float4*>(part_o + (sp * stride + w) * HD + 4 * c);
+  }
+  __syncthreads();
+  if (t >= HD) return;
+  float mx = -INFINITY;
+  for (int sp = 0; sp < n_split; sp++) mx = fmaxf(mx, s_ml[sp][0]);
+  float l = 0.f, acc = 0.f;
+  for (int sp = 0; sp < n_split; sp++) {
+    const float ms = s_ml[sp][0], ls = s_ml[sp][1];
+    const float f = (ms == -INFINITY) ? 0.f : exp2f(ms - mx);
+    l += ls * f;
+    acc += f * s_o[sp][t];
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  o[(size_t)w * HD + t] = (bf16_t)(pack2_bf16(acc * inv, 0.f) & 0xffffu);
 }
 
 // ------------------------------------------------------------------ fp32 kernel
@@ -540,7 +800,21 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(int T_max, const int32_t* 
 
 // Split count of a bf16 launch: enough (query block, head, split) items to
 // fill the chip about twice, at most 16.
+// rows up to this count use the few-rows kernel (bf16, group of 1..16 heads)
+constexpr int ROWS_MAX = 4;
+static bool rows_kernel_ok(const kvb_model_desc* d, int T_max) {
+  const int G = d->n_q_heads / d->n_kv_heads;
+  return T_max <= ROWS_MAX && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16) &&
+         (d->head_dim == 64 || d->head_dim == 128);
+}
+
 int attn_splits(const kvb_model_desc* d, int T_max, int n_cu) {
+  if (rows_kernel_ok(d, T_max)) {
+    // every (row, KV head, split) block 4 waves; about two blocks per CU
+    const long items = (long)T_max * d->n_kv_heads;
+    const long s = (2L * n_cu + items - 1) / items;
+    return (int)(s < 1 ? 1 : (s > ROWS_SPLIT_MAX ? ROWS_SPLIT_MAX : s));
+  }
   const int G = d->n_q_heads / d->n_kv_heads;
   const long items = (long)cdiv(T_max, AQ / G) * d->n_kv_heads;
   const long s = (2L * n_cu + items - 1) / items;
@@ -552,6 +826,7 @@ size_t ws_attn_bytes(const kvb_model_desc* d, int32_t max_rows, int n_cu) {
   // largest n_split * T over T <= max_rows (n_split shrinks as T grows)
   size_t best = 0;
   const int G = d->n_q_heads / d->n_kv_heads, TB = AQ / G;
+  for (int T = 1; T <= ROWS_MAX && T <= max_rows; T++) best = std::max(best, (size_t)attn_splits(d, T, n_cu) * T);
   for (int qb = 1; qb <= cdiv(max_rows, TB); qb++) {
     const int T = qb * TB < max_rows ? qb * TB : max_rows;
     const int s = attn_splits(d, T, n_cu);
@@ -560,6 +835,22 @@ size_t ws_attn_bytes(const kvb_model_desc* d, int32_t max_rows, int n_cu) {
   }
   if (best == 0) return 0;
   return align_up(best * d->n_q_heads * d->head_dim * 4, 256) + align_up(best * d->n_q_heads * 2 * 4, 256);
+}
+
+static kvb_status launch_merge(hipStream_t st, int hd, int T_max, const int32_t* n_rows, int Hq, int n_split,
+                               const float* part_o, const float* part_ml, bf16_t* o) {
+  {
+    LaunchTimer lt(st, "attention_merge");
+    const int waves = T_max * Hq;
+    if (n_split >= 8 && n_split <= MERGE_WIDE_MAX && waves <= 4096) {
+      if (hd == 128) attn_merge_wide_kernel<128><<<waves, 256, 0, st>>>(T_max, n_rows, Hq, n_split, part_o, part_ml, o);
+      else attn_merge_wide_kernel<64><<<waves, 256, 0, st>>>(T_max, n_rows, Hq, n_split, part_o, part_ml, o);
+    } else if (hd == 128)
+      attn_merge_kernel<128><<<cdiv(waves, 4), 256, 0, st>>>(T_max, n_rows, Hq, n_split, part_o, part_ml, o);
+    else
+      attn_merge_kernel<64><<<cdiv(waves, 4), 256, 0, st>>>(T_max, n_rows, Hq, n_split, part_o, part_ml, o);
+  }
+  return check_launch("attn_merge_kernel");
 }
 
 }  // namespace kvb
@@ -618,6 +909,33 @@ extern "C" kvb_status kvb_sparse_query_attn(kvb_ctx* ctx, void* stream, const kv
       a.part_o = (float*)ws;
       a.part_ml = (float*)((char*)ws + part);
     }
+    if (rows_kernel_ok(desc, T_max)) {
+      // a handful of rows: one block per (row, KV head, split)
+      const dim3 rgrid((unsigned)((long)T_max * Hkv * n_split));
+      {
+        LaunchTimer lt(st, "attention");
+        if (hd == 128) {
+          switch (G) {
+            case 1: attn_rows_kernel<128, 1><<<rgrid, 64 * RW, 0, st>>>(a); break;
+            case 2: attn_rows_kernel<128, 2><<<rgrid, 64 * RW, 0, st>>>(a); break;
+            case 4: attn_rows_kernel<128, 4><<<rgrid, 64 * RW, 0, st>>>(a); break;
+            case 8: attn_rows_kernel<128, 8><<<rgrid, 64 * RW, 0, st>>>(a); break;
+            default: attn_rows_kernel<128, 16><<<rgrid, 64 * RW, 0, st>>>(a); break;
+          }
+        } else {
+          switch (G) {
+            case 1: attn_rows_kernel<64, 1><<<rgrid, 64 * RW, 0, st>>>(a); break;
+            case 2: attn_rows_kernel<64, 2><<<rgrid, 64 * RW, 0, st>>>(a); break;
+            case 4: attn_rows_kernel<64, 4><<<rgrid, 64 * RW, 0, st>>>(a); break;
+            case 8: attn_rows_kernel<64, 8><<<rgrid, 64 * RW, 0, st>>>(a); break;
+            default: attn_rows_kernel<64, 16><<<rgrid, 64 * RW, 0, st>>>(a); break;
+          }
+        }
+      }
+      KVB_TRY(check_launch("attn_rows_kernel"));
+      if (n_split > 1) KVB_TRY(launch_merge(st, hd, T_max, n_rows, Hq, n_split, a.part_o, a.part_ml, (bf16_t*)o));
+      return KVB_OK;
+    }
     // one block per (query block, KV head, split) item, in the XCD order the kernel decodes
     const long per_head = (long)a.n_qblocks * n_split;
     long blocks = per_head * Hkv;
@@ -630,17 +948,7 @@ extern "C" kvb_status kvb_sparse_query_attn(kvb_ctx* ctx, void* stream, const kv
       else attn_bf16_kernel<64><<<grid, ATHREADS, 0, st>>>(a);
     }
     KVB_TRY(check_launch("attn_bf16_kernel"));
-    if (n_split > 1) {
-      LaunchTimer lt(st, "attention_merge");
-      const int waves = T_max * Hq;
-      if (hd == 128)
-        attn_merge_kernel<128><<<cdiv(waves, 4), 256, 0, st>>>(T_max, n_rows, Hq, n_split, a.part_o, a.part_ml,
-                                                                (bf16_t*)o);
-      else
-        attn_merge_kernel<64><<<cdiv(waves, 4), 256, 0, st>>>(T_max, n_rows, Hq, n_split, a.part_o, a.part_ml,
-                                                               (bf16_t*)o);
-      KVB_TRY(check_launch("attn_merge_kernel"));
-    }
+    if (n_split > 1) KVB_TRY(launch_merge(st, hd, T_max, n_rows, Hq, n_split, a.part_o, a.part_ml, (bf16_t*)o));
     return KVB_OK;
   }
   LaunchTimer lt(st, "attention");

@@ -414,6 +414,59 @@ def test_sparse_query_attention(ctx, name, req_lens, n_sel, split):
     assert torch.all(o[n_valid:] == 3.0)
 
 
+FEW_SHAPES = {
+    "bf16": SHAPES["bf16"],                      # group of 4, head dim 128
+    "bf16_hd64": SHAPES["bf16_hd64"],            # group of 8, head dim 64
+    "bf16_g1": wl.ModelShape(n_layers=1, d_model=512, n_q_heads=4, n_kv_heads=4, head_dim=128, ffn=512,
+                             dtype="bf16"),
+    "bf16_g16": wl.ModelShape(n_layers=1, d_model=2048, n_q_heads=16, n_kv_heads=1, head_dim=128, ffn=512,
+                              dtype="bf16"),
+}
+
+
+@pytest.mark.parametrize("name", list(FEW_SHAPES))
+@pytest.mark.parametrize("req_lens,rows_at,T_max", [
+    ([2500], [2499], 1),                   # one decode-like row over a long prompt
+    ([2500], [1300], 2),                   # one valid row of two (the padding row stays untouched)
+    ([300, 517, 64], [299, 816, 880], 3),  # one row per request, each at its request's end
+    ([700], [0, 63, 64, 699], 4),          # rows at tile edges, including the first token
+])
+@pytest.mark.parametrize("split", [False, True], ids=["unsplit", "split"])
+def test_few_rows_attention(ctx, name, req_lens, rows_at, T_max, split):
+    """A handful of query rows (decode) runs the per-row kernel: one block per
+    (row, KV head, key split); with workspace its splits go through the merge."""
+    s = FEW_SHAPES[name]
+    g = np.random.default_rng(sum(req_lens) + T_max + 17 * len(name))
+    desc = K.model_desc(s)
+    dt = tdt(s)
+    n_tok = sum(req_lens)
+    cu = np.concatenate([[0], np.cumsum(req_lens)])
+    lo = np.concatenate([np.full(n, cu[b]) for b, n in enumerate(req_lens)])
+    n_pages = (n_tok + 15) // 16 + 5
+    slot_map = g.permutation(n_pages * 16)[:n_tok]
+    rows = np.array(rows_at, dtype=np.int64)
+    n_valid = len(rows)
+    rows_dev = np.concatenate([rows, np.zeros(T_max - n_valid, dtype=rows.dtype)])
+    kp, vp = _pool(s, n_pages, g)
+    q = rand((T_max, s.n_q_heads, s.head_dim), g, 1.5, dtype=dt).to(DEV)
+    o = torch.full((T_max, s.q_dim), 3.0, dtype=dt, device=DEV)
+    ws, wsb = workspace(ctx, desc, T_max, n_tok) if split else (None, 0)
+    if split:
+        ws.fill_(0xFF)
+    K.kvb_timing_enable(ctx, "attention")
+    K.kvb_sparse_query_attn(ctx, sh(), desc, T_max, i32([n_valid]), i32(rows_dev), i32(lo), q, kp, vp, n_pages,
+                            i32(slot_map), 1.0 / np.sqrt(s.head_dim), o, ws, wsb)
+    t = K.kvb_timing_read(ctx)
+    K.kvb_timing_enable(ctx, None)
+    assert t["attention"]["count"] == 1
+    assert t.get("attention_merge", {}).get("count", 0) == (1 if split else 0)
+    torch.cuda.synchronize()
+    Klog, Vlog = _rows_at(kp, slot_map, s), _rows_at(vp, slot_map, s)
+    ref = OM.attention_rows(np64(q)[:n_valid], rows, Klog, Vlog, lo[rows], s)
+    assert max_rel_err(o[:n_valid], ref) < TOL[s.dtype]
+    assert torch.all(o[n_valid:] == 3.0)
+
+
 # ------------------------------------------------------------------ CacheBlend-style attention-map deviation
 
 AMAP_SHAPES = {
