@@ -602,6 +602,35 @@ gemv_bf16_kernel(GemmArgs<bf16_t> p) {
   if (row_count(p.n_rows, p.M_max) < 1) return;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int C = p.K / 8;  // 16-byte chunks per row
+  const int nb = (blockIdx.x * GV_WAVES + wave) * GV_NW;
+  constexpr int R = DUAL ? 2 * GV_NW : GV_NW;  // rows i < GV_NW: B; the rest: B2
+  const uint4* wr[R];
+#pragma unroll
+  for (int i = 0; i < GV_NW; i++) {
+    int n = nb + i < p.N ? nb + i : p.N - 1;
+    n = n < 0 ? 0 : n;
+    wr[i] = reinterpret_cast<const uint4*>(p.B + (size_t)n * p.K);
+    if (DUAL) wr[GV_NW + i] = reinterpret_cast<const uint4*>(p.B2 + (size_t)n * p.K);
+  }
+  // whole batches of 4 chunks per lane: all 4 R weight loads issued before
+  // any is used; then single chunks.  Streamed once: non-temporal, so the
+  // weights do not evict what the neighbouring launches keep in L2.
+  auto load_batch = [&](int c, uint4 (&w)[4][R]) {
+#pragma unroll
+    for (int u = 0; u < 4; u++)
+#pragma unroll
+      for (int i = 0; i < R; i++) {
+        const u32x4_t q = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(&wr[i][c + 64 * u]));
+        w[u][i] = make_uint4(q.x, q.y, q.z, q.w);
+      }
+  };
+  // the first batch is issued before x is staged: the weight stream does not
+  // wait for the staging and its barrier
+  const bool active = nb < p.N;
+  const bool first = active && lane + 192 < C;
+  uint4 w0[4][R];
+  if (first) load_batch(lane, w0);
+
   const uint4* xg = reinterpret_cast<const uint4*>(p.A);
   uint4* xs = reinterpret_cast<uint4*>(gv_x);
   {
@@ -609,49 +638,37 @@ gemv_bf16_kernel(GemmArgs<bf16_t> p) {
     constexpr int TH = 64 * GV_WAVES;
     int c = t;
     for (; c + 3 * TH < C; c += 4 * TH) {
-      uint4 v[4];
-#pragma unroll
-      for (int u = 0; u < 4; u++) v[u] = xg[c + u * TH];
-#pragma unroll
-      for (int u = 0; u < 4; u++) xs[c + u * TH] = v[u];
+      const uint4 v0 = xg[c], v1 = xg[c + TH], v2 = xg[c + 2 * TH], v3 = xg[c + 3 * TH];
+      xs[c] = v0;
+      xs[c + TH] = v1;
+      xs[c + 2 * TH] = v2;
+      xs[c + 3 * TH] = v3;
     }
     for (; c < C; c += TH) xs[c] = xg[c];
   }
   __syncthreads();
-  const int nb = (blockIdx.x * GV_WAVES + wave) * GV_NW;
-  if (nb >= p.N) return;
-  constexpr int R = DUAL ? 2 * GV_NW : GV_NW;  // rows i < GV_NW: B; the rest: B2
-  const uint4* wr[R];
-#pragma unroll
-  for (int i = 0; i < GV_NW; i++) {
-    const int n = nb + i < p.N ? nb + i : p.N - 1;
-    wr[i] = reinterpret_cast<const uint4*>(p.B + (size_t)n * p.K);
-    if (DUAL) wr[GV_NW + i] = reinterpret_cast<const uint4*>(p.B2 + (size_t)n * p.K);
-  }
+  if (!active) return;
   float acc[R];
 #pragma unroll
   for (int i = 0; i < R; i++) acc[i] = 0.f;
-  // whole batches of 4 chunks per lane: all 4 R weight loads issued before
-  // any is used; then single chunks
-  int c = lane;
-  for (; c + 192 < C; c += 256) {
-    uint4 w[4][R];
-#pragma unroll
-    for (int u = 0; u < 4; u++)
-#pragma unroll
-      for (int i = 0; i < R; i++) {
-        // streamed once: non-temporal, so the weights do not evict what the
-        // neighbouring launches keep in L2
-        const u32x4_t q = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(&wr[i][c + 64 * u]));
-        w[u][i] = make_uint4(q.x, q.y, q.z, q.w);
-      }
-    __builtin_amdgcn_sched_group_barrier(0x020, 4 * R, 0);  // every weight load of the batch first
+  auto use_batch = [&](int c, const uint4 (&w)[4][R]) {
 #pragma unroll
     for (int u = 0; u < 4; u++) {
       const uint4 xv = xs[c + 64 * u];
 #pragma unroll
       for (int i = 0; i < R; i++) acc[i] = dot8_bf16(w[u][i], xv, acc[i]);
     }
+  };
+  int c = lane;
+  if (first) {
+    use_batch(c, w0);
+    c += 256;
+  }
+  for (; c + 192 < C; c += 256) {
+    uint4 w[4][R];
+    load_batch(c, w);
+    __builtin_amdgcn_sched_group_barrier(0x020, 4 * R, 0);  // every weight load of the batch first
+    use_batch(c, w);
   }
   for (; c < C; c += 64) {
     const uint4 xv = xs[c];
