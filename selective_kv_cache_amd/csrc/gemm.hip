@@ -736,8 +736,8 @@ size_t ws_gemm_sk_bytes(int) { return SK_BUDGET; }
 // the rate one block streams them (150 GB/s for the large tiles, whose
 // operands mostly hit L2; 60 GB/s for the 64-row tile, which streams the
 // weights); whole waves of blocks run on the CUs; the launch takes at least
-// its unique operand bytes at 5 TB/s; split-K adds the partials' round trip
-// at 5 TB/s and the reduction launch.
+// its unique operand bytes at 5 TB/s; split-K adds the reduction launch, which
+// reads the partials at 5 TB/s (their writes overlap the product's own work).
 template <int MODE, bool DUAL>
 static kvb_status run_bf16(hipStream_t st, const GemmArgs<bf16_t>& p, const char* name, void* sk_ws = nullptr) {
   if (p.M_max == 0 || p.N == 0) return KVB_OK;
@@ -769,7 +769,7 @@ static kvb_status run_bf16(hipStream_t st, const GemmArgs<bf16_t>& p, const char
       const double kk = (double)p.K / S;
       const double blk_us = std::max(2.0 * sh.bm * sh.bn * kk / (4.5e6 * sh.eff), (sh.bm + sh.bn) * kk * 2.0 / sh.rate);
       double tt = std::max((double)((tiles * S + cus - 1) / cus) * blk_us, hbm_us);
-      if (S > 1) tt += 2.0 * S * p.M_max * cols * 4 / 5e6 + 4.0;
+      if (S > 1) tt += (double)S * p.M_max * cols * 4 / 5e6 + 4.0;
       if (tt < best_t * (S > 1 ? 0.92 : 1.0)) {
         best_t = tt;
         best_shape = si;
