@@ -6,6 +6,8 @@
 // bitwise reproducible from run to run and from batch to batch.
 #include "common.h"
 
+#include <type_traits>
+
 #include <algorithm>
 
 namespace kvb {
@@ -421,6 +423,83 @@ __global__ void deviation_kernel(int n_tok, const T* __restrict__ k_rec, const T
   }
 }
 
+__device__ __forceinline__ void unpack8_bf16(const uint4& a, float (&f)[8]) {
+  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+// The same d and alpha, bitwise (per-vector sums of 8 elements, the butterfly
+// over a head's lanes and the sum over heads in head order, as in row_sums),
+// with one wave per DEV_TPW tokens: every slot, K and cached-K load of the
+// wave's tokens is issued before any is used, so more bytes are in flight
+// than with one block and its LDS reduction per token.  (bf16, Hkv * hd a
+// multiple of 512.)
+constexpr int DEV_TPW = 4;
+template <int VPH, int NV>
+__global__ void __launch_bounds__(256) deviation_wave_kernel(int n_tok, const bf16_t* __restrict__ k_rec,
+                                                             const bf16_t* __restrict__ k_pool, int n_slots,
+                                                             const int32_t* __restrict__ reuse_slot,
+                                                             float* __restrict__ d, float* __restrict__ alpha, int Hkv,
+                                                             int hd) {
+  constexpr int HPV = 64 / VPH;  // heads per 64 vectors
+  const int lane = threadIdx.x & 63;
+  const int g0 = (blockIdx.x * 4 + (int)(threadIdx.x >> 6)) * DEV_TPW;
+  if (g0 >= n_tok) return;
+  int sl = -1;
+  if (lane < DEV_TPW && g0 + lane < n_tok) sl = reuse_slot[g0 + lane];
+  uint4 ar[DEV_TPW][NV], br[DEV_TPW][NV];
+#pragma unroll
+  for (int i = 0; i < DEV_TPW; i++) {
+    const int src = __builtin_amdgcn_readlane(sl, i);
+    const bool in = g0 + i < n_tok;
+    const bool have = in && src >= 0 && src < n_slots;
+#pragma unroll
+    for (int v = 0; v < NV; v++) {
+      const int t = lane + 64 * v, h = t / VPH, e0 = (t % VPH) * 8;
+      ar[i][v] = in ? *reinterpret_cast<const uint4*>(k_rec + (size_t)(g0 + i) * Hkv * hd + t * 8)
+                    : make_uint4(0, 0, 0, 0);
+      br[i][v] = have ? *reinterpret_cast<const uint4*>(k_pool + pool_off(src, h, Hkv, hd) + e0)
+                      : make_uint4(0, 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < DEV_TPW; i++) {
+    if (g0 + i >= n_tok) break;
+    float p0[NV], p1[NV];
+#pragma unroll
+    for (int v = 0; v < NV; v++) {
+      float a[8], b[8];
+      unpack8_bf16(ar[i][v], a);
+      unpack8_bf16(br[i][v], b);
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        const float df = a[e] - b[e];
+        s0 += df * df;
+        s1 += b[e] * b[e];
+      }
+      p0[v] = head_reduce<VPH>(s0);
+      p1[v] = head_reduce<VPH>(s1);
+    }
+    float sd = 0.f, sn = 0.f;
+#pragma unroll
+    for (int v = 0; v < NV; v++)
+#pragma unroll
+      for (int hh = 0; hh < HPV; hh++) {
+        sd += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p0[v]), hh * VPH));
+        sn += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p1[v]), hh * VPH));
+      }
+    if (lane == 0) {
+      d[g0 + i] = sd;
+      alpha[g0 + i] = alpha_rule(sd, sn);
+    }
+  }
+}
+
 template <class T>
 kvb_status launch_deviation(hipStream_t st, int n_tok, const void* k_rec, const void* k_pool, int n_pages,
                             const int32_t* reuse_slot, float* d, float* alpha, int Hkv, int hd) {
@@ -428,6 +507,25 @@ kvb_status launch_deviation(hipStream_t st, int n_tok, const void* k_rec, const 
   const int threads = ((nvec + 63) / 64) * 64;
   if (n_tok == 0) return KVB_OK;
   LaunchTimer lt(st, "deviation");
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    const int nv = nvec / 64;
+    if (nvec % 64 == 0 && (nv == 1 || nv == 2 || nv == 4)) {
+      const dim3 grid(cdiv(n_tok, 4 * DEV_TPW)), block(256);
+      const bf16_t* kr = (const bf16_t*)k_rec;
+      const bf16_t* kp = (const bf16_t*)k_pool;
+      const int ns = n_pages * 16;
+      if (hd == 128) {
+        if (nv == 1) deviation_wave_kernel<16, 1><<<grid, block, 0, st>>>(n_tok, kr, kp, ns, reuse_slot, d, alpha, Hkv, hd);
+        else if (nv == 2) deviation_wave_kernel<16, 2><<<grid, block, 0, st>>>(n_tok, kr, kp, ns, reuse_slot, d, alpha, Hkv, hd);
+        else deviation_wave_kernel<16, 4><<<grid, block, 0, st>>>(n_tok, kr, kp, ns, reuse_slot, d, alpha, Hkv, hd);
+      } else {
+        if (nv == 1) deviation_wave_kernel<8, 1><<<grid, block, 0, st>>>(n_tok, kr, kp, ns, reuse_slot, d, alpha, Hkv, hd);
+        else if (nv == 2) deviation_wave_kernel<8, 2><<<grid, block, 0, st>>>(n_tok, kr, kp, ns, reuse_slot, d, alpha, Hkv, hd);
+        else deviation_wave_kernel<8, 4><<<grid, block, 0, st>>>(n_tok, kr, kp, ns, reuse_slot, d, alpha, Hkv, hd);
+      }
+      return check_launch("deviation_wave_kernel");
+    }
+  }
   if (hd == 128)
     deviation_kernel<T, 16><<<n_tok, threads, 0, st>>>(n_tok, (const T*)k_rec, (const T*)k_pool, n_pages * 16,
                                                         reuse_slot, d, alpha, Hkv, hd);

@@ -593,10 +593,26 @@ def test_mlp(ctx, name, T_max, n_valid):
 
 # ------------------------------------------------------------------ deviation + top-k
 
-@pytest.mark.parametrize("name", ["bf16", "fp32"])
+DEV_SHAPES = {
+    "bf16": SHAPES["bf16"],            # one block per token (K/V row of 256 elements)
+    "fp32": SHAPES["fp32"],
+    "bf16_wide": SHAPES["bf16_wide"],  # 4 KV heads x 128: one wave per 4 tokens, one vector per lane
+    "bf16_kv8": wl.ModelShape(n_layers=1, d_model=4096, n_q_heads=32, n_kv_heads=8, head_dim=128, ffn=512,
+                              dtype="bf16"),  # the Mistral rows: two vectors per lane
+    "bf16_kv8_hd64": wl.ModelShape(n_layers=1, d_model=2048, n_q_heads=32, n_kv_heads=8, head_dim=64, ffn=512,
+                                   dtype="bf16"),
+}
+
+
+@pytest.mark.parametrize("name", list(DEV_SHAPES))
 @pytest.mark.parametrize("req_lens", [[517], [4100, 300, 2049, 64], [2048, 2048]])
-def test_deviation_topk(ctx, name, req_lens):
-    s = SHAPES[name]
+@pytest.mark.parametrize("invalid", [False, True], ids=["slots", "invalid"])
+def test_deviation_topk(ctx, name, req_lens, invalid):
+    """d, alpha vs the oracle; the top-k of the GPU's d bit-exact; a token
+    whose reused slot lies outside the pool is compared with a zero cached key."""
+    if invalid and name != "bf16" and name != "bf16_kv8":
+        pytest.skip("invalid slots: one shape per kernel")
+    s = DEV_SHAPES[name]
     g = np.random.default_rng(sum(req_lens))
     desc = K.model_desc(s)
     dt = tdt(s)
@@ -619,6 +635,12 @@ def test_deviation_topk(ctx, name, req_lens):
                 reuse_slot[cu[b] + c] = reuse_slot[cu[b] + a]
                 k_rec[cu[b] + c] = k_rec[cu[b] + a]
     reuse = _rows_at(kp, reuse_slot, s)
+    if invalid:
+        # three tokens per request without a cached row (negative, or past the pool's end)
+        for b in range(B):
+            for j, bad in [(req_lens[b] // 2, -1), (req_lens[b] - 1, n_pages * 16 + 5), (req_lens[b] // 3, -7)]:
+                reuse_slot[cu[b] + j] = bad
+                reuse[cu[b] + j] = 0.0
     k_rec = k_rec.to(DEV)
     k_cap = [int(np.floor(0.26 * n)) for n in req_lens]
     d = torch.zeros(n_tok, device=DEV)
