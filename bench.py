@@ -55,7 +55,7 @@ def kernel_work(eng, layer_rows, layer_pos, shape):
     d, F, Hq, Hkv, hd = s.d_model, s.ffn, s.n_q_heads, s.n_kv_heads, s.head_dim
     esz = 2 if s.dtype == "bf16" else 4
     w = {k: 0.0 for k in ("gemm_qkv", "gemm_oproj", "gemm_swiglu", "gemm_down", "attention", "blend_scatter",
-                          "deviation", "rope", "embed")}
+                          "deviation", "rope", "rope_fuse", "embed")}
     rows_per_layer = []
     for l, (T, pos_lo) in enumerate(zip(layer_rows, layer_pos), start=1):
         rows_per_layer.append(T)
@@ -66,6 +66,12 @@ def kernel_work(eng, layer_rows, layer_pos, shape):
         w["attention"] += 4.0 * Hq * hd * float(pos_lo)
         w["blend_scatter"] += T * (6.0 * Hkv * hd * esz + 16.0)
         w["rope"] += T * 2.0 * (Hq + Hkv) * hd * esz
+        # RoPE + fusion + scatter in one pass (the step's kernel): Q read and
+        # written, K and V read, K and V written to the new slots; CacheSlide's
+        # layers 2..L also read the cached K and V and alpha, and write d,
+        # alpha and CKSim
+        blend = l >= 2 and eng.cfg.mode == "cacheslide"  # the other modes replace the cached rows
+        w["rope_fuse"] += T * ((2.0 * Hq + 4.0 * Hkv) * hd * esz + ((2.0 * Hkv * hd * esz + 16.0) if blend else 0.0))
     w["deviation"] += eng.N * (2.0 * Hkv * hd * esz + 16.0)
     # the embedding gathers every token's row, except in LegoLink (its static rows only)
     w["embed"] += (eng.T_sel if eng.cfg.mode == "legolink" else eng.N) * 2.0 * d * esz
@@ -184,7 +190,7 @@ def sustained_leg(eng, args, st, s):
 
 
 BOUND = {"gemm_qkv": "mfma", "gemm_oproj": "mfma", "gemm_swiglu": "mfma", "gemm_down": "mfma", "attention": "mfma",
-         "blend_scatter": "hbm", "deviation": "hbm", "rope": "hbm", "embed": "hbm"}
+         "blend_scatter": "hbm", "deviation": "hbm", "rope": "hbm", "rope_fuse": "hbm", "embed": "hbm"}
 
 
 def cpu_baseline(w, eng, rec_state, step_flops, layers=(2, 3, 4)):
@@ -342,11 +348,14 @@ def tier_host(eng, args, st, n_selected):
 
 
 def cold_hbm_leg(eng, s, dev):
-    """The two HBM-bound row kernels of the step timed cold: a 1 GiB buffer is
-    rewritten before each call so that no operand is left in the 256 MiB MALL
-    or the L2s.  Deviation over all N tokens (layer 1, as in the step) and the
-    fusion + scatter over the layer-2 rows (alpha, d and CKSim not written, the
-    new-page slots of the last step rewritten with the same kind of values)."""
+    """The HBM-bound row kernels timed cold: before each call a 1 GiB buffer
+    refills the 256 MiB MALL and the L2s, so that no operand is cached.  The
+    buffer is read ("clean": the caches then hold clean lines, the kernel's
+    own bandwidth) or written ("dirty": the kernel's reads also compete with
+    the write-back of the dirty lines the fill leaves).  Deviation over all N
+    tokens (layer 1, as in the step) and the standalone fusion + scatter over
+    the layer-2 rows (alpha, d and CKSim not written, the new-page slots of the
+    last step rewritten with the same kind of values)."""
     import numpy as np
     import torch
 
@@ -354,7 +363,7 @@ def cold_hbm_leg(eng, s, dev):
 
     esz = 2 if s.dtype == "bf16" else 4
     Hkv, hd = s.n_kv_heads, s.head_dim
-    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     c, sh, ds = eng.ctx, eng.sh, eng.desc
     T = int(eng.k_cap[0]) if eng.B == 1 else eng.T_sel
     calls = {
@@ -375,20 +384,26 @@ def cold_hbm_leg(eng, s, dev):
                    eng.cu_pages[2], eng.page_table[1], eng.dst_slot)
     out = {}
     for name, (fn, nbytes) in calls.items():
-        ms = []
-        for _ in range(6):
-            flush.fill_(1.0)
-            K.kvb_timing_enable(c, name)
-            fn()
-            t = K.kvb_timing_read(c)[name]
-            K.kvb_timing_enable(c, None)
-            ms.append(t["ms"] / t["count"])
-        m = float(np.median(ms[1:]))
-        out[name] = {"ms": m, "bytes": nbytes, "GBps": nbytes / (m * 1e-3) / 1e9,
-                     "frac": nbytes / (m * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        res = {}
+        for mode in ("clean", "dirty"):
+            ms = []
+            for _ in range(6):
+                if mode == "clean":
+                    flush.sum()
+                else:
+                    flush.fill_(1.0)
+                K.kvb_timing_enable(c, name)
+                fn()
+                t = K.kvb_timing_read(c)[name]
+                K.kvb_timing_enable(c, None)
+                ms.append(t["ms"] / t["count"])
+            m = float(np.median(ms[1:]))
+            res[mode] = {"ms": m, "GBps": nbytes / (m * 1e-3) / 1e9, "frac": nbytes / (m * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        out[name] = dict(res["clean"], bytes=nbytes, dirty=res["dirty"])
     del flush
     torch.cuda.synchronize()
-    out["note"] = "cold: 1 GiB written before each call; median of 5 calls after one warm-up"
+    out["note"] = ("cold: 1 GiB read before each call (clean caches; under 'dirty', written instead); median of 5 "
+                   "calls after one warm-up")
     return out
 
 
