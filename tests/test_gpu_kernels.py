@@ -604,14 +604,13 @@ DEV_SHAPES = {
 }
 
 
-@pytest.mark.parametrize("name", list(DEV_SHAPES))
+@pytest.mark.parametrize("name,invalid", [(n, False) for n in DEV_SHAPES] + [("bf16", True), ("bf16_kv8", True)],
+                         ids=[n for n in DEV_SHAPES] + ["bf16-invalid", "bf16_kv8-invalid"])
 @pytest.mark.parametrize("req_lens", [[517], [4100, 300, 2049, 64], [2048, 2048]])
-@pytest.mark.parametrize("invalid", [False, True], ids=["slots", "invalid"])
-def test_deviation_topk(ctx, name, req_lens, invalid):
-    """d, alpha vs the oracle; the top-k of the GPU's d bit-exact; a token
-    whose reused slot lies outside the pool is compared with a zero cached key."""
-    if invalid and name != "bf16" and name != "bf16_kv8":
-        pytest.skip("invalid slots: one shape per kernel")
+def test_deviation_topk(ctx, name, invalid, req_lens):
+    """d, alpha vs the oracle; the top-k of the GPU's d bit-exact; with
+    `invalid`, tokens whose reused slot lies outside the pool (one shape per
+    kernel) are compared with a zero cached key."""
     s = DEV_SHAPES[name]
     g = np.random.default_rng(sum(req_lens))
     desc = K.model_desc(s)
