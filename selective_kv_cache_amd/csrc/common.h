@@ -71,6 +71,15 @@ kvb_status noalloc_scratch_setup(int device);
 size_t ws_mlp_bytes(const kvb_model_desc* d, int32_t max_rows, int n_cu);
 size_t ws_gemm_sk_bytes(int n_cu);
 size_t ws_qkv_bytes(const kvb_model_desc* d, int32_t max_rows);
+
+// One bf16 row on a split-K launch, nothing fused with a cached row: RMSNorm,
+// the one-row Q/K/V product, and in its epilogue RoPE of Q and K and the K/V
+// store into slot dst_slot[0] (what kvb_qkv_proj without RoPE followed by the
+// RoPE + fusion pass in KVB_ALPHA_ONE mode writes, bitwise).
+kvb_status qkv_rope_one_row(hipStream_t st, const kvb_model_desc* d, const int32_t* n_rows, const int32_t* row_tok,
+                            const void* hidden, const void* norm_w, const void* w_qkv, const int32_t* tok_pos, void* q,
+                            void* k, void* v, void* k_pool, void* v_pool, int n_slots, const int32_t* dst_slot,
+                            void* ws);
 size_t ws_topk_bytes(int32_t max_tokens, int32_t max_requests);
 size_t ws_refresh_bytes(int32_t max_tokens, int32_t max_requests);
 size_t ws_attn_bytes(const kvb_model_desc* d, int32_t max_rows, int n_cu);
@@ -198,6 +207,11 @@ __device__ __forceinline__ float2 rope_cs(int pos, double f) {
   sincosf((float)red, &s, &c);
   return make_float2(c, s);
 }
+
+// the two halves of a rotated pair, with the products and their one fused
+// add spelled out so that every kernel rounds them the same way
+__device__ __forceinline__ float rot_lo(float x1, float x2, float c, float s) { return fmaf(x1, c, -(x2 * s)); }
+__device__ __forceinline__ float rot_hi(float x2, float x1, float c, float s) { return fmaf(x2, c, x1 * s); }
 
 // wave64 reductions
 __device__ __forceinline__ float wave_sum(float v) {

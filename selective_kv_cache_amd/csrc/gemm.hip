@@ -594,20 +594,37 @@ __device__ __forceinline__ float dot8_bf16(const uint4& w, const uint4& x, float
   return acc;
 }
 
+// RoPE epilogue of the one-row Q/K/V product (decode): the wave's two outputs
+// are the pair (i, i + hd/2) of one head, rotated together; K and V also go to
+// the row's slot in the pool.
+struct RopeEpi {
+  const int32_t* tok_pos;
+  const int32_t* row_tok;
+  const int32_t* dst_slot;
+  bf16_t* k_pool;
+  bf16_t* v_pool;
+  int n_slots, Hkv, hd;
+  RopeFreq rf;
+};
+
 // (at most 4 waves per SIMD: the registers for a whole batch of loads in flight)
-template <int MODE, bool DUAL>
+template <int MODE, bool DUAL, bool ROPE = false>
 __global__ void __launch_bounds__(64 * GV_WAVES) __attribute__((amdgpu_waves_per_eu(1, 4)))
-gemv_bf16_kernel(GemmArgs<bf16_t> p) {
+gemv_bf16_kernel(GemmArgs<bf16_t> p, RopeEpi re) {
+  static_assert(!ROPE || (MODE == EPI_QKV && !DUAL && GV_NW == 2), "RoPE pairs two Q/K/V outputs");
   extern __shared__ __align__(16) uint8_t gv_x[];
   if (row_count(p.n_rows, p.M_max) < 1) return;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int C = p.K / 8;  // 16-byte chunks per row
-  const int nb = (blockIdx.x * GV_WAVES + wave) * GV_NW;
+  const int wg = blockIdx.x * GV_WAVES + wave;
+  // the wave's outputs: nb + i (ROPE: the pair of one head, hd / 2 apart)
+  const int nb = ROPE ? (wg / (re.hd / 2)) * re.hd + wg % (re.hd / 2) : wg * GV_NW;
+  const int nstep = ROPE ? re.hd / 2 : 1;
   constexpr int R = DUAL ? 2 * GV_NW : GV_NW;  // rows i < GV_NW: B; the rest: B2
   const uint4* wr[R];
 #pragma unroll
   for (int i = 0; i < GV_NW; i++) {
-    int n = nb + i < p.N ? nb + i : p.N - 1;
+    int n = nb + i * nstep < p.N ? nb + i * nstep : p.N - 1;
     n = n < 0 ? 0 : n;
     wr[i] = reinterpret_cast<const uint4*>(p.B + (size_t)n * p.K);
     if (DUAL) wr[GV_NW + i] = reinterpret_cast<const uint4*>(p.B2 + (size_t)n * p.K);
@@ -626,7 +643,7 @@ gemv_bf16_kernel(GemmArgs<bf16_t> p) {
   };
   // the first batch is issued before x is staged: the weight stream does not
   // wait for the staging and its barrier
-  const bool active = nb < p.N;
+  const bool active = ROPE ? 2 * wg < p.N : nb < p.N;
   const bool first = active && lane + 192 < C;
   uint4 w0[4][R];
   if (first) load_batch(lane, w0);
@@ -675,6 +692,33 @@ gemv_bf16_kernel(GemmArgs<bf16_t> p) {
 #pragma unroll
     for (int i = 0; i < R; i++) acc[i] = dot8_bf16(wr[i][c], xv, acc[i]);
   }
+  if constexpr (ROPE) {
+    // both sums in every lane; lane 0 stores the low half of the pair, lane 1
+    // the high half.  Each value is first rounded to bf16, as the product
+    // stores it, then rotated (Q, K) and rounded again, as the RoPE pass does.
+    const float x0 = bf2f(f2bf(wave_sum(acc[0]))), x1 = bf2f(f2bf(wave_sum(acc[1])));
+    if (lane >= 2) return;
+    const int n = nb + lane * nstep;
+    float y = lane == 0 ? x0 : x1;
+    if (nb < p.n1) {
+      const int g = re.row_tok ? re.row_tok[0] : 0;
+      const float2 cs = rope_cs(re.tok_pos[g], re.rf.f[nb % re.hd]);
+      y = lane == 0 ? rot_lo(x0, x1, cs.x, cs.y) : rot_hi(x1, x0, cs.x, cs.y);
+      y = bf2f(f2bf(y));
+    }
+    const bf16_t yb = f2bf(y);
+    if (n < p.n0) {
+      p.out0[n] = yb;
+      return;
+    }
+    const bool is_k = n < p.n1;
+    const int kn = is_k ? n - p.n0 : n - p.n1;
+    (is_k ? p.out1 : p.out2)[kn] = yb;
+    const int dst = re.dst_slot[0];
+    if (dst >= 0 && dst < re.n_slots)
+      (is_k ? re.k_pool : re.v_pool)[pool_off(dst, kn / re.hd, re.Hkv, re.hd) + kn % re.hd] = yb;
+    return;
+  }
   float v = 0.f, v2 = 0.f;
 #pragma unroll
   for (int i = 0; i < GV_NW; i++) {
@@ -704,11 +748,11 @@ gemv_bf16_kernel(GemmArgs<bf16_t> p) {
   *dst = (bf16_t)(pack2_bf16(v, 0.f) & 0xffffu);
 }
 
-template <int MODE, bool DUAL>
-static kvb_status launch_gemv(hipStream_t st, const GemmArgs<bf16_t>& p, const char* name) {
+template <int MODE, bool DUAL, bool ROPE = false>
+static kvb_status launch_gemv(hipStream_t st, const GemmArgs<bf16_t>& p, const char* name, const RopeEpi& re = {}) {
   {
     LaunchTimer lt(st, name);
-    gemv_bf16_kernel<MODE, DUAL><<<cdiv(p.N, GV_NW * GV_WAVES), 64 * GV_WAVES, (size_t)p.K * 2, st>>>(p);
+    gemv_bf16_kernel<MODE, DUAL, ROPE><<<cdiv(p.N, GV_NW * GV_WAVES), 64 * GV_WAVES, (size_t)p.K * 2, st>>>(p, re);
   }
   return check_launch("gemv_bf16_kernel");
 }
@@ -929,6 +973,38 @@ static kvb_status qkv_impl(hipStream_t st, const kvb_model_desc* d, int T_max, c
   }
   if (tok_pos) return launch_rope<T>(st, T_max, n_rows, row_tok, tok_pos, q, k, d);
   return KVB_OK;
+}
+
+kvb_status qkv_rope_one_row(hipStream_t st, const kvb_model_desc* d, const int32_t* n_rows, const int32_t* row_tok,
+                            const void* hidden, const void* norm_w, const void* w_qkv, const int32_t* tok_pos, void* q,
+                            void* k, void* v, void* k_pool, void* v_pool, int n_slots, const int32_t* dst_slot,
+                            void* ws) {
+  GemmArgs<bf16_t> p{};
+  p.B = (const bf16_t*)w_qkv;
+  p.M_max = 1;
+  p.n_rows = n_rows;
+  p.K = d->d_model;
+  p.n0 = d->n_q_heads * d->head_dim;
+  p.n1 = p.n0 + d->n_kv_heads * d->head_dim;
+  p.N = p.n1 + d->n_kv_heads * d->head_dim;
+  p.eps = d->rms_eps;
+  p.out0 = (bf16_t*)q;
+  p.out1 = (bf16_t*)k;
+  p.out2 = (bf16_t*)v;
+  bf16_t* a = (bf16_t*)ws;  // the normalised row
+  KVB_TRY(rmsnorm_rows(st, (const bf16_t*)hidden, row_tok, n_rows, 1, d->d_model, (const bf16_t*)norm_w, d->rms_eps, a));
+  p.A = a;
+  RopeEpi re{};
+  re.tok_pos = tok_pos;
+  re.row_tok = row_tok;
+  re.dst_slot = dst_slot;
+  re.k_pool = (bf16_t*)k_pool;
+  re.v_pool = (bf16_t*)v_pool;
+  re.n_slots = n_slots;
+  re.Hkv = d->n_kv_heads;
+  re.hd = d->head_dim;
+  re.rf = rope_freq(d->head_dim, d->rope_base);
+  return launch_gemv<EPI_QKV, false, true>(st, p, "gemm_qkv", re);
 }
 
 template <class T>

@@ -38,10 +38,6 @@ __global__ void embed_kernel(int T_max, const int32_t* __restrict__ n_rows, cons
 template <class T> __device__ __forceinline__ void load8(const T* p, float* o);
 template <class T> __device__ __forceinline__ void store8(T* p, const float* v);
 
-// the two halves of a rotated pair, with the products and their one fused
-// add spelled out so that every kernel rounds them the same way
-__device__ __forceinline__ float rot_lo(float x1, float x2, float c, float s) { return fmaf(x1, c, -(x2 * s)); }
-__device__ __forceinline__ float rot_hi(float x2, float x1, float c, float s) { return fmaf(x2, c, x1 * s); }
 
 template <class T>
 __global__ void __launch_bounds__(256) rope_kernel(int T_max, const int32_t* __restrict__ n_rows,
@@ -740,6 +736,21 @@ extern "C" kvb_status kvb_qkv_fused(kvb_ctx* ctx, void* stream, const kvb_model_
     return fail(KVB_ERR_INVALID_ARG, "without src_slot only KVB_ALPHA_ONE and no d_out / cksim_out");
   if ((long)n_pages * 16 > 0x7fffffffL) return fail(KVB_ERR_INVALID_ARG, "too many pages for int32 slots");
   const int Hkv = desc->n_kv_heads, hd = desc->head_dim;
+  if (desc->dtype == KVB_BF16 && T_max == 1 && flags == KVB_QKV_SPLIT_K && !src_slot && tok_pos &&
+      desc->d_model % 8 == 0 && desc->d_model <= 32768) {
+    // one row replacing nothing cached (decode): RoPE and the K/V store run in
+    // the epilogue of the one-row product, no separate pass
+    KVB_CHECK_PTR(hidden, "hidden");
+    KVB_CHECK_PTR(w_qkv, "w_qkv");
+    KVB_CHECK_PTR(q, "q");
+    KVB_CHECK_PTR(k, "k");
+    KVB_CHECK_PTR(v, "v");
+    const size_t need = ws_qkv_bytes(desc, T_max) + ws_gemm_sk_bytes(0);
+    if (!ws || ws_bytes < need) return fail(KVB_ERR_WORKSPACE, "kvb_qkv_fused workspace too small");
+    CtxScope scope(ctx);
+    return qkv_rope_one_row((hipStream_t)stream, desc, n_rows, row_tok, hidden, norm_w, w_qkv, tok_pos, q, k, v,
+                            k_pool, v_pool, n_pages * 16, dst_slot, ws);
+  }
   const int nkv = 2 * Hkv * hd / 8;  // K and V vectors of a row, one per thread
   if (nkv > 1024 || Hkv > 64 || (long)desc->n_q_heads * hd / 8 > 8L * std::max(64, (nkv + 63) / 64 * 64)) {
     KVB_TRY(kvb_qkv_proj(ctx, stream, desc, T_max, n_rows, row_tok, hidden, norm_w, w_qkv, tok_pos, q, k, v, ws,

@@ -233,10 +233,11 @@ def test_blend_scatter(ctx, name, mode):
 @pytest.mark.parametrize("flags,T_max,n_valid", [(K.KVB_QKV_BATCH_INVARIANT, 200, 173), (K.KVB_QKV_SPLIT_K, 200, 173),
                                                  (K.KVB_QKV_SPLIT_K, 1, 1)], ids=["inv", "splitk", "one-row"])
 def test_qkv_fused(ctx, name, mode, cached, flags, T_max, n_valid):
-    """Projection, then RoPE + fusion + scatter in one pass: bitwise the result of
-    kvb_qkv_proj (with positions) followed by kvb_blend_scatter on the same
-    inputs; Q/K/V against the oracle, and the fused rows, d, alpha and CKSim
-    against the oracle applied to the call's own recomputed K/V."""
+    """Projection, then RoPE + fusion + scatter in one pass (for one bf16 row
+    with nothing cached, as in decode, inside the product's epilogue): bitwise
+    the result of kvb_qkv_proj (with positions) followed by kvb_blend_scatter
+    on the same inputs; Q/K/V against the oracle, and the fused rows, d, alpha
+    and CKSim against the oracle applied to the call's own recomputed K/V."""
     s = SHAPES[name]
     g = np.random.default_rng(31 + mode + 7 * T_max)
     desc = K.model_desc(s)
@@ -280,7 +281,12 @@ def test_qkv_fused(ctx, name, mode, cached, flags, T_max, n_valid):
         return o
 
     ref, got = run(False), run(True)
-    assert "rope_fuse" in got["launched"] and "rope" not in got["launched"] and "blend_scatter" not in got["launched"]
+    assert "rope" not in got["launched"] and "blend_scatter" not in got["launched"]
+    if T_max == 1 and flags == K.KVB_QKV_SPLIT_K and not cached and s.dtype == "bf16":
+        # one row replacing nothing cached (decode): RoPE and the K/V store in the product's epilogue
+        assert "rope_fuse" not in got["launched"] and got["launched"]["gemm_qkv"]["count"] == 1
+    else:
+        assert "rope_fuse" in got["launched"]
     for key in ("q", "k", "v", "kp", "vp", "alpha", "d", "ck"):
         assert torch.equal(got[key], ref[key]), key
     q, k, v, kp, vp, alpha, d_out, ck = (got[x] for x in ("q", "k", "v", "kp", "vp", "alpha", "d", "ck"))
