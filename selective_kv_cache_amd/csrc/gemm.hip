@@ -233,12 +233,12 @@ struct Tile {
   __device__ __forceinline__ static int swz(int r) { return KB == 32 ? ((r >> 2) & 3) : ((r >> 1) & 7); }
 };
 
-// The ring stages are separate LDS objects and the K loop is unrolled by NST,
-// so every stage address is a compile-time constant.
-template <class TL, int S>
-struct StageLds {
+// The ring: NST stages of ARR bytes in one LDS object; the K loop is unrolled
+// by NST, so every stage address is a compile-time constant.
+template <class TL>
+struct RingLds {
   __device__ static uint8_t* ptr() {
-    __shared__ __align__(16) uint8_t buf[TL::ARR];
+    __shared__ __align__(16) uint8_t buf[TL::NST * TL::ARR];
     return buf;
   }
 };
@@ -280,6 +280,24 @@ __device__ __forceinline__ void tile_coords(int t, int num_m, int num_n, int& tm
   tn = in / gm;
 }
 
+// Epilogue staging of a tile with OUT_N output columns: float slabs of 32
+// rows x (OUT_N + 8) (rows 4 apart land 32 banks apart), SPS of them in each
+// ring stage; each phase fills G slabs per wave row, G the largest divisor of
+// the wave's subtile count whose WM * G slabs fit the ring.
+template <class TL, int OUT_N>
+struct EpiPlan {
+  static constexpr int SLAB = 32 * (OUT_N + 8) * 4;
+  static constexpr int SPS = TL::ARR / SLAB;
+  static constexpr int pick() {
+    int g = TL::TM;
+    while (g > 1 && (TL::TM % g || TL::WM * g > TL::NST * SPS)) g--;
+    return g;
+  }
+  static constexpr int G = pick();
+  static_assert(TL::WM * G <= TL::NST * SPS, "epilogue slabs exceed the ring");
+  static_assert(TL::WM * G * 32 * (OUT_N / 8) % GEMM_THREADS == 0, "epilogue chunks per thread");
+};
+
 template <int MODE, bool DUAL, class TL, bool SK>
 __global__ void __launch_bounds__(GEMM_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_bf16_kernel(GemmArgs<bf16_t> p, SkArgs sk) {
@@ -289,8 +307,8 @@ gemm_bf16_kernel(GemmArgs<bf16_t> p, SkArgs sk) {
   constexpr int OUT_N = DUAL ? BN / 2 : BN;  // output columns per block
   constexpr bool PA = NST >= 3;              // publish the next stage one step ahead
   static_assert(!DUAL || TN % 2 == 0, "SwiGLU pairs gate and up subtiles inside a wave");
-  uint8_t* const stg[4] = {StageLds<TL, 0>::ptr(), StageLds<TL, 1>::ptr(),
-                           NST > 2 ? StageLds<TL, 2>::ptr() : nullptr, NST > 3 ? StageLds<TL, 3>::ptr() : nullptr};
+  uint8_t* const ring = RingLds<TL>::ptr();
+  uint8_t* const stg[4] = {ring, ring + TL::ARR, ring + 2 * TL::ARR, ring + 3 * TL::ARR};  // stages < NST
 
   const int M = row_count(p.n_rows, p.M_max);
   const int num_m = cdiv_dev(p.M_max, BM), num_n = cdiv_dev(p.N, OUT_N);
@@ -447,40 +465,83 @@ gemm_bf16_kernel(GemmArgs<bf16_t> p, SkArgs sk) {
       return;
     }
 
-    // ---- epilogue, staged through LDS in BM / 32 phases of 32 rows: the waves
-    // owning a phase's rows (subtile i of their wave row) write their float
-    // accumulators (SwiGLU already combined) to a [32][OUT_N] tile, then all
-    // threads read 8 consecutive outputs of a row, apply the mode (residual,
-    // scatter) and store 16 bytes at a time.
+    // ---- epilogue, staged through LDS: in each phase every wave row writes
+    // the float accumulators (SwiGLU already combined) of G of its 32-row
+    // subtiles to slabs [32][OUT_N + 8] in the ring's stages, then all threads
+    // read 8 consecutive outputs of a row, apply the mode (residual, scatter)
+    // and store 16 bytes at a time.  The gather / scatter indices and residual
+    // rows of every chunk a thread stores are loaded before its first store,
+    // so no wait for them also waits for a store (vmcnt counts both).
     // acc[i][j][r] sits at tile row wm + 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4,
     // tile col wn + 32 j + lane % 32 (DUAL: output col (wn / 32 + j) / 2 * 32 + lane % 32).
-    constexpr int LDC = OUT_N + 8;  // floats; rows 4 apart land 32 banks apart
-    float* sC = reinterpret_cast<float*>(stg[0]);
-    const int lc = lane & 31;
+    using EP = EpiPlan<TL, OUT_N>;
+    constexpr int G = EP::G, LDC = OUT_N + 8, CPRO = OUT_N / 8;
+    constexpr int NPH = TM / G;                                 // phases
+    constexpr int NCH = TL::WM * G * 32 * CPRO / GEMM_THREADS;  // chunks per thread per phase
+    constexpr bool LOADS = MODE == EPI_RESID || MODE == EPI_SCATTER;
+    const int wr = wave / WN, lc = lane & 31;
+    // slab s = wave row * G + g: ring stage s % NST, slab (s / NST) of that stage
+    auto slab = [&](int s) { return reinterpret_cast<float*>(ring + (s % NST) * TL::ARR + (s / NST) * EP::SLAB); };
+    // thread t stores chunks k of each phase: phase row q = t / CPRO + k * (GEMM_THREADS / CPRO)
+    // (slab q / 32, row q % 32), columns n0 + cc .. + 7
+    const int cc = (t % CPRO) * 8, n = n0 + cc;
+    auto tile_row = [&](int ph, int k) {
+      const int q = t / CPRO + k * (GEMM_THREADS / CPRO), s = q >> 5;
+      return (s / G) * 32 * TM + (ph * G + s % G) * 32 + (q & 31);
+    };
+    uint4 hres[LOADS ? NPH : 1][LOADS ? NCH : 1];
+    int orow[MODE == EPI_SCATTER ? NPH : 1][MODE == EPI_SCATTER ? NCH : 1];
+    if constexpr (LOADS) {
+      // clamped into range, so every load is issued (invalid chunks store nothing)
+      const int nl = n < p.N ? n : p.N - 8;
+      const int32_t* gidx = MODE == EPI_RESID ? p.resid_rows : p.out_rows;
+      int rr[NPH][NCH];
 #pragma unroll
-    for (int ph = 0; ph < BM / 32; ph++) {
-      const int i = ph % TM;
-      if (wave / WN == ph / TM) {
+      for (int ph = 0; ph < NPH; ph++)
+#pragma unroll
+        for (int k = 0; k < NCH; k++) {
+          const int m = min(m0 + tile_row(ph, k), M - 1);
+          const int g = gidx ? gidx[m] : m;
+          if constexpr (MODE == EPI_SCATTER) orow[ph][k] = g;
+          rr[ph][k] = MODE == EPI_RESID ? g : m;
+        }
+#pragma unroll
+      for (int ph = 0; ph < NPH; ph++)
+#pragma unroll
+        for (int k = 0; k < NCH; k++)
+          hres[ph][k] = *reinterpret_cast<const uint4*>(p.resid + (size_t)rr[ph][k] * p.ldr + nl);
+    }
+#pragma unroll
+    for (int ph = 0; ph < NPH; ph++) {
+#pragma unroll
+      for (int g = 0; g < G; g++) {
+        const int i = ph * G + g;
+        float* sC = slab(wr * G + g);
 #pragma unroll
         for (int j = 0; j < TN; j += (DUAL ? 2 : 1)) {
           const int cl = DUAL ? ((wn / 32 + j) >> 1) * 32 + lc : wn + j * 32 + lc;
 #pragma unroll
           for (int r = 0; r < 16; r++) {
-            const int rl = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);  // row inside the phase
+            const int rl = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);  // row inside the subtile
             float v = acc[i][j][r];
             if (DUAL) v = silu_bf16(v) * acc[i][j + 1][r];
             sC[rl * LDC + cl] = v;
           }
         }
       }
-      __syncthreads();
-      constexpr int CPRO = OUT_N / 8;  // 8-output chunks per row
-      for (int c = t; c < 32 * CPRO; c += GEMM_THREADS) {
-        const int rl = c / CPRO, cc = (c % CPRO) * 8;
-        const int ml = ph * 32 + rl, m = m0 + ml, n = n0 + cc;
+      lds_barrier();
+      // the residual loads, issued before the first slab fill, are all in
+      // before any store is issued (the stores sit in branches, which the
+      // compiler's own wait counts cannot see past)
+      if (LOADS && ph == 0) wait_vmcnt<0>();
+#pragma unroll
+      for (int k = 0; k < NCH; k++) {
+        const int q = t / CPRO + k * (GEMM_THREADS / CPRO);
+        const int m = m0 + tile_row(ph, k);
         if (m >= M || n >= p.N) continue;
-        const float4 lo = *reinterpret_cast<const float4*>(sC + rl * LDC + cc);
-        const float4 hi = *reinterpret_cast<const float4*>(sC + rl * LDC + cc + 4);
+        const float* src = slab(q >> 5) + (q & 31) * LDC + cc;
+        const float4 lo = *reinterpret_cast<const float4*>(src);
+        const float4 hi = *reinterpret_cast<const float4*>(src + 4);
         float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
         bf16_t* dst;
         if (MODE == EPI_QKV) {
@@ -490,21 +551,20 @@ gemm_bf16_kernel(GemmArgs<bf16_t> p, SkArgs sk) {
         } else if (MODE == EPI_SWIGLU) {
           dst = p.out0 + (size_t)m * p.ldo + n;
         } else {
-          const int rr = (MODE == EPI_RESID && p.resid_rows) ? p.resid_rows[m] : m;
-          const uint4 h = *reinterpret_cast<const uint4*>(p.resid + (size_t)rr * p.ldr + n);
+          const uint4 h = hres[LOADS ? ph : 0][LOADS ? k : 0];
           const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
 #pragma unroll
           for (int e = 0; e < 4; e++) {
             v[2 * e] += __uint_as_float(hw[e] << 16);
             v[2 * e + 1] += __uint_as_float(hw[e] & 0xffff0000u);
           }
-          const int orow = (MODE == EPI_SCATTER && p.out_rows) ? p.out_rows[m] : m;
-          dst = p.out0 + (size_t)orow * p.ldo + n;
+          const int o = MODE == EPI_SCATTER ? orow[MODE == EPI_SCATTER ? ph : 0][MODE == EPI_SCATTER ? k : 0] : m;
+          dst = p.out0 + (size_t)o * p.ldo + n;
         }
         *reinterpret_cast<uint4*>(dst) = make_uint4(pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3]),
                                                     pack2_bf16(v[4], v[5]), pack2_bf16(v[6], v[7]));
       }
-      __syncthreads();
+      if (ph + 1 < NPH) lds_barrier();  // every thread has read the slabs the next phase overwrites
     }
   }
 }
