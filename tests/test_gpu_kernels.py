@@ -597,6 +597,56 @@ def test_mlp(ctx, name, T_max, n_valid):
     assert torch.equal(hidden[others].cpu(), hidden0[others])
 
 
+@pytest.mark.parametrize("T_max", [700, 1000, 1300, 1700, 2500, 2800, 4200, 6300])
+def test_gemm_tile_epilogues(ctx, T_max):
+    """Q/K/V projection (batch-invariant and split-K launches), O-projection and
+    MLP at row counts for which the launch rule on a 256-CU device picks, over
+    the eight sizes, every tile shape's own epilogue (no split) in every mode:
+    256x256, 192x256, 256x128 and 128x128 for Q/K/V, residual, SwiGLU and
+    scatter, 64x256 for Q/K/V and SwiGLU.  Gathered rows, a row count below
+    the launch bound, oracle on sampled rows (tile edges included), untouched
+    rows checked whole."""
+    s = SHAPES["bf16_wide"]
+    g = np.random.default_rng(70 + T_max)
+    desc = K.model_desc(s)
+    dt = tdt(s)
+    n_valid = T_max - 29
+    n_tok = T_max + 97
+    W = weights(s, g)
+    Wn = {kk: np64(vv) for kk, vv in W.items()}
+    hidden0 = rand((n_tok, s.d_model), g, dtype=dt)
+    rows = np.sort(g.choice(n_tok, T_max, replace=False))
+    pos = g.integers(0, 32768, n_tok)
+    edges = [e + d_ for e in (64, 128, 192, 256, 384, 512, 768, 1024) for d_ in (-1, 0)]
+    smp = np.unique(np.concatenate([[0, n_valid - 1], [e for e in edges if e < n_valid],
+                                    g.choice(n_valid, 40, replace=False)]))
+    ws, wsb = workspace(ctx, desc, T_max, n_tok)
+
+    for flags in (K.KVB_QKV_BATCH_INVARIANT, K.KVB_QKV_SPLIT_K):
+        hidden = hidden0.to(DEV)
+        q = torch.full((T_max, s.n_q_heads, s.head_dim), 7.0, dtype=dt, device=DEV)
+        k = torch.full((T_max, s.n_kv_heads, s.head_dim), 7.0, dtype=dt, device=DEV)
+        v = torch.full((T_max, s.n_kv_heads, s.head_dim), 7.0, dtype=dt, device=DEV)
+        K.kvb_qkv_proj(ctx, sh(), desc, T_max, i32([n_valid]), i32(rows), hidden, W["norm1"], W["w_qkv"], i32(pos),
+                       q, k, v, ws, wsb, flags)
+        torch.cuda.synchronize()
+        rq, rk, rv = OM.qkv(np64(hidden0)[rows[smp]], pos[rows[smp]], Wn, s)
+        assert max_rel_err(q[smp], rq) < TOL[s.dtype]
+        assert max_rel_err(k[smp], rk) < TOL[s.dtype]
+        assert max_rel_err(v[smp], rv) < TOL[s.dtype]
+        assert torch.all(q[n_valid:] == 7.0) and torch.all(k[n_valid:] == 7.0) and torch.all(v[n_valid:] == 7.0)
+
+    hidden = hidden0.to(DEV)
+    o = rand((T_max, s.q_dim), g, dtype=dt).to(DEV)
+    K.kvb_mlp(ctx, sh(), desc, T_max, i32([n_valid]), i32(rows), o, W["w_o"], hidden, W["norm2"], W["w_gate_up"],
+              W["w_down"], ws, wsb)
+    torch.cuda.synchronize()
+    ref = OM.post_attention(np64(hidden0)[rows[smp]], np64(o)[smp], Wn, s)
+    assert max_rel_err(hidden[rows[smp]], ref) < TOL[s.dtype]
+    others = np.setdiff1d(np.arange(n_tok), rows[:n_valid])
+    assert torch.equal(hidden[others].cpu(), hidden0[others])
+
+
 # ------------------------------------------------------------------ deviation + top-k
 
 DEV_SHAPES = {
