@@ -300,6 +300,7 @@ __global__ void __launch_bounds__(1024) rope_fuse_kernel(int T_max, const int32_
     for (int e = 0; e < 8; e++) x[e] = 0.f;
   }
   const int g = row_tok ? row_tok[r] : r;
+  const int dst = dst_slot[r];  // read now: after the barriers its latency would end the block
   const int src = src_slot ? src_slot[g] : -1;
   const bool have_src = src_slot && src >= 0 && src < n_slots;
 #pragma unroll
@@ -373,7 +374,6 @@ __global__ void __launch_bounds__(1024) rope_fuse_kernel(int T_max, const int32_
       if (cksim_out) cksim_out[r] = cks;
     }
   }
-  const int dst = dst_slot[r];
   if (!act || dst < 0 || dst >= n_slots) return;
   float o[8];
   if (src_slot && a_use != 1.f) {
