@@ -22,6 +22,8 @@
 #include "common.h"
 
 #include <algorithm>
+#include <functional>
+#include <vector>
 #include <type_traits>
 
 namespace kvb {
@@ -263,11 +265,26 @@ __device__ __forceinline__ void wait_vm_upto(int allowed) {
 
 // split-K schedule of one launch
 struct SkArgs {
-  int S;           // K slices per tile (1: no split)
+  int S;           // K slices per tile (1: no split); a mixed plan gives a tile S or S + 1
   int rows;        // row stride of a slice: M_max rounded up to the tile height
   int cols;        // N (DUAL: 2 N, gate columns then up columns)
-  float* part;     // [S][rows][cols]
+  float* part;     // [slice][rows][cols]
+  // Mixed plan (xcd_blocks > 0): the tile order is cut into 8 contiguous runs,
+  // run x for the blocks of XCD x; a run of n tiles gives its last
+  // h = clamp(xcd_blocks - n S, 0, n) tiles S + 1 slices and the others S,
+  // and its S-slice blocks come first, so whole rounds of blocks fill the CUs.
+  int xcd_blocks;
+  int bm, bn;      // tile rows and output columns; tiles per column and row
+  int num_m, num_n;
 };
+
+// run x of a mixed plan: first tile t0, nt tiles, the last nh of them with S + 1 slices
+__host__ __device__ inline void mixed_run(int tiles, int x, int S, int xcd_blocks, int& t0, int& nt, int& nh) {
+  t0 = (int)((long)x * tiles / 8);
+  nt = (int)((long)(x + 1) * tiles / 8) - t0;
+  nh = xcd_blocks - nt * S;
+  nh = nh < 0 ? 0 : (nh > nt ? nt : nh);
+}
 
 // grouped tile order: GM m-tiles sweep all n-tiles, so concurrent tiles share panels
 __device__ __forceinline__ void tile_coords(int t, int num_m, int num_n, int& tm, int& tn) {
@@ -278,6 +295,14 @@ __device__ __forceinline__ void tile_coords(int t, int num_m, int num_n, int& tm
   const int in = t - grp * gsize;
   tm = first + in % gm;
   tn = in / gm;
+}
+
+// inverse of tile_coords
+__device__ __forceinline__ int tile_index(int tm, int tn, int num_m, int num_n) {
+  const int GM = num_m <= 16 ? num_m : 8;
+  const int grp = tm / GM, first = grp * GM;
+  const int gm = min(GM, num_m - first);
+  return grp * GM * num_n + tn * gm + (tm - first);
 }
 
 // Epilogue staging of a tile with OUT_N output columns: float slabs of 32
@@ -324,12 +349,30 @@ gemm_bf16_kernel(GemmArgs<bf16_t> p, SkArgs sk) {
   // this block's work: K slice `split` of one tile.  Workgroups go to the 8
   // XCDs round-robin (id % 8), each XCD with its own L2: give every XCD a
   // contiguous run of the (tile, slice) order.
-  const int S = SK ? sk.S : 1;
-  const int total = tiles * S;
-  const int per = (total + 7) >> 3;
-  const int tid = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
-  if (tid >= total) return;
-  const int tile = tid / S, split = tid - tile * S;
+  int tile, split, S;
+  if (SK && sk.xcd_blocks > 0) {
+    int t0, nt, nh;
+    mixed_run(tiles, (int)(blockIdx.x & 7), sk.S, sk.xcd_blocks, t0, nt, nh);
+    const int li = (int)(blockIdx.x >> 3), n_long = (nt - nh) * sk.S;
+    if (li >= n_long + nh * (sk.S + 1)) return;
+    if (li < n_long) {
+      S = sk.S;
+      tile = t0 + li / S;
+      split = li % S;
+    } else {
+      S = sk.S + 1;
+      tile = t0 + (nt - nh) + (li - n_long) / S;
+      split = (li - n_long) % S;
+    }
+  } else {
+    S = SK ? sk.S : 1;
+    const int total = tiles * S;
+    const int per = (total + 7) >> 3;
+    const int tid = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+    if (tid >= total) return;
+    tile = tid / S;
+    split = tid - tile * S;
+  }
   const int kbeg = split * KT / S, kend = (split + 1) * KT / S;
   {
     f32x16_t acc[TM][TN];
@@ -572,8 +615,17 @@ gemm_bf16_kernel(GemmArgs<bf16_t> p, SkArgs sk) {
 template <int MODE, bool DUAL, class TL, bool SK>
 static kvb_status launch_bf16(hipStream_t st, const GemmArgs<bf16_t>& p, const SkArgs& sk, const char* name) {
   constexpr int OUT_N = DUAL ? TL::BN / 2 : TL::BN;
-  const int total = cdiv(p.M_max, TL::BM) * cdiv(p.N, OUT_N) * (SK ? sk.S : 1);
-  dim3 grid(((total + 7) / 8) * 8);
+  const int tiles = cdiv(p.M_max, TL::BM) * cdiv(p.N, OUT_N);
+  int per = (tiles * (SK ? sk.S : 1) + 7) / 8;
+  if (SK && sk.xcd_blocks > 0) {
+    per = 0;
+    for (int x = 0; x < 8; x++) {
+      int t0, nt, nh;
+      mixed_run(tiles, x, sk.S, sk.xcd_blocks, t0, nt, nh);
+      per = std::max(per, (nt - nh) * sk.S + nh * (sk.S + 1));
+    }
+  }
+  dim3 grid(per * 8);
   {
     LaunchTimer lt(st, name);
     gemm_bf16_kernel<MODE, DUAL, TL, SK><<<grid, GEMM_THREADS, 0, st>>>(p, sk);
@@ -581,7 +633,7 @@ static kvb_status launch_bf16(hipStream_t st, const GemmArgs<bf16_t>& p, const S
   return check_launch("gemm_bf16_kernel");
 }
 
-// Sum of the S split-K partials in slice order, then the epilogue of MODE;
+// Sum of a tile's split-K partials in slice order, then the epilogue of MODE;
 // one thread per 8 consecutive output columns of a row.
 template <int MODE, bool DUAL>
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmArgs<bf16_t> p, SkArgs sk) {
@@ -590,8 +642,18 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmArgs<bf16_t> p, 
   const long c = (long)blockIdx.x * 256 + threadIdx.x;
   const int m = (int)(c / cpr), n = (int)(c % cpr) * 8;
   if (m >= M) return;
+  int S = sk.S;
+  if (sk.xcd_blocks > 0) {
+    // this element's tile and the run of the mixed plan it sits in
+    const int t = tile_index(m / sk.bm, n / sk.bn, sk.num_m, sk.num_n), tiles = sk.num_m * sk.num_n;
+    for (int x = 0; x < 8; x++) {
+      int t0, nt, nh;
+      mixed_run(tiles, x, sk.S, sk.xcd_blocks, t0, nt, nh);
+      if (t >= t0 && t < t0 + nt) S = sk.S + (t - t0 >= nt - nh ? 1 : 0);
+    }
+  }
   float v[8] = {}, u[8] = {};
-  for (int s = 0; s < sk.S; s++) {
+  for (int s = 0; s < S; s++) {
     const float* src = sk.part + ((size_t)s * sk.rows + m) * sk.cols + n;
     const float4 a = *reinterpret_cast<const float4*>(src), b = *reinterpret_cast<const float4*>(src + 4);
     v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w; v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
@@ -842,6 +904,23 @@ size_t ws_gemm_sk_bytes(int) { return SK_BUDGET; }
 // weights); whole waves of blocks run on the CUs; the launch takes at least
 // its unique operand bytes at 5 TB/s; split-K adds the reduction launch, which
 // reads the partials at 5 TB/s (their writes overlap the product's own work).
+// A mixed split (some tiles S slices, some S + 1, whole rounds of blocks per
+// XCD) is timed by placing each XCD's blocks in order on its CUs, each on the
+// CU that frees first; the slowest XCD sets the time.
+
+// time by which n_a blocks of length a, then n_b of length b, end on C CUs
+static double greedy_finish(int C, int n_a, double a, int n_b, double b) {
+  std::vector<double> cu(C, 0.0);
+  double end = 0.0;
+  for (int i = 0; i < n_a + n_b; i++) {
+    std::pop_heap(cu.begin(), cu.end(), std::greater<double>());
+    cu.back() += i < n_a ? a : b;
+    end = std::max(end, cu.back());
+    std::push_heap(cu.begin(), cu.end(), std::greater<double>());
+  }
+  return end;
+}
+
 template <int MODE, bool DUAL>
 static kvb_status run_bf16(hipStream_t st, const GemmArgs<bf16_t>& p, const char* name, void* sk_ws = nullptr) {
   if (p.M_max == 0 || p.N == 0) return KVB_OK;
@@ -861,33 +940,63 @@ static kvb_status run_bf16(hipStream_t st, const GemmArgs<bf16_t>& p, const char
                            {64, 256, 64, 0.5, 60e3, true}};
   const double cols = DUAL ? 2.0 * p.N : (double)p.N;
   const double hbm_us = (cols * p.K + (double)p.M_max * p.K) * 2.0 / 5e6;
-  int best_shape = -1, best_s = 1;
+  int best_shape = -1, best_s = 1, best_xb = 0;
   double best_t = 1e30;
   for (int si = 0; si < 5; si++) {
     const Shape& sh = shapes[si];
     if (p.K % sh.kb) continue;
     const long tiles = (long)cdiv(p.M_max, sh.bm) * cdiv(p.N, DUAL ? sh.bn / 2 : sh.bn);
     const int max_split = (sh.split && sk_ws && p.N % 8 == 0) ? 16 : 1;
+    auto blk_us = [&](int S) {
+      const double kk = (double)p.K / S;
+      return std::max(2.0 * sh.bm * sh.bn * kk / (4.5e6 * sh.eff), (sh.bm + sh.bn) * kk * 2.0 / sh.rate);
+    };
     for (int S = 1; S <= max_split && S <= p.K / sh.kb; S++) {
       if (S > 1 && (size_t)S * p.M_max * (size_t)cols * 4 > SK_BUDGET) break;
-      const double kk = (double)p.K / S;
-      const double blk_us = std::max(2.0 * sh.bm * sh.bn * kk / (4.5e6 * sh.eff), (sh.bm + sh.bn) * kk * 2.0 / sh.rate);
-      double tt = std::max((double)((tiles * S + cus - 1) / cus) * blk_us, hbm_us);
+      double tt = std::max((double)((tiles * S + cus - 1) / cus) * blk_us(S), hbm_us);
       if (S > 1) tt += (double)S * p.M_max * cols * 4 / 5e6 + 4.0;
       if (tt < best_t * (S > 1 ? 0.92 : 1.0)) {
         best_t = tt;
         best_shape = si;
         best_s = S;
+        best_xb = 0;
+      }
+      // mixed S / S + 1 filling the rounds the uniform S plan needs (up to 4)
+      const long rounds = (tiles * S + cus - 1) / cus;
+      if (S + 1 > max_split || S + 1 > p.K / sh.kb || cus % 8 || rounds > 4 || tiles < 8 ||
+          (size_t)(S + 1) * p.M_max * (size_t)cols * 4 > SK_BUDGET)
+        continue;
+      const int C = (int)(cus / 8), xb = (int)(rounds * C);
+      double mk = 0.0;
+      long extra = 0;
+      for (int x = 0; x < 8; x++) {
+        int t0, nt, nh;
+        mixed_run((int)tiles, x, S, xb, t0, nt, nh);
+        mk = std::max(mk, greedy_finish(C, (nt - nh) * S, blk_us(S), nh * (S + 1), blk_us(S + 1)));
+        extra += nh;
+      }
+      if (extra == 0) continue;
+      tt = std::max(mk, hbm_us) + (S + (double)extra / tiles) * p.M_max * cols * 4 / 5e6 + 4.0;
+      if (tt < best_t * 0.92) {
+        best_t = tt;
+        best_shape = si;
+        best_s = S;
+        best_xb = xb;
       }
     }
   }
   SkArgs sk{};
   sk.S = 1;
-  if (best_s > 1) {
+  if (best_s > 1 || best_xb > 0) {
     sk.S = best_s;
     sk.rows = p.M_max;  // partial row stride; only rows below the row count are written
     sk.cols = DUAL ? 2 * p.N : p.N;
     sk.part = (float*)sk_ws;
+    sk.xcd_blocks = best_xb;
+    sk.bm = shapes[best_shape].bm;
+    sk.bn = DUAL ? shapes[best_shape].bn / 2 : shapes[best_shape].bn;
+    sk.num_m = cdiv(p.M_max, sk.bm);
+    sk.num_n = cdiv(p.N, sk.bn);
     if (best_shape == 0) KVB_TRY((launch_bf16<MODE, DUAL, TileL, true>(st, p, sk, name)));
     else KVB_TRY((launch_bf16<MODE, DUAL, TileN, true>(st, p, sk, name)));
     return launch_splitk_reduce<MODE, DUAL>(st, p, sk, "splitk_reduce");
