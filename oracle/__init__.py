@@ -18,7 +18,8 @@ Modules:
 Every function is pinned by tests under tests/ (closed forms, special cases
 that reduce to library routines, brute force on tiny inputs, worked examples
 under tests/golden/).  Parts with no such pin are the readings marked there as
-"parity unpinned": the alpha lag order, the refresh direction, the hidden
-state of refilled tokens and the absence of key re-rotation.
+"parity unpinned": the alpha lag order and the refresh direction (the hidden
+state of refilled tokens is pinned by the hand-worked refresh schedule, the
+absence of key re-rotation by the layer-1 closed form).
 """
 from . import model, pages, select, link  # noqa: F401
