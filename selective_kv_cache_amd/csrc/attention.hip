@@ -943,9 +943,11 @@ extern "C" kvb_status kvb_sparse_query_attn(kvb_ctx* ctx, void* stream, const kv
     if (blocks > 0x7fffffffL) return fail(KVB_ERR_UNSUPPORTED, "attention grid too large");
     const dim3 grid((unsigned)blocks);
     {
-      LaunchTimer lt(st, "attention");
-      if (hd == 128) attn_bf16_kernel<128><<<grid, ATHREADS, 0, st>>>(a);
-      else attn_bf16_kernel<64><<<grid, ATHREADS, 0, st>>>(a);
+      LaunchTimer lt(st, "attention", true);
+      if (hd == 128)
+        hipExtLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(ATHREADS), 0, st, lt.start(), lt.stop(), 0, a);
+      else
+        hipExtLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(ATHREADS), 0, st, lt.start(), lt.stop(), 0, a);
     }
     KVB_TRY(check_launch("attn_bf16_kernel"));
     if (n_split > 1) KVB_TRY(launch_merge(st, hd, T_max, n_rows, Hq, n_split, a.part_o, a.part_ml, (bf16_t*)o));

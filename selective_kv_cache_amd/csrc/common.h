@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 #include <string.h>
 #include <math.h>
@@ -45,14 +46,21 @@ struct CtxScope {
   ~CtxScope();
 };
 
-// Bracket one kernel launch with timing events when the current context asks for it.
+// Bracket one kernel launch with timing events when the current context asks
+// for it.  By default the events are recorded on the stream before and after
+// the launch; with `ext` the launch itself records them (start and stop of
+// the dispatch, hipExtLaunchKernelGGL with start() and stop()), which puts no
+// marker between this kernel and its neighbours.
 struct LaunchTimer {
   Ctx* c = nullptr;
   hipStream_t st;
   const char* name;
-  hipEvent_t a = nullptr;
-  LaunchTimer(hipStream_t s, const char* n);
+  hipEvent_t a = nullptr, b = nullptr;
+  bool ext;
+  LaunchTimer(hipStream_t s, const char* n, bool ext = false);
   ~LaunchTimer();
+  hipEvent_t start() const { return ext ? a : nullptr; }
+  hipEvent_t stop() const { return ext ? b : nullptr; }
 };
 
 // Validates the model description; returns KVB_OK or an error with message.

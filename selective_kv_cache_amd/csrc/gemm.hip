@@ -627,8 +627,9 @@ static kvb_status launch_bf16(hipStream_t st, const GemmArgs<bf16_t>& p, const S
   }
   dim3 grid(per * 8);
   {
-    LaunchTimer lt(st, name);
-    gemm_bf16_kernel<MODE, DUAL, TL, SK><<<grid, GEMM_THREADS, 0, st>>>(p, sk);
+    LaunchTimer lt(st, name, true);
+    hipExtLaunchKernelGGL(gemm_bf16_kernel<MODE, DUAL, TL, SK>, grid, dim3(GEMM_THREADS), 0, st, lt.start(), lt.stop(),
+                          0, p, sk);
   }
   return check_launch("gemm_bf16_kernel");
 }
@@ -692,8 +693,9 @@ static kvb_status launch_splitk_reduce(hipStream_t st, const GemmArgs<bf16_t>& p
                                        const char* name) {
   const long n = (long)p.M_max * (p.N / 8);
   {
-    LaunchTimer lt(st, name);
-    splitk_reduce_kernel<MODE, DUAL><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(p, sk);
+    LaunchTimer lt(st, name, true);
+    hipExtLaunchKernelGGL(splitk_reduce_kernel<MODE, DUAL>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                          lt.start(), lt.stop(), 0, p, sk);
   }
   return check_launch("splitk_reduce_kernel");
 }
@@ -873,8 +875,9 @@ gemv_bf16_kernel(GemmArgs<bf16_t> p, RopeEpi re) {
 template <int MODE, bool DUAL, bool ROPE = false>
 static kvb_status launch_gemv(hipStream_t st, const GemmArgs<bf16_t>& p, const char* name, const RopeEpi& re = {}) {
   {
-    LaunchTimer lt(st, name);
-    gemv_bf16_kernel<MODE, DUAL, ROPE><<<cdiv(p.N, GV_NW * GV_WAVES), 64 * GV_WAVES, (size_t)p.K * 2, st>>>(p, re);
+    LaunchTimer lt(st, name, true);
+    hipExtLaunchKernelGGL(gemv_bf16_kernel<MODE, DUAL, ROPE>, dim3(cdiv(p.N, GV_NW * GV_WAVES)), dim3(64 * GV_WAVES),
+                          (uint32_t)((size_t)p.K * 2), st, lt.start(), lt.stop(), 0, p, re);
   }
   return check_launch("gemv_bf16_kernel");
 }

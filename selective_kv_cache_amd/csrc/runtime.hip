@@ -44,12 +44,23 @@ static hipEvent_t take_event(Ctx* c) {
   return e;
 }
 
-LaunchTimer::LaunchTimer(hipStream_t s, const char* n) : st(s), name(n) {
+LaunchTimer::LaunchTimer(hipStream_t s, const char* n, bool e) : st(s), name(n), ext(e) {
   Ctx* cur = g_current;
   if (!cur || !cur->timing) return;
   if (!cur->filter.empty() && std::string(n).find(cur->filter) == std::string::npos) return;
   a = take_event(cur);
   if (!a) return;
+  if (ext) {
+    // both events go to the launch, which records them
+    b = take_event(cur);
+    if (!b) {
+      cur->spare.push_back(a);
+      a = nullptr;
+      return;
+    }
+    c = cur;
+    return;
+  }
   if (hipEventRecord(a, st) != hipSuccess) {
     cur->spare.push_back(a);
     a = nullptr;
@@ -60,11 +71,13 @@ LaunchTimer::LaunchTimer(hipStream_t s, const char* n) : st(s), name(n) {
 
 LaunchTimer::~LaunchTimer() {
   if (!c) return;
-  hipEvent_t b = take_event(c);
-  if (!b || hipEventRecord(b, st) != hipSuccess) {
-    c->spare.push_back(a);
-    if (b) c->spare.push_back(b);
-    return;
+  if (!ext) {
+    b = take_event(c);
+    if (!b || hipEventRecord(b, st) != hipSuccess) {
+      c->spare.push_back(a);
+      if (b) c->spare.push_back(b);
+      return;
+    }
   }
   c->recs.push_back(TimingRec{name, a, b});
 }
