@@ -731,11 +731,18 @@ struct RopeEpi {
   RopeFreq rf;
 };
 
+// With NORM the row is RMS-normalised inside the product: while x is staged,
+// each thread adds the squares of its elements and stores x * gain (rounded
+// to bf16); the per-wave sums (in wave order) give 1 / rms, which scales the
+// dot products in the epilogue.  This is the normalised product up to the
+// rounding point of the scaled row, with no separate pass and no extra
+// barrier.  p.a_rows, if set, picks the row of A.
 // (at most 4 waves per SIMD: the registers for a whole batch of loads in flight)
-template <int MODE, bool DUAL, bool ROPE = false>
+template <int MODE, bool DUAL, bool ROPE = false, bool NORM = false>
 __global__ void __launch_bounds__(64 * GV_WAVES) __attribute__((amdgpu_waves_per_eu(1, 4)))
 gemv_bf16_kernel(GemmArgs<bf16_t> p, RopeEpi re) {
   static_assert(!ROPE || (MODE == EPI_QKV && !DUAL && GV_NW == 2), "RoPE pairs two Q/K/V outputs");
+  static_assert(!NORM || MODE == EPI_QKV || MODE == EPI_SWIGLU, "the norm precedes Q/K/V and SwiGLU products");
   extern __shared__ __align__(16) uint8_t gv_x[];
   if (row_count(p.n_rows, p.M_max) < 1) return;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -745,6 +752,7 @@ gemv_bf16_kernel(GemmArgs<bf16_t> p, RopeEpi re) {
   const int nb = ROPE ? (wg / (re.hd / 2)) * re.hd + wg % (re.hd / 2) : wg * GV_NW;
   const int nstep = ROPE ? re.hd / 2 : 1;
   constexpr int R = DUAL ? 2 * GV_NW : GV_NW;  // rows i < GV_NW: B; the rest: B2
+  constexpr int NB = 4;                        // 16-byte chunks per row in one batch of loads
   const uint4* wr[R];
 #pragma unroll
   for (int i = 0; i < GV_NW; i++) {
@@ -753,12 +761,14 @@ gemv_bf16_kernel(GemmArgs<bf16_t> p, RopeEpi re) {
     wr[i] = reinterpret_cast<const uint4*>(p.B + (size_t)n * p.K);
     if (DUAL) wr[GV_NW + i] = reinterpret_cast<const uint4*>(p.B2 + (size_t)n * p.K);
   }
-  // whole batches of 4 chunks per lane: all 4 R weight loads issued before
-  // any is used; then single chunks.  Streamed once: non-temporal, so the
-  // weights do not evict what the neighbouring launches keep in L2.
-  auto load_batch = [&](int c, uint4 (&w)[4][R]) {
+  // batches of NB chunks per lane: all NB R weight loads of a batch issued
+  // before any is used (eight chunks a batch ran 1 % slower over a decode
+  // step); a lane adds its chunks in index order whatever the batching.
+  // Streamed once: non-temporal, so the weights do not evict what the
+  // neighbouring launches keep in L2.
+  auto load_batch = [&](int c, uint4 (&w)[NB][R]) {
 #pragma unroll
-    for (int u = 0; u < 4; u++)
+    for (int u = 0; u < NB; u++)
 #pragma unroll
       for (int i = 0; i < R; i++) {
         const u32x4_t q = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(&wr[i][c + 64 * u]));
@@ -768,13 +778,45 @@ gemv_bf16_kernel(GemmArgs<bf16_t> p, RopeEpi re) {
   // the first batch is issued before x is staged: the weight stream does not
   // wait for the staging and its barrier
   const bool active = ROPE ? 2 * wg < p.N : nb < p.N;
-  const bool first = active && lane + 192 < C;
-  uint4 w0[4][R];
+  const bool first = active && lane + 64 * (NB - 1) < C;
+  uint4 w0[NB][R];
   if (first) load_batch(lane, w0);
 
-  const uint4* xg = reinterpret_cast<const uint4*>(p.A);
+  const uint4* xg = reinterpret_cast<const uint4*>(p.A + (p.a_rows ? (size_t)p.a_rows[0] * p.K : 0));
   uint4* xs = reinterpret_cast<uint4*>(gv_x);
-  {
+  float* red = reinterpret_cast<float*>(gv_x + (size_t)p.K * 2);  // NORM: the waves' sums of squares
+  if constexpr (NORM) {
+    // two chunks (and their gains) in flight per thread; squares in element order
+    constexpr int TH = 64 * GV_WAVES;
+    const uint4* gg = reinterpret_cast<const uint4*>(p.norm_w);
+    float ss = 0.f;
+    auto put = [&](int c, const uint4& v, const uint4& w) {
+      float f[8], gf[8];
+      unpack8(v, f);
+      unpack8(w, gf);
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        ss += f[e] * f[e];
+        f[e] *= gf[e];
+      }
+      xs[c] = make_uint4(pack2_bf16(f[0], f[1]), pack2_bf16(f[2], f[3]), pack2_bf16(f[4], f[5]),
+                         pack2_bf16(f[6], f[7]));
+    };
+    const uint4 one = make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);  // bf16 1.0 pairs
+    for (int c = t; c < C; c += 2 * TH) {
+      const bool two = c + TH < C;
+      const uint4 v0 = xg[c], g0 = gg ? gg[c] : one;
+      uint4 v1 = one, g1 = one;
+      if (two) {
+        v1 = xg[c + TH];
+        g1 = gg ? gg[c + TH] : one;
+      }
+      put(c, v0, g0);
+      if (two) put(c + TH, v1, g1);
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) red[wave] = ss;
+  } else {
     // four 16-byte loads in flight per thread, then the tail
     constexpr int TH = 64 * GV_WAVES;
     int c = t;
@@ -792,9 +834,9 @@ gemv_bf16_kernel(GemmArgs<bf16_t> p, RopeEpi re) {
   float acc[R];
 #pragma unroll
   for (int i = 0; i < R; i++) acc[i] = 0.f;
-  auto use_batch = [&](int c, const uint4 (&w)[4][R]) {
+  auto use_batch = [&](int c, const uint4 (&w)[NB][R]) {
 #pragma unroll
-    for (int u = 0; u < 4; u++) {
+    for (int u = 0; u < NB; u++) {
       const uint4 xv = xs[c + 64 * u];
 #pragma unroll
       for (int i = 0; i < R; i++) acc[i] = dot8_bf16(w[u][i], xv, acc[i]);
@@ -803,24 +845,47 @@ gemv_bf16_kernel(GemmArgs<bf16_t> p, RopeEpi re) {
   int c = lane;
   if (first) {
     use_batch(c, w0);
-    c += 256;
+    c += 64 * NB;
   }
-  for (; c + 192 < C; c += 256) {
-    uint4 w[4][R];
+  for (; c + 64 * (NB - 1) < C; c += 64 * NB) {
+    uint4 w[NB][R];
     load_batch(c, w);
-    __builtin_amdgcn_sched_group_barrier(0x020, 4 * R, 0);  // every weight load of the batch first
+    __builtin_amdgcn_sched_group_barrier(0x020, NB * R, 0);  // every weight load of the batch first
     use_batch(c, w);
   }
-  for (; c < C; c += 64) {
-    const uint4 xv = xs[c];
+  if (c < C) {
+    // the last, partial batch: its chunks below C, all loads again before any use
+    uint4 w[NB][R];
 #pragma unroll
-    for (int i = 0; i < R; i++) acc[i] = dot8_bf16(wr[i][c], xv, acc[i]);
+    for (int u = 0; u < NB; u++)
+      if (c + 64 * u < C) {
+#pragma unroll
+        for (int i = 0; i < R; i++) {
+          const u32x4_t q = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(&wr[i][c + 64 * u]));
+          w[u][i] = make_uint4(q.x, q.y, q.z, q.w);
+        }
+      }
+#pragma unroll
+    for (int u = 0; u < NB; u++)
+      if (c + 64 * u < C) {
+        const uint4 xv = xs[c + 64 * u];
+#pragma unroll
+        for (int i = 0; i < R; i++) acc[i] = dot8_bf16(w[u][i], xv, acc[i]);
+      }
+  }
+  float rs = 1.f;  // NORM: 1 / rms of the row
+  if constexpr (NORM) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < GV_WAVES; w++) s += red[w];
+    rs = 1.f / sqrtf(s / (float)p.K + p.eps);
   }
   if constexpr (ROPE) {
     // both sums in every lane; lane 0 stores the low half of the pair, lane 1
     // the high half.  Each value is first rounded to bf16, as the product
     // stores it, then rotated (Q, K) and rounded again, as the RoPE pass does.
-    const float x0 = bf2f(f2bf(wave_sum(acc[0]))), x1 = bf2f(f2bf(wave_sum(acc[1])));
+    const float x0 = bf2f(f2bf(NORM ? wave_sum(acc[0]) * rs : wave_sum(acc[0])));
+    const float x1 = bf2f(f2bf(NORM ? wave_sum(acc[1]) * rs : wave_sum(acc[1])));
     if (lane >= 2) return;
     const int n = nb + lane * nstep;
     float y = lane == 0 ? x0 : x1;
@@ -846,8 +911,12 @@ gemv_bf16_kernel(GemmArgs<bf16_t> p, RopeEpi re) {
   float v = 0.f, v2 = 0.f;
 #pragma unroll
   for (int i = 0; i < GV_NW; i++) {
-    const float a = wave_sum(acc[i]);
-    const float b = DUAL ? wave_sum(acc[GV_NW + i]) : 0.f;
+    float a = wave_sum(acc[i]);
+    float b = DUAL ? wave_sum(acc[GV_NW + i]) : 0.f;
+    if constexpr (NORM) {
+      a *= rs;
+      b *= rs;
+    }
     if (lane == i) {
       v = a;
       v2 = b;
@@ -872,12 +941,16 @@ gemv_bf16_kernel(GemmArgs<bf16_t> p, RopeEpi re) {
   *dst = (bf16_t)(pack2_bf16(v, 0.f) & 0xffffu);
 }
 
-template <int MODE, bool DUAL, bool ROPE = false>
+// the one-row product takes the row whole into LDS
+static bool gemv_ok(const GemmArgs<bf16_t>& p) { return p.M_max == 1 && p.K % 8 == 0 && p.K <= 32768; }
+
+template <int MODE, bool DUAL, bool ROPE = false, bool NORM = false>
 static kvb_status launch_gemv(hipStream_t st, const GemmArgs<bf16_t>& p, const char* name, const RopeEpi& re = {}) {
   {
     LaunchTimer lt(st, name, true);
-    hipExtLaunchKernelGGL(gemv_bf16_kernel<MODE, DUAL, ROPE>, dim3(cdiv(p.N, GV_NW * GV_WAVES)), dim3(64 * GV_WAVES),
-                          (uint32_t)((size_t)p.K * 2), st, lt.start(), lt.stop(), 0, p, re);
+    hipExtLaunchKernelGGL(gemv_bf16_kernel<MODE, DUAL, ROPE, NORM>, dim3(cdiv(p.N, GV_NW * GV_WAVES)),
+                          dim3(64 * GV_WAVES), (uint32_t)((size_t)p.K * 2 + (NORM ? 4 * GV_WAVES : 0)), st,
+                          lt.start(), lt.stop(), 0, p, re);
   }
   return check_launch("gemv_bf16_kernel");
 }
@@ -932,7 +1005,7 @@ static kvb_status run_bf16(hipStream_t st, const GemmArgs<bf16_t>& p, const char
   if (p.a_rows || (size_t)p.M_max * p.K * 2 > 0xffffffffu || b_span > 0xffffffffu)
     return fail(KVB_ERR_UNSUPPORTED, std::string(name) + ": operands beyond 4 GiB of one base");
   // one row on a launch that may split K: the weight-streaming product
-  if (sk_ws && p.M_max == 1 && p.K % 8 == 0 && p.K <= 32768) return launch_gemv<MODE, DUAL>(st, p, name);
+  if (sk_ws && gemv_ok(p)) return launch_gemv<MODE, DUAL>(st, p, name);
   Ctx* c = current_ctx();
   const long cus = c ? c->n_cu : 256;
   struct Shape { int bm, bn, kb; double eff, rate; bool split; };
@@ -1129,6 +1202,15 @@ static kvb_status qkv_impl(hipStream_t st, const kvb_model_desc* d, int T_max, c
   p.out1 = (T*)k;
   p.out2 = (T*)v;
   if constexpr (sizeof(T) == 2) {
+    if (split_k && T_max == 1 && gemv_ok(p)) {
+      // one row: the norm inside the weight-streaming product
+      p.A = (const T*)hidden;
+      p.a_rows = row_tok;
+      p.norm_w = (const T*)norm_w;
+      KVB_TRY((launch_gemv<EPI_QKV, false, false, true>(st, p, "gemm_qkv")));
+      if (tok_pos) return launch_rope<T>(st, T_max, n_rows, row_tok, tok_pos, q, k, d);
+      return KVB_OK;
+    }
     // normalised rows a [T, d] in workspace, then a plain GEMM
     bf16_t* a = (bf16_t*)ws;
     KVB_TRY(rmsnorm_rows(st, (const bf16_t*)hidden, row_tok, n_rows, T_max, d->d_model, (const bf16_t*)norm_w,
@@ -1163,9 +1245,10 @@ kvb_status qkv_rope_one_row(hipStream_t st, const kvb_model_desc* d, const int32
   p.out0 = (bf16_t*)q;
   p.out1 = (bf16_t*)k;
   p.out2 = (bf16_t*)v;
-  bf16_t* a = (bf16_t*)ws;  // the normalised row
-  KVB_TRY(rmsnorm_rows(st, (const bf16_t*)hidden, row_tok, n_rows, 1, d->d_model, (const bf16_t*)norm_w, d->rms_eps, a));
-  p.A = a;
+  (void)ws;
+  p.A = (const bf16_t*)hidden;  // normalised inside the product
+  p.a_rows = row_tok;
+  p.norm_w = (const bf16_t*)norm_w;
   RopeEpi re{};
   re.tok_pos = tok_pos;
   re.row_tok = row_tok;
@@ -1176,7 +1259,7 @@ kvb_status qkv_rope_one_row(hipStream_t st, const kvb_model_desc* d, const int32
   re.Hkv = d->n_kv_heads;
   re.hd = d->head_dim;
   re.rf = rope_freq(d->head_dim, d->rope_base);
-  return launch_gemv<EPI_QKV, false, true>(st, p, "gemm_qkv", re);
+  return launch_gemv<EPI_QKV, false, true, true>(st, p, "gemm_qkv", re);
 }
 
 template <class T>
@@ -1231,6 +1314,11 @@ static kvb_status mlp_impl(hipStream_t st, const kvb_model_desc* d, int T_max, c
   c.out_rows = row_tok;
   if constexpr (sizeof(T) == 2) {
     KVB_TRY((run_bf16<EPI_RESID, false>(st, a, "gemm_oproj", sk_ws)));
+    if (gemv_ok(b)) {
+      // one row: the norm inside the weight-streaming product
+      KVB_TRY((launch_gemv<EPI_SWIGLU, true, false, true>(st, b, "gemm_swiglu")));
+      return run_bf16<EPI_SCATTER, false>(st, c, "gemm_down", sk_ws);
+    }
     KVB_TRY(rmsnorm_rows(st, h1, nullptr, n_rows, T_max, D, (const bf16_t*)norm2_w, d->rms_eps, hn));
     b.A = hn;
     b.norm_w = nullptr;
