@@ -395,6 +395,89 @@ kvb_status kvb_page_dirty_add(kvb_ctx* ctx, void* stream, const kvb_model_desc* 
                               const int32_t* n_rows, const int32_t* slots, int32_t n_pages,
                               int32_t* page_dirty);
 
+/* ------------------------------------------------------ the whole link step */
+
+/* Weights of one layer (device pointers, storage type desc->dtype). */
+typedef struct kvb_layer_weights {
+  const void* norm1;      /* [d] RMSNorm gain before Q/K/V */
+  const void* w_qkv;      /* [(Hq + 2 Hkv) hd, d] */
+  const void* w_o;        /* [d, Hq hd] */
+  const void* norm2;      /* [d] RMSNorm gain before the MLP */
+  const void* w_gate_up;  /* [2 F, d]: gate rows, then up rows */
+  const void* w_down;     /* [d, F] */
+} kvb_layer_weights;
+
+#define KVB_LINK_CACHESLIDE 0  /* layer 1 in full, deviation top-k, fusion and refresh in layers 2..L */
+#define KVB_LINK_STATIC 1      /* a fixed row set recomputed in every layer, replacing the cached K/V */
+
+/* Everything one link step reads and writes.  Sizes: N = n_tok, L = n_layers,
+ * B = requests; device pointers unless marked host. */
+typedef struct kvb_link_desc {
+  int32_t mode;           /* KVB_LINK_CACHESLIDE or KVB_LINK_STATIC */
+  int32_t B, n_tok, n_layers, n_pages, vocab;
+  int32_t rows;           /* row bound of layers 2..L: the sum of the per-request k
+                           * (CacheSlide), or the size of the static row set */
+  int32_t period;         /* CacheSlide: refresh after layer l when l % period == 0 and l < L */
+  int32_t refresh_rule;   /* KVB_REFRESH_LITERAL or KVB_REFRESH_DISSIM */
+  int32_t alpha_mode;     /* CacheSlide fusion of layers 2..L: KVB_ALPHA_LAG / _CURRENT / _ONE */
+  float tau;              /* refresh threshold */
+  float scale;            /* attention scale, 1 / sqrt(hd) */
+  const kvb_layer_weights* layers;     /* host [L] */
+  const void* embedding;               /* [vocab, d] */
+  const int32_t* tokens;               /* [N] vocabulary ids */
+  const int32_t* pos;                  /* [N] RoPE positions in the spliced requests */
+  const int32_t* lo;                   /* [N] first visible key (start of the request) */
+  const int32_t* cu_tok;               /* [B + 1] */
+  const int32_t* k_cap;                /* [B] CacheSlide k per request (NULL for static) */
+  const int32_t* reuse_slot;           /* [L, N] slot of each token's compiled K/V, or -1 */
+  const int32_t* const* new_pages;     /* host [L]: layer l + 1's new page ids (device) */
+  const int32_t* const* cu_pages;      /* host [L]: its per-request offsets [B + 1] (device) */
+  const int32_t* static_rows;          /* static: [rows] tokens, ascending within a request */
+  const int32_t* static_cu;            /* static: [B + 1] row offsets of the requests */
+  int32_t* page_table;                 /* [L, N] out: slot of every token's K/V per layer */
+  void* k_pool;                        /* [n_pages, Hkv, 16, hd] in/out */
+  void* v_pool;
+  void* hidden;                        /* [N, d] out: hidden rows of the recomputed tokens */
+  void* q;                             /* [N, Hq, hd] scratch */
+  void* k;                             /* [N, Hkv, hd] scratch */
+  void* v;                             /* [N, Hkv, hd] scratch */
+  void* o;                             /* [N, Hq hd] scratch */
+  float* d;                            /* [N] CacheSlide layer-1 deviation */
+  float* alpha;                        /* [N] CacheSlide fusion weights */
+  float* dev;                          /* [rows] per-row deviation of the current layer */
+  float* cksim;                        /* [rows] per-row cosine similarity of a refresh layer */
+  int32_t* ranking;                    /* [N] */
+  int32_t* s_count;                    /* [B] */
+  int32_t* cursor;                     /* [B] */
+  int32_t* sel[2];                     /* [N] each: the selection, ping-pong across refreshes */
+  int32_t* cu_rows[2];                 /* [B + 1] each */
+  int32_t* dst_slot;                   /* [N] scratch */
+  int32_t* page_dirty;                 /* [n_pages] SLIDE dirty counters, cleared here; or NULL */
+  void* ws;                            /* workspace of kvb_workspace_size(max_rows >= N, max_tokens >= N, B) */
+  size_t ws_bytes;
+} kvb_link_desc;
+
+/* The whole link step as one call: the layer loop of CacheSlide's Algorithm 2
+ * (CacheSlide page, "Method details" and Algorithm 2: layer 1 recomputes
+ * every token, the deviation ranks them and the top-k are recomputed in
+ * layers 2..L, fused with the cached K/V, with the cosine refresh every
+ * `period` layers) or of EPIC's LegoLink (EPIC page, section 4: the static
+ * set recomputed in every layer), built from the calls above in the order a
+ * caller would make them: per layer kvb_slot_map, kvb_qkv_fused (layer 1
+ * batch-invariant, later layers allowed to split K), the refresh right after
+ * the fusion when the layer has one, kvb_sparse_query_attn, kvb_mlp.
+ * Nothing is read back to the host: every selective layer is launched for
+ * link->rows rows and the device row counts bound the work, so the call
+ * queues the step without a host synchronisation and can be recorded in a
+ * HIP graph (the counters are cleared by a kernel, not a memset).  Results
+ * are bitwise those of the same calls made one by one with these bounds.
+ * *final_sel (host, may be NULL) receives which selection buffer holds the
+ * set after the last layer.  Every argument is checked before anything is
+ * queued; a HIP launch error returns KVB_ERR_HIP with the earlier steps
+ * already queued. */
+kvb_status kvb_link_run(kvb_ctx* ctx, void* stream, const kvb_model_desc* desc, const kvb_link_desc* link,
+                        int32_t* final_sel);
+
 #ifdef __cplusplus
 }
 #endif

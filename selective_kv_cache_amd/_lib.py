@@ -26,6 +26,7 @@ KVB_REFRESH_LITERAL, KVB_REFRESH_DISSIM = 0, 1
 KVB_COPY_H2D, KVB_COPY_D2H = 0, 1
 KVB_QKV_BATCH_INVARIANT, KVB_QKV_SPLIT_K = 0, 1
 KVB_NOALLOC_MAX_TOKENS, KVB_NOALLOC_MAX_REQUESTS = 131072, 4096
+KVB_LINK_CACHESLIDE, KVB_LINK_STATIC = 0, 1
 
 
 class KvbError(RuntimeError):
@@ -38,6 +39,26 @@ class kvb_model_desc(ctypes.Structure):
     _fields_ = [("d_model", c_int32), ("n_q_heads", c_int32), ("n_kv_heads", c_int32),
                 ("head_dim", c_int32), ("ffn", c_int32), ("page_size", c_int32),
                 ("rope_base", c_float), ("rms_eps", c_float), ("dtype", c_int32)]
+
+
+class kvb_layer_weights(ctypes.Structure):
+    _fields_ = [("norm1", c_void_p), ("w_qkv", c_void_p), ("w_o", c_void_p), ("norm2", c_void_p),
+                ("w_gate_up", c_void_p), ("w_down", c_void_p)]
+
+
+class kvb_link_desc(ctypes.Structure):
+    _fields_ = [("mode", c_int32), ("B", c_int32), ("n_tok", c_int32), ("n_layers", c_int32),
+                ("n_pages", c_int32), ("vocab", c_int32), ("rows", c_int32), ("period", c_int32),
+                ("refresh_rule", c_int32), ("alpha_mode", c_int32), ("tau", c_float), ("scale", c_float),
+                ("layers", c_void_p), ("embedding", c_void_p), ("tokens", c_void_p), ("pos", c_void_p),
+                ("lo", c_void_p), ("cu_tok", c_void_p), ("k_cap", c_void_p), ("reuse_slot", c_void_p),
+                ("new_pages", c_void_p), ("cu_pages", c_void_p), ("static_rows", c_void_p),
+                ("static_cu", c_void_p), ("page_table", c_void_p), ("k_pool", c_void_p), ("v_pool", c_void_p),
+                ("hidden", c_void_p), ("q", c_void_p), ("k", c_void_p), ("v", c_void_p), ("o", c_void_p),
+                ("d", c_void_p), ("alpha", c_void_p), ("dev", c_void_p), ("cksim", c_void_p),
+                ("ranking", c_void_p), ("s_count", c_void_p), ("cursor", c_void_p), ("sel", c_void_p * 2),
+                ("cu_rows", c_void_p * 2), ("dst_slot", c_void_p), ("page_dirty", c_void_p), ("ws", c_void_p),
+                ("ws_bytes", c_size_t)]
 
 
 P = c_void_p
@@ -70,6 +91,7 @@ _SIGS = {
     "kvb_cosine_refresh": ([P, P, P, I, I, P, I, P, P, P, c_float, I, P, P, P, P, P, P, c_size_t], I),
     "kvb_slot_map": ([P, P, P, I, I, I, P, P, P, P, P, P, P, I, P], I),
     "kvb_page_dirty_add": ([P, P, P, I, P, P, I, P], I),
+    "kvb_link_run": ([P, P, P, P, P], I),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -290,3 +312,11 @@ def kvb_slot_map(ctx, stream, desc, B, n_tok, T_max, cu_rows, row_tok, reuse_slo
 
 def kvb_page_dirty_add(ctx, stream, desc, T_max, n_rows, slots, n_pages, page_dirty):
     _call("kvb_page_dirty_add", ctx, stream, desc, T_max, n_rows, slots, n_pages, page_dirty)
+
+
+def kvb_link_run(ctx, stream, desc, link) -> int:
+    """Queue a whole link step described by `link` (a kvb_link_desc); returns
+    which selection buffer holds the set after the last layer."""
+    out = c_int32(0)
+    _call("kvb_link_run", ctx, stream, desc, link, ctypes.addressof(out))
+    return int(out.value)

@@ -21,6 +21,7 @@ every layer (LegoLink).  An uncached query chunk has no compile pages.
 """
 from __future__ import annotations
 
+import ctypes
 import math
 from dataclasses import dataclass
 from typing import Callable, List, Optional
@@ -414,6 +415,52 @@ class LinkEngine:
         else:
             self._link_static(hook)
         self._tier_end()
+
+    def link_desc(self) -> "K.kvb_link_desc":
+        """The kvb_link_desc of this engine's link step (CacheSlide or LegoLink;
+        the reused cache resident in the pool).  The host arrays it points to
+        are kept on the engine."""
+        if self.cfg.mode not in ("cacheslide", "legolink"):
+            raise ValueError("kvb_link_run covers the CacheSlide and LegoLink link steps")
+        if self.cfg.reuse_tier != "hbm":
+            raise ValueError("kvb_link_run reads the reused cache from the device pool")
+        L, cs = self.L, self.cfg.mode == "cacheslide"
+        lw = (K.kvb_layer_weights * L)()
+        for i, W in enumerate(self.model.layers):
+            lw[i] = K.kvb_layer_weights(W["norm1"].data_ptr(), W["w_qkv"].data_ptr(), W["w_o"].data_ptr(),
+                                        W["norm2"].data_ptr(), W["w_gate_up"].data_ptr(), W["w_down"].data_ptr())
+        npg = (ctypes.c_void_p * L)(*[self.new_pages[l].data_ptr() for l in range(1, L + 1)])
+        cpg = (ctypes.c_void_p * L)(*[self.cu_pages[l].data_ptr() for l in range(1, L + 1)])
+        self._link_host = (lw, npg, cpg)
+        t = lambda x: x.data_ptr() if x is not None else None
+        k = K.kvb_link_desc()
+        k.mode = K.KVB_LINK_CACHESLIDE if cs else K.KVB_LINK_STATIC
+        k.B, k.n_tok, k.n_layers, k.n_pages, k.vocab = self.B, self.N, L, self.n_pages, self.shape.vocab
+        k.rows, k.period, k.refresh_rule, k.alpha_mode = self.T_sel, self.cfg.period, self.cfg.refresh_rule, \
+            self.cfg.alpha_mode
+        k.tau, k.scale = float(self.cfg.tau), float(self.scale)
+        k.layers = ctypes.addressof(lw)
+        k.embedding, k.tokens, k.pos, k.lo = t(self.model.embedding), t(self.tok_l), t(self.pos_l), t(self.lo_l)
+        k.cu_tok, k.k_cap, k.reuse_slot = t(self.cu_tok), t(self.k_cap_d) if cs else None, t(self.reuse_slot)
+        k.new_pages, k.cu_pages = ctypes.addressof(npg), ctypes.addressof(cpg)
+        if not cs:
+            k.static_rows, k.static_cu = t(self.lego_sel), t(self.lego_cu)
+        k.page_table, k.k_pool, k.v_pool, k.hidden = t(self.page_table), t(self.k_pool), t(self.v_pool), t(self.hidden)
+        k.q, k.k, k.v, k.o = t(self.q), t(self.k), t(self.v), t(self.o)
+        k.d, k.alpha, k.dev, k.cksim = t(self.d), t(self.alpha), t(self.dev_l), t(self.cksim)
+        k.ranking, k.s_count, k.cursor = t(self.ranking), t(self.s_count), t(self.cursor)
+        k.sel[0], k.sel[1] = t(self.sel[0]), t(self.sel[1])
+        k.cu_rows[0], k.cu_rows[1] = t(self.cu_rows[0]), t(self.cu_rows[1])
+        k.dst_slot, k.page_dirty, k.ws, k.ws_bytes = t(self.dst_slot), t(self.page_dirty), t(self.ws), self.ws_bytes
+        return k
+
+    def run_link_native(self, link_desc=None):
+        """The link step as one library call (kvb_link_run): the same steps as
+        run_link with exact_rows=False, queued by the library's C++ layer loop
+        with no host synchronisation (so it can be recorded in a HIP graph)."""
+        k = link_desc if link_desc is not None else self.link_desc()
+        self._pt_reuse_rows = set()
+        self.cur = K.kvb_link_run(self.ctx, self.sh, self.desc, k)
 
     def _layer_rows(self, l, T, n_rows, rows, cu_rows, src_slot, alpha_mode, alpha, d_out, cksim_out,
                     after_blend=None):

@@ -202,3 +202,68 @@ def test_host_spill_order_matches_oracle(rng):
         counts = rng.integers(0, 4, n) * (rng.random(n) > 0.4)
         pages = rng.choice(n, int(rng.integers(0, n + 1)), replace=False)
         assert spill_order(counts, pages) == OP.spill_order(counts, pages)
+
+
+LINK_FIELDS = [f for f, _ in K.kvb_link_desc._fields_]
+
+
+def test_link_desc_layout_matches_header(tmp_path):
+    """The ctypes kvb_link_desc and kvb_layer_weights have the C structs' size and offsets."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    fields = [f if f not in ("sel", "cu_rows") else f + "[1]" for f in LINK_FIELDS]
+    lines = [f'  printf("%zu\\n", offsetof(kvb_link_desc, {f}));' for f in fields]
+    lines += ['  printf("%zu\\n", sizeof(kvb_link_desc));', '  printf("%zu\\n", sizeof(kvb_layer_weights));',
+              '  printf("%zu\\n", offsetof(kvb_layer_weights, w_down));']
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "kvb.h"\nint main(void) {\n'
+                   + "\n".join(lines) + "\n  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    want = [getattr(K.kvb_link_desc, f).offset + (8 if f in ("sel", "cu_rows") else 0) for f in LINK_FIELDS]
+    want += [ctypes.sizeof(K.kvb_link_desc), ctypes.sizeof(K.kvb_layer_weights), K.kvb_layer_weights.w_down.offset]
+    assert got == want
+
+
+def test_link_run_checks(lib):
+    """kvb_link_run refuses a missing or inconsistent description before queuing anything."""
+    d = _desc()
+    with pytest.raises(K.KvbError) as e:
+        K._call("kvb_link_run", FAKE_CTX, None, d, None, None)
+    assert e.value.status == K.KVB_ERR_INVALID_ARG and "link" in K.kvb_last_error()
+    k = K.kvb_link_desc()
+    k.mode, k.B, k.n_tok, k.n_layers, k.n_pages, k.vocab, k.rows, k.period = 0, 1, 64, 2, 8, 100, 16, 4
+    with pytest.raises(K.KvbError) as e:
+        K.kvb_link_run(FAKE_CTX, None, d, k)
+    assert e.value.status == K.KVB_ERR_INVALID_ARG and "layers" in K.kvb_last_error()
+    lw = (K.kvb_layer_weights * 2)(K.kvb_layer_weights(1, 1, 1, 1, 1, 1), K.kvb_layer_weights(1, 1, 1, 1, 1, None))
+    k.layers = ctypes.addressof(lw)
+    with pytest.raises(K.KvbError) as e:
+        K.kvb_link_run(FAKE_CTX, None, d, k)
+    assert e.value.status == K.KVB_ERR_INVALID_ARG and "layer 2" in K.kvb_last_error()
+    lw[1] = K.kvb_layer_weights(1, 1, 1, 1, 1, 1)
+    pages = (ctypes.c_void_p * 2)(1, 1)
+    k.new_pages = k.cu_pages = ctypes.addressof(pages)
+    for f in ("embedding", "tokens", "pos", "lo", "cu_tok", "k_cap", "reuse_slot", "page_table", "k_pool",
+              "v_pool", "hidden", "q", "k", "v", "o", "d", "alpha", "dev", "cksim", "ranking", "s_count", "cursor",
+              "dst_slot"):
+        setattr(k, f, 1)
+    k.sel[0], k.sel[1], k.cu_rows[0], k.cu_rows[1] = 1, 1, 2, 3
+    with pytest.raises(K.KvbError) as e:  # one selection buffer for both
+        K.kvb_link_run(FAKE_CTX, None, d, k)
+    assert e.value.status == K.KVB_ERR_INVALID_ARG and "differ" in K.kvb_last_error()
+    k.sel[1] = 5
+    for bad in (dict(mode=3), dict(rows=65), dict(period=0), dict(refresh_rule=4), dict(alpha_mode=9)):
+        k2 = K.kvb_link_desc.from_buffer_copy(k)
+        for f, v in bad.items():
+            setattr(k2, f, v)
+        with pytest.raises(K.KvbError) as e:
+            K.kvb_link_run(FAKE_CTX, None, d, k2)
+        assert e.value.status == K.KVB_ERR_INVALID_ARG, bad
+    with pytest.raises(K.KvbError) as e:  # everything set but the workspace
+        K.kvb_link_run(FAKE_CTX, None, d, k)
+    assert e.value.status == K.KVB_ERR_WORKSPACE
