@@ -43,6 +43,7 @@ def parse():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode continuation leg")
     ap.add_argument("--no-cacheblend", action="store_true", help="skip the CacheBlend-style selection leg")
     ap.add_argument("--no-sustained", action="store_true", help="skip the sustained-set leg")
+    ap.add_argument("--no-native", action="store_true", help="skip the leg timing the library's own layer loop")
     ap.add_argument("--rule", choices=["literal", "dissim"], default="literal",
                     help="retire rule of the timed step (dissim: the set stays at k on these weights)")
     ap.add_argument("--profile-only", action="store_true", help="warmup + timed steps only (for rocprofv3)")
@@ -187,6 +188,51 @@ def sustained_leg(eng, args, st, s):
             "kernels": per_kernel_rates(breakdown, work),
             "note": "retire when CKSim > 1 - tau: no token retires on these weights, so every layer recomputes "
                     "the layer-1 selection; same engine, weights and compiled cache as the headline step"}
+
+
+def native_loop_leg(eng, args, st, n_selected):
+    """The same link step queued by the library's C++ layer loop (kvb_link_run):
+    no host synchronisation inside the step, every selective layer launched for
+    the layer-1 selection's size (the device row counts bound the work).  Timed
+    with HIP events on the engine stream, eagerly and as a replayed HIP graph."""
+    import numpy as np
+    import torch
+
+    from selective_kv_cache_amd import _lib as K
+
+    k = eng.link_desc()
+
+    def timed(fn):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for a, b in ev:
+            a.record(st)
+            fn()
+            b.record(st)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+
+    for _ in range(args.warmup):
+        eng.run_link_native(k)
+    eager = timed(lambda: eng.run_link_native(k))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        K.kvb_link_run(eng.ctx, K.stream_handle(torch.cuda.current_stream()), eng.desc, k)
+
+    def replay():
+        with torch.cuda.stream(st):
+            g.replay()
+
+    replay()
+    torch.cuda.synchronize()
+    graph = timed(replay)
+    del g
+    ms_e, ms_g = float(np.mean(eager)), float(np.mean(graph))
+    return {"ms_per_step": ms_e, "ms_per_step_graph": ms_g,
+            "selected_tokens_per_s": n_selected / (ms_e * 1e-3),
+            "selected_tokens_per_s_graph": n_selected / (ms_g * 1e-3),
+            "note": "kvb_link_run: one library call per step, every selective layer launched for the layer-1 "
+                    "selection's size with device row counts, no host readback; eager and HIP graph replay"}
 
 
 BOUND = {"gemm_qkv": "mfma", "gemm_oproj": "mfma", "gemm_swiglu": "mfma", "gemm_down": "mfma", "attention": "mfma",
@@ -572,6 +618,8 @@ def main():
     }
     if cfg.mode == "cacheslide" and not args.no_sustained:
         out["sustained"] = sustained_leg(eng, args, st, s)
+    if cfg.mode in ("cacheslide", "legolink") and not args.no_native:
+        out["native_loop"] = native_loop_leg(eng, args, st, n_selected)
     if not args.no_decode:
         out["decode"] = decode_leg(eng, st)
     if cfg.mode == "cacheslide":
