@@ -144,3 +144,23 @@ def test_link_run_nothing_selected():
     assert_same(ref, got)
     assert sum(len(x) for x in got["selected"]) == 0
     eng.close()
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("make", [wl.mistral_cacheslide, wl.mistral_legolink], ids=["cacheslide-8k", "legolink-16k"])
+def test_link_run_fullsize(make):
+    """At the benchmark sizes (the Mistral-shaped 8192-token CacheSlide request
+    and the 16384-token LegoLink prompt, bf16, 32 layers) the library's loop is
+    bitwise the per-call loop with device row counts."""
+    w = make()
+    eng = engine(w, w.tau, K.KVB_REFRESH_LITERAL, K.KVB_ALPHA_LAG)
+    eng.run_compile()
+    eng.run_link()
+    ref = state(eng)
+    eng.hidden.fill_(7)
+    eng.page_table.fill_(-9)
+    eng.page_dirty.fill_(3)
+    eng.run_link_native()
+    got = state(eng)
+    assert_same(ref, got)
+    eng.close()
