@@ -147,11 +147,13 @@ def test_link_run_nothing_selected():
 
 
 @pytest.mark.timeout(300)
-@pytest.mark.parametrize("make", [wl.mistral_cacheslide, wl.mistral_legolink], ids=["cacheslide-8k", "legolink-16k"])
+@pytest.mark.parametrize("make", [wl.mistral_cacheslide, wl.mistral_legolink, wl.mistral_batch8],
+                         ids=["cacheslide-8k", "legolink-16k", "batch8"])
 def test_link_run_fullsize(make):
-    """At the benchmark sizes (the Mistral-shaped 8192-token CacheSlide request
-    and the 16384-token LegoLink prompt, bf16, 32 layers) the library's loop is
-    bitwise the per-call loop with device row counts."""
+    """At the benchmark sizes (the Mistral-shaped 8192-token CacheSlide request,
+    the 16384-token LegoLink prompt and the batch of 8 requests sharing fixed
+    chunks; bf16, 32 layers) the library's loop is bitwise the per-call loop
+    with device row counts."""
     w = make()
     eng = engine(w, w.tau, K.KVB_REFRESH_LITERAL, K.KVB_ALPHA_LAG)
     eng.run_compile()
