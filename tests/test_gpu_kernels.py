@@ -26,6 +26,10 @@ SHAPES = {
     "bf16_wide": wl.ModelShape(n_layers=1, d_model=2048, n_q_heads=16, n_kv_heads=4, head_dim=128, ffn=2816,
                                dtype="bf16"),
     "fp32": wl.ModelShape(n_layers=1, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn=688, dtype="fp32"),
+    # a row of 320 16-byte chunks: in the one-row products' normalising
+    # staging some threads take two chunks and the others one
+    "bf16_ragged": wl.ModelShape(n_layers=1, d_model=2560, n_q_heads=20, n_kv_heads=4, head_dim=128, ffn=6912,
+                                 dtype="bf16"),
 }
 
 
@@ -227,7 +231,7 @@ def test_blend_scatter(ctx, name, mode):
     assert np.array_equal(_rows_at(kp, untouched, s), _rows_at(kp0, untouched, s))
 
 
-@pytest.mark.parametrize("name", ["bf16", "bf16_hd64", "bf16_wide", "fp32"])
+@pytest.mark.parametrize("name", ["bf16", "bf16_hd64", "bf16_wide", "bf16_ragged", "fp32"])
 @pytest.mark.parametrize("mode,cached", [(K.KVB_ALPHA_LAG, True), (K.KVB_ALPHA_ONE, True), (K.KVB_ALPHA_ONE, False),
                                          (K.KVB_ALPHA_CURRENT, True)], ids=["lag", "one", "one-nocache", "current"])
 @pytest.mark.parametrize("flags,T_max,n_valid", [(K.KVB_QKV_BATCH_INVARIANT, 200, 173), (K.KVB_QKV_SPLIT_K, 200, 173),
@@ -569,7 +573,7 @@ def test_topk_from_scores(ctx, req_lens):
 
 # ------------------------------------------------------------------ O-proj + MLP
 
-@pytest.mark.parametrize("name", ["bf16", "bf16_wide", "fp32"])
+@pytest.mark.parametrize("name", ["bf16", "bf16_wide", "bf16_ragged", "fp32"])
 @pytest.mark.parametrize("T_max,n_valid", [(230, 201), (64, 64), (7, 5), (1, 1)])
 def test_mlp(ctx, name, T_max, n_valid):
     """O-proj + MLP on gathered rows; the small batches take the 64-row tiles with split-K,
