@@ -409,14 +409,15 @@ typedef struct kvb_layer_weights {
 
 #define KVB_LINK_CACHESLIDE 0  /* layer 1 in full, deviation top-k, fusion and refresh in layers 2..L */
 #define KVB_LINK_STATIC 1      /* a fixed row set recomputed in every layer, replacing the cached K/V */
+#define KVB_LINK_CACHEBLEND 2  /* layer 1 in full, attention-map deviation top-k, those rows replace the cached K/V */
 
 /* Everything one link step reads and writes.  Sizes: N = n_tok, L = n_layers,
  * B = requests; device pointers unless marked host. */
 typedef struct kvb_link_desc {
-  int32_t mode;           /* KVB_LINK_CACHESLIDE or KVB_LINK_STATIC */
+  int32_t mode;           /* KVB_LINK_CACHESLIDE, KVB_LINK_STATIC or KVB_LINK_CACHEBLEND */
   int32_t B, n_tok, n_layers, n_pages, vocab;
   int32_t rows;           /* row bound of layers 2..L: the sum of the per-request k
-                           * (CacheSlide), or the size of the static row set */
+                           * (CacheSlide, CacheBlend), or the size of the static row set */
   int32_t period;         /* CacheSlide: refresh after layer l when l % period == 0 and l < L */
   int32_t refresh_rule;   /* KVB_REFRESH_LITERAL or KVB_REFRESH_DISSIM */
   int32_t alpha_mode;     /* CacheSlide fusion of layers 2..L: KVB_ALPHA_LAG / _CURRENT / _ONE */
@@ -428,7 +429,7 @@ typedef struct kvb_link_desc {
   const int32_t* pos;                  /* [N] RoPE positions in the spliced requests */
   const int32_t* lo;                   /* [N] first visible key (start of the request) */
   const int32_t* cu_tok;               /* [B + 1] */
-  const int32_t* k_cap;                /* [B] CacheSlide k per request (NULL for static) */
+  const int32_t* k_cap;                /* [B] k per request (CacheSlide, CacheBlend; NULL for static) */
   const int32_t* reuse_slot;           /* [L, N] slot of each token's compiled K/V, or -1 */
   const int32_t* const* new_pages;     /* host [L]: layer l + 1's new page ids (device) */
   const int32_t* const* cu_pages;      /* host [L]: its per-request offsets [B + 1] (device) */
@@ -442,7 +443,7 @@ typedef struct kvb_link_desc {
   void* k;                             /* [N, Hkv, hd] scratch */
   void* v;                             /* [N, Hkv, hd] scratch */
   void* o;                             /* [N, Hq hd] scratch */
-  float* d;                            /* [N] CacheSlide layer-1 deviation */
+  float* d;                            /* [N] layer-1 deviation (CacheBlend: attention-map deviation) */
   float* alpha;                        /* [N] CacheSlide fusion weights */
   float* dev;                          /* [rows] per-row deviation of the current layer */
   float* cksim;                        /* [rows] per-row cosine similarity of a refresh layer */
@@ -461,8 +462,11 @@ typedef struct kvb_link_desc {
  * (CacheSlide page, "Method details" and Algorithm 2: layer 1 recomputes
  * every token, the deviation ranks them and the top-k are recomputed in
  * layers 2..L, fused with the cached K/V, with the cosine refresh every
- * `period` layers) or of EPIC's LegoLink (EPIC page, section 4: the static
- * set recomputed in every layer), built from the calls above in the order a
+ * `period` layers), of EPIC's LegoLink (EPIC page, section 4: the static
+ * set recomputed in every layer) or of the CacheBlend baseline as the EPIC
+ * page describes it (section 3.2: layer 1 in full, kvb_attnmap_deviation and
+ * kvb_topk, the selected rows replace the cached K/V in layers 2..L),
+ * built from the calls above in the order a
  * caller would make them: per layer kvb_slot_map, kvb_qkv_fused (layer 1
  * batch-invariant, later layers allowed to split K), the refresh right after
  * the fusion when the layer has one, kvb_sparse_query_attn, kvb_mlp.

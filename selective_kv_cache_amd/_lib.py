@@ -26,7 +26,7 @@ KVB_REFRESH_LITERAL, KVB_REFRESH_DISSIM = 0, 1
 KVB_COPY_H2D, KVB_COPY_D2H = 0, 1
 KVB_QKV_BATCH_INVARIANT, KVB_QKV_SPLIT_K = 0, 1
 KVB_NOALLOC_MAX_TOKENS, KVB_NOALLOC_MAX_REQUESTS = 131072, 4096
-KVB_LINK_CACHESLIDE, KVB_LINK_STATIC = 0, 1
+KVB_LINK_CACHESLIDE, KVB_LINK_STATIC, KVB_LINK_CACHEBLEND = 0, 1, 2
 
 
 class KvbError(RuntimeError):

@@ -1,7 +1,8 @@
 // The whole link step as one call (kvb_link_run): the layer loop of
 // CacheSlide's Algorithm 2 (CacheSlide page, "Method details" and
-// Algorithm 2) or of EPIC's LegoLink (EPIC page, section 4), queued from the
-// host with the per-step entry points and no host synchronisation.
+// Algorithm 2), of EPIC's LegoLink (EPIC page, section 4) or of the
+// CacheBlend baseline as the EPIC page describes it (section 3.2), queued
+// from the host with the per-step entry points and no host synchronisation.
 //
 // CacheSlide: embed every token; layer 1 recomputes all of them at their
 // spliced positions into the layer's new pages; the deviation and top-k pick
@@ -11,6 +12,8 @@
 // the other buffer.  The refresh needs only the cosine similarities that the
 // layer's fusion writes, so it is queued right after the fusion.  LegoLink:
 // embed the static rows, recompute them in every layer (alpha = 1).
+// CacheBlend: layer 1 as CacheSlide's, then the attention-map deviation and
+// its top-k; layers 2..L recompute the selection, replacing the cached K/V.
 //
 // Launch bounds: a selective layer is launched for link->rows rows; the
 // device count of the current selection (cu_rows[cur][B]) bounds the work.
@@ -27,7 +30,8 @@ namespace {
 
 kvb_status check_link(kvb_ctx* ctx, const kvb_model_desc* desc, const kvb_link_desc* k) {
   KVB_CHECK_PTR(k, "link");
-  if (k->mode != KVB_LINK_CACHESLIDE && k->mode != KVB_LINK_STATIC) return fail(KVB_ERR_INVALID_ARG, "bad link mode");
+  if (k->mode != KVB_LINK_CACHESLIDE && k->mode != KVB_LINK_STATIC && k->mode != KVB_LINK_CACHEBLEND)
+    return fail(KVB_ERR_INVALID_ARG, "bad link mode");
   if (k->B < 1 || k->n_tok < 1 || k->n_layers < 1 || k->n_pages < 1 || k->vocab < 1)
     return fail(KVB_ERR_INVALID_ARG, "B, n_tok, n_layers, n_pages and vocab must be >= 1");
   if (k->rows < 0 || k->rows > k->n_tok) return fail(KVB_ERR_INVALID_ARG, "rows outside [0, n_tok]");
@@ -78,6 +82,14 @@ kvb_status check_link(kvb_ctx* ctx, const kvb_model_desc* desc, const kvb_link_d
     KVB_CHECK_PTR(k->cu_rows[1], "cu_rows[1]");
     if (k->sel[0] == k->sel[1] || k->cu_rows[0] == k->cu_rows[1])
       return fail(KVB_ERR_INVALID_ARG, "the two selection buffers must differ");
+  } else if (k->mode == KVB_LINK_CACHEBLEND) {
+    KVB_CHECK_PTR(k->k_cap, "k_cap");
+    KVB_CHECK_PTR(k->d, "d");
+    KVB_CHECK_PTR(k->ranking, "ranking");
+    KVB_CHECK_PTR(k->s_count, "s_count");
+    KVB_CHECK_PTR(k->cursor, "cursor");
+    KVB_CHECK_PTR(k->sel[0], "sel[0]");
+    KVB_CHECK_PTR(k->cu_rows[0], "cu_rows[0]");
   } else if (k->rows > 0) {
     KVB_CHECK_PTR(k->static_rows, "static_rows");
     KVB_CHECK_PTR(k->static_cu, "static_cu");
@@ -151,6 +163,23 @@ extern "C" kvb_status kvb_link_run(kvb_ctx* ctx, void* stream, const kvb_model_d
       for (int l = 1; l <= k->n_layers; l++)
         KVB_TRY(layer_rows(ctx, stream, desc, k, l, T, nullptr, k->static_rows, k->static_cu, nullptr, KVB_ALPHA_ONE,
                            nullptr, nullptr, nullptr, nothing));
+    }
+  } else if (k->mode == KVB_LINK_CACHEBLEND) {
+    const int N = k->n_tok, B = k->B, T = k->rows;
+    KVB_TRY(kvb_embed(ctx, stream, desc, N, nullptr, nullptr, k->tokens, k->vocab, k->embedding, k->hidden));
+    KVB_TRY(layer_rows(ctx, stream, desc, k, 1, N, nullptr, nullptr, k->cu_tok, nullptr, KVB_ALPHA_ONE, nullptr,
+                       nullptr, nullptr, nothing));
+    // q and k still hold layer 1's queries and recomputed keys of every token
+    KVB_TRY(kvb_attnmap_deviation(ctx, stream, desc, N, k->lo, k->q, k->k, k->k_pool, k->n_pages, k->reuse_slot,
+                                  k->scale, k->d, k->ws, k->ws_bytes));
+    KVB_TRY(kvb_topk(ctx, stream, desc, B, N, k->cu_tok, k->d, k->k_cap, k->ranking, k->s_count, k->sel[0],
+                     k->cu_rows[0], k->cursor, k->ws, k->ws_bytes));
+    if (T == 0) {
+      KVB_TRY(reuse_tables(ctx, stream, desc, k, 2));
+    } else {
+      for (int l = 2; l <= k->n_layers; l++)
+        KVB_TRY(layer_rows(ctx, stream, desc, k, l, T, k->cu_rows[0] + B, k->sel[0], k->cu_rows[0], nullptr,
+                           KVB_ALPHA_ONE, nullptr, nullptr, nullptr, nothing));
     }
   } else {
     const int N = k->n_tok, B = k->B, T = k->rows;

@@ -417,14 +417,13 @@ class LinkEngine:
         self._tier_end()
 
     def link_desc(self) -> "K.kvb_link_desc":
-        """The kvb_link_desc of this engine's link step (CacheSlide or LegoLink;
-        the reused cache resident in the pool).  The host arrays it points to
-        are kept on the engine."""
-        if self.cfg.mode not in ("cacheslide", "legolink"):
-            raise ValueError("kvb_link_run covers the CacheSlide and LegoLink link steps")
+        """The kvb_link_desc of this engine's link step (the reused cache
+        resident in the pool).  The host arrays it points to are kept on the
+        engine."""
         if self.cfg.reuse_tier != "hbm":
             raise ValueError("kvb_link_run reads the reused cache from the device pool")
-        L, cs = self.L, self.cfg.mode == "cacheslide"
+        L, mode = self.L, self.cfg.mode
+        cs = mode == "cacheslide"
         lw = (K.kvb_layer_weights * L)()
         for i, W in enumerate(self.model.layers):
             lw[i] = K.kvb_layer_weights(W["norm1"].data_ptr(), W["w_qkv"].data_ptr(), W["w_o"].data_ptr(),
@@ -434,16 +433,18 @@ class LinkEngine:
         self._link_host = (lw, npg, cpg)
         t = lambda x: x.data_ptr() if x is not None else None
         k = K.kvb_link_desc()
-        k.mode = K.KVB_LINK_CACHESLIDE if cs else K.KVB_LINK_STATIC
+        k.mode = {"cacheslide": K.KVB_LINK_CACHESLIDE, "legolink": K.KVB_LINK_STATIC,
+                  "cacheblend": K.KVB_LINK_CACHEBLEND}[mode]
         k.B, k.n_tok, k.n_layers, k.n_pages, k.vocab = self.B, self.N, L, self.n_pages, self.shape.vocab
         k.rows, k.period, k.refresh_rule, k.alpha_mode = self.T_sel, self.cfg.period, self.cfg.refresh_rule, \
             self.cfg.alpha_mode
         k.tau, k.scale = float(self.cfg.tau), float(self.scale)
         k.layers = ctypes.addressof(lw)
         k.embedding, k.tokens, k.pos, k.lo = t(self.model.embedding), t(self.tok_l), t(self.pos_l), t(self.lo_l)
-        k.cu_tok, k.k_cap, k.reuse_slot = t(self.cu_tok), t(self.k_cap_d) if cs else None, t(self.reuse_slot)
+        k.cu_tok, k.reuse_slot = t(self.cu_tok), t(self.reuse_slot)
+        k.k_cap = t(self.k_cap_d) if mode != "legolink" else None
         k.new_pages, k.cu_pages = ctypes.addressof(npg), ctypes.addressof(cpg)
-        if not cs:
+        if mode == "legolink":
             k.static_rows, k.static_cu = t(self.lego_sel), t(self.lego_cu)
         k.page_table, k.k_pool, k.v_pool, k.hidden = t(self.page_table), t(self.k_pool), t(self.v_pool), t(self.hidden)
         k.q, k.k, k.v, k.o = t(self.q), t(self.k), t(self.v), t(self.o)

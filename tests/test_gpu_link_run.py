@@ -2,6 +2,7 @@
 one by one from Python.
 
 kvb_link_run queues what LinkEngine.run_link queues with exact_rows=False
+(CacheSlide, LegoLink and the CacheBlend-style selection)
 (every selective layer launched for the layer-1 selection's size, the device
 row counts bounding the work), so every output must be bitwise the same:
 hidden rows, both K/V pools, page tables, deviation, alpha, per-layer
@@ -42,6 +43,10 @@ CASES = {
                   K.KVB_REFRESH_LITERAL, K.KVB_ALPHA_LAG),
     "lego-bf16-query": (lambda: wl.small_bf16(n_layers=3, mode="legolink", query_len=24), 0.12,
                         K.KVB_REFRESH_LITERAL, K.KVB_ALPHA_LAG),
+    "cacheblend-tiny": (lambda: wl.tiny(n_layers=3, mode="cacheblend"), 0.12, K.KVB_REFRESH_LITERAL,
+                        K.KVB_ALPHA_LAG),
+    "cacheblend-bf16": (lambda: wl.small_bf16(n_layers=3, mode="cacheblend"), 0.12, K.KVB_REFRESH_LITERAL,
+                        K.KVB_ALPHA_LAG),
 }
 
 
@@ -62,9 +67,12 @@ def state(eng):
         out = {name: getattr(eng, name).clone() for name in ("k_pool", "v_pool", "page_table", "page_dirty")}
         out["hidden"] = eng.hidden[eng.lego_sel.long()].clone()
         return out
-    out = {name: getattr(eng, name).clone() for name in
-           ("hidden", "k_pool", "v_pool", "page_table", "d", "alpha", "dev_l", "cksim", "ranking", "s_count",
-            "cursor", "page_dirty")}
+    names = ("hidden", "k_pool", "v_pool", "page_table", "d", "alpha", "dev_l", "cksim", "ranking", "s_count",
+             "cursor", "page_dirty")
+    if eng.cfg.mode == "cacheblend":
+        # no fusion and no refresh: alpha and the per-row deviation and similarity are not written
+        names = tuple(n for n in names if n not in ("alpha", "dev_l", "cksim"))
+    out = {name: getattr(eng, name).clone() for name in names}
     out["selected"] = eng.selected()
     return out
 
@@ -95,7 +103,7 @@ def test_link_run_matches_per_call_loop(case):
     eng.run_link_native()
     got = state(eng)
     assert_same(ref, got)
-    if eng.cfg.mode == "cacheslide":
+    if eng.cfg.mode != "legolink":
         # rows were recomputed after layer 1
         assert sum(len(x) for x in got["selected"]) > 0
     eng.close()
